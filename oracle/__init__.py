@@ -1,0 +1,139 @@
+"""fp64 CPU oracle for the Momentum DeltaNet (MDN) hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(``linear_attention_sequence_mdn_amd``) never imports it, and the two share no
+code: the only module both sides use is the seeded input generator, which holds
+none of the method's arithmetic.
+
+Contents
+--------
+* ``fwd`` / ``step``: the token-by-token recurrence, in C (``mdn_oracle.c``),
+  fp64, OpenMP over heads.  This is the plain definition of what the chunkwise
+  forward and the decode step compute (MDN paper summary at paper.rainbus.top,
+  method walk-through step 1; ijyty.com article on MDN, sections 3 and 6).
+* ``chunk_ref``: a NumPy fp64 restatement of the chunkwise algorithm (same
+  summary, steps 2-5), used to pin the oracle and to give the per-chunk
+  intermediates (coefficients, Gamma, T) a definition of their own.
+
+Every function cites the passage it follows; the pins that tie the oracle to
+the pages live in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mdn_oracle.c")
+_LIB = os.path.join(_HERE, "libmdn_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (-O2, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-Wall", "-o", tmp, _SRC]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        d = ctypes.POINTER(ctypes.c_double)
+        L = ctypes.c_long
+        lib.mdn_oracle_fwd.argtypes = [L, L, L, L] + [d] * 7 + [ctypes.c_void_p, ctypes.c_void_p] + [d] * 4
+        lib.mdn_oracle_fwd.restype = None
+        lib.mdn_oracle_step.argtypes = [L, L, L] + [d] * 7 + [d] * 4
+        lib.mdn_oracle_step.restype = None
+        lib.mdn_oracle_threads.argtypes = []
+        lib.mdn_oracle_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def threads() -> int:
+    """OpenMP threads the C oracle uses."""
+    return int(_load().mdn_oracle_threads())
+
+
+def fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None):
+    """Token-by-token MDN forward in fp64.
+
+    Shapes: q, k ``[..., T, dk]``; v ``[..., T, dv]``; gates ``[..., T]``;
+    S0, M0 ``[..., dk, dv]`` or None (zero).  Leading dims are flattened into
+    independent heads.  Returns ``(O, S_T, M_T, Vtilde)`` as float64 arrays
+    with ``O, Vtilde: [..., T, dv]`` and ``S_T, M_T: [..., dk, dv]``.
+
+    Follows the recurrence of the MDN summary (paper.rainbus.top), method
+    walk-through step 1, with the read-out o_t = S_t^T q_t taken after the
+    update of token t.
+    """
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    alpha, mu, beta, eta = _f64(alpha), _f64(mu), _f64(beta), _f64(eta)
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:-1] == q.shape[:-1]
+    assert alpha.shape == lead + (T,) and mu.shape == alpha.shape
+    assert beta.shape == alpha.shape and eta.shape == alpha.shape
+    BH = int(np.prod(lead)) if lead else 1
+    O = np.zeros(lead + (T, dv))
+    Vt = np.zeros(lead + (T, dv))
+    ST = np.zeros(lead + (dk, dv))
+    MT = np.zeros(lead + (dk, dv))
+    s0p = None
+    m0p = None
+    if S0 is not None:
+        S0 = _f64(np.broadcast_to(S0, lead + (dk, dv)))
+        s0p = S0.ctypes.data
+    if M0 is not None:
+        M0 = _f64(np.broadcast_to(M0, lead + (dk, dv)))
+        m0p = M0.ctypes.data
+    lib.mdn_oracle_fwd(BH, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu),
+                       _ptr(beta), _ptr(eta), s0p, m0p, _ptr(O), _ptr(ST), _ptr(MT), _ptr(Vt))
+    return O, ST, MT, Vt
+
+
+def step(q, k, v, alpha, mu, beta, eta, S, M):
+    """One decode step of the recurrence for every head, fp64.
+
+    q, k ``[..., dk]``; v ``[..., dv]``; gates ``[...]``; S, M ``[..., dk, dv]``.
+    Returns ``(o, S_new, M_new, vtilde)``; the inputs S and M are not modified.
+    Same equations as :func:`fwd` (one token): the recurrent form the MDN
+    article (ijyty.com, section 6) says generation uses.
+    """
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    alpha, mu, beta, eta = _f64(alpha), _f64(mu), _f64(beta), _f64(eta)
+    lead = q.shape[:-1]
+    dk, dv = q.shape[-1], v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    S2 = np.array(np.broadcast_to(S, lead + (dk, dv)), dtype=np.float64, order="C", copy=True)
+    M2 = np.array(np.broadcast_to(M, lead + (dk, dv)), dtype=np.float64, order="C", copy=True)
+    o = np.zeros(lead + (dv,))
+    vt = np.zeros(lead + (dv,))
+    lib.mdn_oracle_step(BH, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu),
+                        _ptr(beta), _ptr(eta), _ptr(S2), _ptr(M2), _ptr(o), _ptr(vt))
+    return o, S2, M2, vt
+
+
+from . import chunk_ref  # noqa: E402,F401
