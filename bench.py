@@ -1,0 +1,294 @@
+"""Benchmark of the MDN hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A *step* is one ``mdn_chunk_fwd`` call (coefficients, intra-chunk and
+inter-chunk kernels: the whole chunkwise forward) over one batch of the
+400M-layer workload: B=8, H=8, T=4096, dk=dv=128, C=64, bf16 q/k/v, fp32
+gates, zero initial state.  Inputs are synthetic (seeded generator) and
+resident in HBM before the timed region.  W untimed warm-up steps, then K
+steps timed with HIP events on the stream the kernels run on, bracketed by
+device synchronisation.  ``value`` = B*T / time per step (tokens/s).
+
+The same run also reports, each measured live with HIP events:
+  * per-kernel average durations (K launches of each stage) and the roofline
+    of the dominant kernel;
+  * the decode workload (B=256, H=16, d=128, 128 consecutive ``mdn_step``
+    calls, median of 5 repetitions) as GB/s of algorithmic HBM traffic;
+  * the fp64 CPU oracle on a bounded sample of the chunk workload.
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MDN chunk-fwd tokens/s at 400M layer shape (% bf16 MFMA peak); decode GB/s"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+# FLOP per token*head of the whole chunk forward (d = 128, C = 64), counting
+# only the causal triangles: 12 d^2 + 6 C d + (2/3) C^2.
+F_TOKEN_HEAD = 248_491
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-chunk", action="store_true")
+    p.add_argument("--decode-reps", type=int, default=5)
+    p.add_argument("--decode-steps", type=int, default=128)
+    p.add_argument("--calibration-copy", action="store_true",
+                   help="run one 1 GiB device copy first (HBM counter calibration)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def kernel_sources_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "linear_attention_sequence_mdn_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(summary, sha):
+    """Counter-derived HBM bytes per launch from a committed rocprofv3 summary,
+    or None when the summary is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", open(path).read(), flags=re.M)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_sha") != sha:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def chunk_bench(args, torch, mdn, inputs):
+    cfg = inputs.CONFIGS[1]
+    x = inputs.config_inputs(1)
+    B, H, T, d, C = x.B, x.H, x.T, x.dk, x.C
+    to = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+                              if bf else torch.from_numpy(np.ascontiguousarray(a)).cuda())
+    q, k, v = to(x.q, True), to(x.k, True), to(x.v, True)
+    gates = [to(x.alpha), to(x.mu), to(x.beta), to(x.eta)]
+    call = mdn.ChunkCall(q, k, v, *gates, None, None, C)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        call.run()
+    torch.cuda.synchronize()
+
+    # whole steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        call.run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per kernel: events between the two stages of each step
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[i][0].record()
+        call.intra()
+        ev[i][1].record()
+        call.inter()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    ms_intra = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms_inter = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    O, ST, MT, Vt = call.outputs
+    finite = bool(torch.isfinite(O.float()).all() and torch.isfinite(ST).all())
+
+    tokens = B * T
+    tok_head = B * H * T
+    es = 2
+    # algorithmic bytes / FLOP per launch of each kernel (documented in the design doc)
+    intra_bytes = tok_head * (2 * 2 * d + 16 + 2 * C * es + 8 * 4)
+    inter_bytes = tok_head * (es * 3 * d + es * 2 * d + 2 * C * es + 8 * 4) + B * H * 2 * d * d * 4
+    intra_flop = tok_head * (2 * C * d + (2 * C * C) // 3)
+    inter_flop = tok_head * (12 * d * d + 2 * C * d)
+    kernels = {
+        "mdn_intra_kernel": {"ms": ms_intra, "alg_bytes": intra_bytes, "alg_flop": intra_flop},
+        "mdn_inter_kernel": {"ms": ms_inter, "alg_bytes": inter_bytes, "alg_flop": inter_flop},
+    }
+    for kd in kernels.values():
+        s = kd["ms"] / 1e3
+        kd["GBps"] = kd["alg_bytes"] / s / 1e9
+        kd["TFLOPs"] = kd["alg_flop"] / s / 1e12
+        t_hbm = kd["alg_bytes"] / (PEAK_HBM_GBS * 1e9)
+        t_mfma = kd["alg_flop"] / (PEAK_BF16_TFLOPS * 1e12)
+        kd["bound"] = "hbm" if t_hbm >= t_mfma else "mfma"
+    dom_name = max(kernels, key=lambda n: kernels[n]["ms"])
+    dom = kernels[dom_name]
+    sha = kernel_sources_sha(["mdn_chunk.hip", "mdn_device.h"])
+    traffic = load_traffic("traffic_mdn_inter_kernel_400M_layer.md", sha) if dom_name == "mdn_inter_kernel" else None
+    if dom["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": dom["GBps"] / PEAK_HBM_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": dom["TFLOPs"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": dom["TFLOPs"] / PEAK_BF16_TFLOPS}
+    roof.update({"traffic": traffic, "kernel": dom_name, "ms": dom["ms"],
+                 "alg_bytes_per_launch": dom["alg_bytes"], "alg_flop_per_launch": dom["alg_flop"],
+                 "source_sha": sha})
+    tps = tokens / (ms_step / 1e3)
+    mfma_frac = tps * H * F_TOKEN_HEAD / (PEAK_BF16_TFLOPS * 1e12)
+    return dict(ms_step=ms_step, tokens_per_s=tps, mfma_frac=mfma_frac, kernels=kernels,
+                roofline=roof, finite=finite, x=x, cfg=cfg)
+
+
+def decode_bench(args, torch, mdn, inputs):
+    c = inputs.CONFIGS[3]
+    B, H, d, n = c["B"], c["H"], c["dk"], args.decode_steps
+    qs, ks, vs, gs = [], [], [], []
+    for st in inputs.decode_steps(B, H, d, steps=n, dtype="bf16", seed=c["seed"]):
+        qs.append(st.q); ks.append(st.k); vs.append(st.v)
+        gs.append(np.stack([st.alpha, st.mu, st.beta, st.eta]))
+    bf = lambda a: torch.from_numpy(np.stack(a)).cuda().to(torch.bfloat16)
+    Q, K, V = bf(qs), bf(ks), bf(vs)
+    G = torch.from_numpy(np.stack(gs)).cuda()          # [n, 4, B, H]
+    S = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda")
+    M = torch.zeros_like(S)
+    o = torch.empty((n, B, H, d), dtype=torch.bfloat16, device="cuda")
+    L = mdn.lib()
+    import ctypes
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    argv = [(P(Q[i]), P(K[i]), P(V[i]), P(G[i, 0]), P(G[i, 1]), P(G[i, 2]), P(G[i, 3]), P(S), P(M), P(o[i]))
+            for i in range(n)]
+
+    def run_all():
+        for a in argv:
+            st = L.mdn_step(B, H, d, d, mdn.MDN_BF16, *a, stream)
+            if st != 0:
+                raise mdn.MdnError(st, "mdn_step")
+
+    run_all()                                           # warm-up pass
+    times = []
+    for _ in range(args.decode_reps):
+        S.zero_(); M.zero_()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run_all()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    bytes_step = B * H * (16 * d * d + 2 * (2 * d + d) + 16 + 2 * d)
+    gbs = n * bytes_step / (ms / 1e3) / 1e9
+    sha = kernel_sources_sha(["mdn_step.hip", "mdn_device.h"])
+    traffic = load_traffic("traffic_mdn_step_kernel_decode.md", sha)
+    return {"metric": "decode GB/s", "value": gbs, "unit": "GB/s",
+            "workload": f"decode B{B} H{H} d{d} bf16, {n} consecutive mdn_step calls",
+            "ms_per_decode_step": ms / n, "reps": args.decode_reps,
+            "alg_bytes_per_step": bytes_step,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "kernel": "mdn_step_kernel",
+                         "source_sha": sha}}
+
+
+def cpu_baseline(args, x):
+    """The fp64 oracle, untuned, on all heads of the chunk workload over a
+    prefix of the sequence sized to about ``--cpu-seconds`` of CPU work."""
+    import oracle
+    H = x.H
+
+    def run(Ts):
+        sl = lambda a: np.ascontiguousarray(a[:, :, :Ts])
+        t0 = time.perf_counter()
+        oracle.fwd(sl(x.q), sl(x.k), sl(x.v), sl(x.alpha), sl(x.mu), sl(x.beta), sl(x.eta))
+        return time.perf_counter() - t0
+
+    t_probe = run(64)
+    Ts = int(min(x.T, max(64, 64 * args.cpu_seconds / max(t_probe, 1e-3))))
+    Ts = max(64, Ts // 64 * 64)
+    wall = run(Ts)
+    return {"value": x.B * Ts / wall, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"fp64 oracle on all B{x.B} x H{H} heads, first {Ts} of {x.T} tokens "
+                      f"({wall:.1f} s wall)",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the MDN hot path here runs on a single MI355X "
+              f"(requested --gpus {args.gpus}, WORLD_SIZE {world}); multi-GPU sharding is a design, "
+              f"not a built path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    import linear_attention_sequence_mdn_amd as mdn
+    from linear_attention_sequence_mdn_amd import inputs
+    mdn.lib()                                            # fail loudly if the library is missing
+
+    if args.calibration_copy:
+        src = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    out = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    ch = None
+    if not args.no_chunk:
+        ch = chunk_bench(args, torch, mdn, inputs)
+        x = ch["x"]
+        out.update({"value": ch["tokens_per_s"], "ms_per_step": ch["ms_step"],
+                    "config": {"workload": "400M-layer chunk forward B8 H8 T4096 dk=dv=128 C64 bf16, "
+                                           "zero initial state", "B": x.B, "H": x.H, "T": x.T,
+                               "dk": x.dk, "dv": x.dv, "C": x.C, "tokens_per_step": x.B * x.T},
+                    "mfma_frac_of_bf16_peak": ch["mfma_frac"], "flop_per_token_head": F_TOKEN_HEAD,
+                    "kernels": ch["kernels"], "roofline": ch["roofline"], "outputs_finite": ch["finite"]})
+    if not args.no_decode:
+        out["decode"] = decode_bench(args, torch, mdn, inputs)
+    if ch is not None and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, ch["x"])
+    try:
+        out["gpu"] = torch.cuda.get_device_name(0)
+    except Exception:
+        pass
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * mdn.h -- C ABI of the MI355X (gfx950) Momentum DeltaNet hot path.
+ *
+ * Operation (pages about "MDN: Parallelizing Stepwise Momentum for Delta
+ * Linear Attention"; the MDN summary at paper.rainbus.top, method
+ * walk-through step 1, and the ijyty.com article on MDN, section 3):
+ *
+ *     vtilde_t = v_t - S_{t-1}^T (alpha_t k_t)
+ *     M_t      = mu_t M_{t-1} - eta_t k_t vtilde_t^T
+ *     S_t      = alpha_t S_{t-1} - beta_t M_t
+ *     o_t      = S_t^T q_t
+ *
+ * mdn_chunk_fwd evaluates this over a whole sequence with the chunkwise
+ * parallel algorithm (summary, steps 2-5: log-domain coefficients, the
+ * unit-lower T = (I + (P K^T) o Gamma^-)^{-1}, vtilde = U - Y S + Z M, the
+ * intra-chunk term ((Q K^T) o Gamma) vtilde) and returns O, the final states
+ * and the materialised vtilde (summary, step 7; article, section 6).
+ * mdn_step is the one-token recurrent form used for generation (article,
+ * section 6).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers owned by the caller (e.g. torch tensors).
+ *   The library allocates nothing, keeps no pointer after returning and has
+ *   no mutable global state, so calls are reentrant.
+ * - Every tensor is contiguous, row-major, in the layout stated per
+ *   argument, and 16-byte aligned.
+ * - dtype (mdn_dtype) is the element type of q, k, v, O, vtilde and o.
+ *   Gates and the states S, M are always fp32.  In the bf16 path the
+ *   matrix products take bf16 operands with fp32 accumulation; states,
+ *   coefficients and every accumulation stay fp32.
+ * - Gate preconditions (documented, not checked on the device): alpha, mu in
+ *   (0, 1]; beta, eta >= 0 and finite.  The coefficients are formed from
+ *   logarithms of alpha and mu, so a gate of exactly 0 is outside the
+ *   contract (the results are undefined, not an error).
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   the call returns without synchronising.  Arguments are validated on the
+ *   host before any HIP call; a failed validation enqueues nothing.
+ *   Launch failures return MDN_ERR_HIP; device faults surface at the
+ *   caller's next synchronisation.
+ * - Return value: an mdn_status (0 = success).
+ */
+#ifndef MDN_H
+#define MDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mdn_status {
+    MDN_OK = 0,
+    MDN_ERR_NULL_ARG = 1,    /* a required pointer is NULL */
+    MDN_ERR_BAD_SHAPE = 2,   /* negative size, or sizes whose product overflows */
+    MDN_ERR_UNSUPPORTED = 3, /* dtype / head dim / chunk size outside the compiled set */
+    MDN_ERR_ALIAS = 4,       /* an output overlaps an input (other than the allowed aliases) */
+    MDN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+    MDN_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
+    MDN_ERR_HIP = 7          /* a HIP launch or runtime call failed */
+} mdn_status;
+
+typedef enum mdn_dtype {
+    MDN_F32 = 0,             /* fp32 q, k, v, outputs; fp32 matrix-core products */
+    MDN_BF16 = 1             /* bf16 q, k, v, outputs; bf16 operands, fp32 accumulation */
+} mdn_dtype;
+
+/* Rows of the per-chunk coefficient block written by mdn_chunk_coef (and
+ * kept in the workspace of mdn_chunk_fwd).  Each row holds C fp32 values
+ * indexed by the chunk-local token r = 0..C-1.  Definitions (summary, steps 2
+ * and 5; every cumulative quantity restarts at each chunk):
+ *   LA    Lambda_alpha_r = sum_{s<=r} log alpha_s        (cumsum of logs)
+ *   LM    Lambda_mu_r    = sum_{s<=r} log mu_s
+ *   LOGC  log c_r = logcumsumexp_{j<=r}(log beta_j + LM_j - LA_j)
+ *   ABAR  abar_r = exp(LA_r)
+ *   B     b_r = exp(LA_r + LOGC_r) = sum_{j<=r} beta_j (abar_r/abar_j) mubar_j
+ *   ABP   alpha_r * b_{r-1} (b_{-1} = 0): the momentum weight of the error term
+ *   GS    Gamma_{C-1,i}: weight of k_i vtilde_i^T in the end-of-chunk S
+ *   GM    eta_i mubar_{C-1}/mubar_i: weight of k_i vtilde_i^T in the end-of-chunk M
+ * Tokens past the end of a ragged last chunk are padded with alpha = mu = 1,
+ * beta = eta = 0 and zero q, k, v, which leaves every quantity unchanged. */
+enum {
+    MDN_COEF_ABAR = 0, MDN_COEF_ABP = 1, MDN_COEF_B = 2, MDN_COEF_GS = 3,
+    MDN_COEF_GM = 4, MDN_COEF_LA = 5, MDN_COEF_LM = 6, MDN_COEF_LOGC = 7,
+    MDN_COEF_ROWS = 8
+};
+
+/* Bytes of workspace mdn_chunk_fwd needs for these sizes (0 if none).
+ * Returns (size_t)-1 when the sizes are invalid or unsupported.
+ * Layout (documented for diagnostics; NT = ceil(T / C)):
+ *   [B*H*NT][C][C]  T matrices   (dtype)
+ *   [B*H*NT][C][C]  (Q K^T) o Gamma, zero above the diagonal (dtype)
+ *   [B*H*NT][MDN_COEF_ROWS][C]  coefficients (fp32)
+ * each section starting on a 256-byte boundary. */
+size_t mdn_chunk_fwd_workspace_bytes(int64_t B, int64_t H, int64_t T,
+                                     int dk, int dv, int C, int dtype);
+
+/* Chunkwise-parallel forward over a whole sequence.
+ *   B, H, T     batch, heads, sequence length (any T >= 0; a last chunk
+ *               shorter than C is handled by neutral padding; B*H == 0 or
+ *               T == 0 is valid: with T == 0 only S_T, M_T are written,
+ *               as copies of S0, M0).
+ *   dk, dv      head dims: dk == dv, in {16, 32, 64, 128} for MDN_F32 and
+ *               {32, 64, 128} for MDN_BF16.
+ *   C           chunk size: {16, 32, 64} for MDN_F32, {32, 64} for MDN_BF16.
+ *   q, k        [B][H][T][dk]  (dtype); every k_t is used as given.
+ *   v           [B][H][T][dv]  (dtype)
+ *   alpha, mu, beta, eta   [B][H][T] fp32, linear (not log) gates.
+ *   S0, M0      [B][H][dk][dv] fp32 initial states, or NULL for zero.
+ *   O           [B][H][T][dv]  (dtype) out: o_t = S_t^T q_t.
+ *   S_T, M_T    [B][H][dk][dv] fp32 out: states after token T.  S_T may be
+ *               exactly S0 and M_T exactly M0 (in-place update); any other
+ *               overlap with an input is MDN_ERR_ALIAS.
+ *   Vtilde      [B][H][T][dv]  (dtype) out: the materialised vtilde_t.
+ *   workspace   device scratch of at least mdn_chunk_fwd_workspace_bytes();
+ *               must not overlap any other argument.  Its contents on return
+ *               follow the layout above.
+ *   stream      hipStream_t.
+ */
+int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                  const void* q, const void* k, const void* v,
+                  const float* alpha, const float* mu, const float* beta, const float* eta,
+                  const float* S0, const float* M0,
+                  void* O, float* S_T, float* M_T, void* Vtilde,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two stages of mdn_chunk_fwd, exposed separately so that each kernel
+ * can be timed or checked on its own.  mdn_chunk_fwd(args) is exactly
+ * mdn_chunk_intra(args) followed by mdn_chunk_inter(args) on one stream.
+ *
+ * mdn_chunk_intra: coefficients (summary, step 5), T = (I + (P K^T) o
+ *   Gamma^-)^{-1} and (Q K^T) o Gamma (steps 3-4) for every chunk, written to
+ *   `workspace` (layout above).  Reads q, k and the gates only; same
+ *   validation as mdn_chunk_fwd for the arguments it takes.
+ * mdn_chunk_inter: the sequential inter-chunk stage: vtilde = T W, O and the
+ *   S/M carry (step 4 and the closed form of step 2).  Takes the arguments of
+ *   mdn_chunk_fwd and reads the workspace mdn_chunk_intra left for the same
+ *   q, k and gates; the gates themselves are validated but not read. */
+int mdn_chunk_intra(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                    const void* q, const void* k,
+                    const float* alpha, const float* mu, const float* beta, const float* eta,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+int mdn_chunk_inter(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                    const void* q, const void* k, const void* v,
+                    const float* alpha, const float* mu, const float* beta, const float* eta,
+                    const float* S0, const float* M0,
+                    void* O, float* S_T, float* M_T, void* Vtilde,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* One recurrent decode step for every (batch, head), states updated in place
+ * (article, section 6: generation runs the recurrence token by token).
+ *   q, k        [B][H][dk] (dtype);  v [B][H][dv] (dtype)
+ *   alpha, mu, beta, eta   [B][H] fp32
+ *   S, M        [B][H][dk][dv] fp32, read and overwritten with S_t, M_t.
+ *   o           [B][H][dv] (dtype) out.
+ *   dk == dv in {16, 32, 64, 128} for both dtypes.
+ * S and M must not overlap each other or any other argument. */
+int mdn_step(int64_t B, int64_t H, int dk, int dv, int dtype,
+             const void* q, const void* k, const void* v,
+             const float* alpha, const float* mu, const float* beta, const float* eta,
+             float* S, float* M, void* o, void* stream);
+
+/* Diagnostic: the log-domain coefficient stage alone (summary, step 5), as
+ * used inside mdn_chunk_fwd.
+ *   alpha, mu, beta, eta   [B][H][T] fp32;  C in {16, 32, 64}.
+ *   coef   out [B][H][NT][MDN_COEF_ROWS][C] fp32 (rows as defined above).
+ *   gamma  out [B][H][NT][C][C] fp32: Gamma_{r,i} = eta_i gamma_{r,i} for
+ *          i <= r, 0 above the diagonal; or NULL to skip. */
+int mdn_chunk_coef(int64_t B, int64_t H, int64_t T, int C,
+                   const float* alpha, const float* mu, const float* beta, const float* eta,
+                   float* coef, float* gamma, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mdn_status_string(int status);
+
+/* ABI revision of this header (incremented on any signature change). */
+int mdn_abi_version(void);
+
+#define MDN_ABI_VERSION 2
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MDN_H */

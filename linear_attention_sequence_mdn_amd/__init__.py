@@ -1,1 +1,229 @@
-"""MI355X-native Momentum DeltaNet hot path (placeholder; binding added with the C-ABI)."""
+"""MI355X-native Momentum DeltaNet hot path: thin binding over ``libmdn.so``.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(``include/mdn.h``).  This module only marshals torch tensors into pointers,
+sizes and the current HIP stream, allocates outputs and workspace with torch,
+and turns nonzero status codes into :class:`MdnError`.  There is no CPU or
+PyTorch fallback: if the library is missing, every call raises.
+
+Entry points (same names as the C ABI):
+    chunk_fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64)
+        -> (O, S_T, M_T, Vtilde)
+    step(q, k, v, alpha, mu, beta, eta, S, M) -> o   (S, M updated in place)
+    chunk_coef(alpha, mu, beta, eta, C) -> (coef, gamma)
+    chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype) -> int
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmdn.so")
+
+MDN_F32 = 0
+MDN_BF16 = 1
+COEF_ROWS = 8
+COEF_NAMES = ("abar", "abp", "b", "gS", "gM", "la", "lm", "logc")
+
+_lib = None
+
+
+class MdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().mdn_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def lib():
+    """The loaded C library (ctypes); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m linear_attention_sequence_mdn_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        L.mdn_chunk_fwd_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32]
+        L.mdn_chunk_fwd_workspace_bytes.restype = sz
+        L.mdn_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
+        L.mdn_chunk_fwd.restype = i32
+        L.mdn_chunk_intra.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 6 + [vp, sz, vp]
+        L.mdn_chunk_intra.restype = i32
+        L.mdn_chunk_inter.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
+        L.mdn_chunk_inter.restype = i32
+        L.mdn_step.argtypes = [i64, i64, i32, i32, i32] + [vp] * 10 + [vp]
+        L.mdn_step.restype = i32
+        L.mdn_chunk_coef.argtypes = [i64, i64, i64, i32] + [vp] * 6 + [vp]
+        L.mdn_chunk_coef.restype = i32
+        L.mdn_status_string.argtypes = [i32]
+        L.mdn_status_string.restype = ctypes.c_char_p
+        L.mdn_abi_version.argtypes = []
+        L.mdn_abi_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return MDN_BF16
+    if t.dtype == torch.float32:
+        return MDN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MdnError(status, where)
+
+
+def _need(t, name, dtype, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype) -> int:
+    n = lib().mdn_chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise MdnError(3, "mdn_chunk_fwd_workspace_bytes")
+    return int(n)
+
+
+class ChunkCall:
+    """Validated, preallocated arguments of one chunk forward.
+
+    Holds the output tensors and the workspace so that repeated calls (the
+    benchmark, a training loop) allocate nothing; ``run()`` is
+    ``mdn_chunk_fwd``, ``intra()``/``inter()`` its two stages."""
+
+    def __init__(self, q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, *,
+                 out=None, S_T=None, M_T=None, workspace=None):
+        torch = _torch()
+        B, H, T, dk = q.shape
+        dv = v.shape[-1]
+        self.dt = _dtype_code(q)
+        dev = q.device
+        _need(q, "q", q.dtype, (B, H, T, dk), dev)
+        _need(k, "k", q.dtype, (B, H, T, dk), dev)
+        _need(v, "v", q.dtype, (B, H, T, dv), dev)
+        for name, g in (("alpha", alpha), ("mu", mu), ("beta", beta), ("eta", eta)):
+            _need(g, name, torch.float32, (B, H, T), dev)
+        for name, s in (("S0", S0), ("M0", M0)):
+            if s is not None:
+                _need(s, name, torch.float32, (B, H, dk, dv), dev)
+        if out is None:
+            O = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+            Vt = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+        else:
+            O, Vt = out
+        if S_T is None:
+            S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        if M_T is None:
+            M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        nws = chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, self.dt)
+        if workspace is None and nws > 0:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+        self.sizes = (B, H, T, dk, dv, C, self.dt)
+        self.tensors = (q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vt)
+        self.workspace = workspace
+        self.outputs = (O, S_T, M_T, Vt)
+        self._ptrs = [_ptr(t) for t in self.tensors]
+        self._ws = (_ptr(workspace) if workspace is not None else None,
+                    workspace.numel() if workspace is not None else 0)
+
+    def run(self, stream=None):
+        _check(lib().mdn_chunk_fwd(*self.sizes, *self._ptrs, *self._ws, _stream(stream)), "mdn_chunk_fwd")
+        return self.outputs
+
+    def intra(self, stream=None):
+        p = self._ptrs
+        _check(lib().mdn_chunk_intra(*self.sizes, p[0], p[1], p[3], p[4], p[5], p[6], *self._ws,
+                                     _stream(stream)), "mdn_chunk_intra")
+
+    def inter(self, stream=None):
+        _check(lib().mdn_chunk_inter(*self.sizes, *self._ptrs, *self._ws, _stream(stream)), "mdn_chunk_inter")
+        return self.outputs
+
+
+def chunk_fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, *,
+              out=None, S_T=None, M_T=None, workspace=None, stream=None):
+    """Chunkwise forward: returns (O, S_T, M_T, Vtilde).
+
+    q, k: [B,H,T,dk]; v: [B,H,T,dv] (bf16 or fp32, same dtype, on the GPU);
+    gates [B,H,T] fp32; S0, M0 [B,H,dk,dv] fp32 or None.  ``out`` may be an
+    (O, Vtilde) pair of preallocated tensors; ``S_T``/``M_T`` may alias S0/M0
+    for an in-place update; ``workspace`` a uint8 tensor of at least
+    ``chunk_fwd_workspace_bytes`` bytes.
+    """
+    call = ChunkCall(q, k, v, alpha, mu, beta, eta, S0, M0, C, out=out, S_T=S_T, M_T=M_T,
+                     workspace=workspace)
+    return call.run(stream)
+
+
+def step(q, k, v, alpha, mu, beta, eta, S, M, *, o=None, stream=None):
+    """One decode step; S and M ([B,H,dk,dv] fp32) are updated in place.
+    q, k: [B,H,dk]; v: [B,H,dv]; gates [B,H].  Returns o [B,H,dv]."""
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    dev = q.device
+    _need(k, "k", q.dtype, (B, H, dk), dev)
+    _need(v, "v", q.dtype, (B, H, dv), dev)
+    for name, g in (("alpha", alpha), ("mu", mu), ("beta", beta), ("eta", eta)):
+        _need(g, name, torch.float32, (B, H), dev)
+    _need(S, "S", torch.float32, (B, H, dk, dv), dev)
+    _need(M, "M", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    st = lib().mdn_step(B, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu),
+                        _ptr(beta), _ptr(eta), _ptr(S), _ptr(M), _ptr(o), _stream(stream))
+    _check(st, "mdn_step")
+    return o
+
+
+def chunk_coef(alpha, mu, beta, eta, C, *, with_gamma=True, stream=None):
+    """The log-domain coefficient stage alone (diagnostic).
+
+    Returns (coef [B,H,NT,8,C], gamma [B,H,NT,C,C] or None); coefficient rows
+    are named in ``COEF_NAMES``."""
+    torch = _torch()
+    B, H, T = alpha.shape
+    dev = alpha.device
+    for name, g in (("alpha", alpha), ("mu", mu), ("beta", beta), ("eta", eta)):
+        _need(g, name, torch.float32, (B, H, T), dev)
+    NT = (T + C - 1) // C
+    coef = torch.empty((B, H, NT, COEF_ROWS, C), dtype=torch.float32, device=dev)
+    gamma = torch.empty((B, H, NT, C, C), dtype=torch.float32, device=dev) if with_gamma else None
+    st = lib().mdn_chunk_coef(B, H, T, C, _ptr(alpha), _ptr(mu), _ptr(beta), _ptr(eta),
+                              _ptr(coef), _ptr(gamma), _stream(stream))
+    _check(st, "mdn_chunk_coef")
+    return coef, gamma

@@ -1,0 +1,293 @@
+// mdn_api.cpp -- C entry points declared in include/mdn.h.
+//
+// Every argument is validated here, on the host, before any HIP call: sizes,
+// the compiled (dtype, head dim, chunk size) set, NULL pointers, 16-byte
+// alignment, overlap between outputs and inputs, and workspace size.  A
+// failed check returns its status and enqueues nothing.  Validated calls are
+// handed to the launchers in mdn_step.hip / mdn_chunk.hip.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mdn.h"
+#include "mdn_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;   // per tensor; keeps every offset in range
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+    const uintptr_t a = (uintptr_t)p;
+    return Range{a, a + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > kMaxElems / a) return false;
+    *out = a * b;
+    return *out <= kMaxElems;
+}
+
+int64_t elem_size(int dtype) { return dtype == MDN_BF16 ? 2 : 4; }
+
+bool dims_supported_chunk(int dtype, int dk, int dv, int C) {
+    if (dk != dv) return false;
+    if (dtype == MDN_F32)
+        return (dk == 16 || dk == 32 || dk == 64 || dk == 128) && (C == 16 || C == 32 || C == 64);
+    if (dtype == MDN_BF16)
+        return (dk == 32 || dk == 64 || dk == 128) && (C == 32 || C == 64);
+    return false;
+}
+
+bool dims_supported_step(int dtype, int dk, int dv) {
+    if (dtype != MDN_F32 && dtype != MDN_BF16) return false;
+    return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct ChunkSizes {
+    int64_t BH, NT, tok;         // tok = BH * T
+    int64_t qk_elems, v_elems, g_elems, st_elems, tiles;
+};
+
+int chunk_sizes(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, ChunkSizes* s) {
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0 || C <= 0) return MDN_ERR_BAD_SHAPE;
+    if (!mul_ok(B, H, &s->BH) || !mul_ok(s->BH, T, &s->tok)) return MDN_ERR_BAD_SHAPE;
+    s->NT = (T + C - 1) / C;
+    if (!mul_ok(s->tok, dk, &s->qk_elems) || !mul_ok(s->tok, dv, &s->v_elems)) return MDN_ERR_BAD_SHAPE;
+    s->g_elems = s->tok;
+    int64_t dd;
+    if (!mul_ok((int64_t)dk, (int64_t)dv, &dd) || !mul_ok(s->BH, dd, &s->st_elems)) return MDN_ERR_BAD_SHAPE;
+    int64_t cc;
+    if (!mul_ok(s->BH, s->NT, &s->tiles) || !mul_ok(s->tiles, (int64_t)C * C, &cc)) return MDN_ERR_BAD_SHAPE;
+    // one workgroup per chunk tile / per column slab: keep the grids in range
+    if (s->tiles > INT32_MAX || s->BH > INT32_MAX / 8) return MDN_ERR_BAD_SHAPE;
+    return MDN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MDN_OK : MDN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mdn_status_string(int status)
+{
+    switch (status) {
+    case MDN_OK: return "MDN_OK";
+    case MDN_ERR_NULL_ARG: return "MDN_ERR_NULL_ARG: a required pointer is NULL";
+    case MDN_ERR_BAD_SHAPE: return "MDN_ERR_BAD_SHAPE: negative or overflowing size";
+    case MDN_ERR_UNSUPPORTED: return "MDN_ERR_UNSUPPORTED: dtype, head dim or chunk size not compiled";
+    case MDN_ERR_ALIAS: return "MDN_ERR_ALIAS: an output overlaps an input or another output";
+    case MDN_ERR_WORKSPACE: return "MDN_ERR_WORKSPACE: workspace missing or too small";
+    case MDN_ERR_ALIGN: return "MDN_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case MDN_ERR_HIP: return "MDN_ERR_HIP: a HIP launch or runtime call failed";
+    default: return "unknown mdn status";
+    }
+}
+
+int mdn_abi_version(void) { return MDN_ABI_VERSION; }
+
+size_t mdn_chunk_fwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype)
+{
+    ChunkSizes s;
+    if (chunk_sizes(B, H, T, dk, dv, C, &s) != MDN_OK) return (size_t)-1;
+    if (!dims_supported_chunk(dtype, dk, dv, C)) return (size_t)-1;
+    const size_t mat = align256((size_t)s.tiles * C * C * elem_size(dtype));
+    const size_t cf = align256((size_t)s.tiles * MDN_COEF_ROWS * C * sizeof(float));
+    return 2 * mat + cf;
+}
+
+// Validation shared by mdn_chunk_fwd and its two stages.  `stage` is
+// 3 (both), 1 (intra only) or 2 (inter only); only the pointers a stage
+// reads or writes are required.
+static int chunk_prepare(int stage, int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                         const void* q, const void* k, const void* v,
+                         const float* alpha, const float* mu, const float* beta, const float* eta,
+                         const float* S0, const float* M0,
+                         void* O, float* S_T, float* M_T, void* Vtilde,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         mdn::ChunkArgs* a, bool* empty)
+{
+    ChunkSizes s;
+    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
+    if (st != MDN_OK) return st;
+    if (!dims_supported_chunk(dtype, dk, dv, C)) return MDN_ERR_UNSUPPORTED;
+    *empty = s.BH == 0;
+    if (*empty) return MDN_OK;
+
+    const int64_t es = elem_size(dtype);
+    const bool seq = s.tok > 0;
+    const bool inter = (stage & 2) != 0;
+    if (inter && (!S_T || !M_T)) return MDN_ERR_NULL_ARG;
+    if (seq && (!q || !k || !alpha || !mu || !beta || !eta)) return MDN_ERR_NULL_ARG;
+    if (seq && inter && (!v || !O || !Vtilde)) return MDN_ERR_NULL_ARG;
+    const size_t need = mdn_chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return MDN_ERR_WORKSPACE;
+
+    const void* all[] = {q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde, workspace};
+    for (const void* p : all)
+        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
+
+    const Range rq = range_of(q, s.qk_elems * es), rk = range_of(k, s.qk_elems * es);
+    const Range rv = range_of(v, s.v_elems * es);
+    const Range ra = range_of(alpha, s.g_elems * 4), rm = range_of(mu, s.g_elems * 4);
+    const Range rb = range_of(beta, s.g_elems * 4), re = range_of(eta, s.g_elems * 4);
+    const Range rs0 = range_of(S0, S0 ? s.st_elems * 4 : 0), rm0 = range_of(M0, M0 ? s.st_elems * 4 : 0);
+    const Range rO = range_of(O, O ? s.v_elems * es : 0), rVt = range_of(Vtilde, Vtilde ? s.v_elems * es : 0);
+    const Range rST = range_of(S_T, S_T ? s.st_elems * 4 : 0), rMT = range_of(M_T, M_T ? s.st_elems * 4 : 0);
+    const Range rW = range_of(workspace, (int64_t)need);
+    const Range ins[] = {rq, rk, rv, ra, rm, rb, re, rs0, rm0};
+    const Range outs[] = {rO, rVt, rST, rMT, rW};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 9; ++j) {
+            if (!overlap(outs[i], ins[j])) continue;
+            // the states may be updated in place, as exact aliases only
+            if (i == 2 && j == 7 && (const void*)S_T == (const void*)S0) continue;
+            if (i == 3 && j == 8 && (const void*)M_T == (const void*)M0) continue;
+            return MDN_ERR_ALIAS;
+        }
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(outs[i], outs[j])) return MDN_ERR_ALIAS;
+    }
+
+    memset(a, 0, sizeof(*a));
+    a->BH = s.BH; a->T = T; a->NT = s.NT;
+    a->dk = dk; a->dv = dv; a->C = C; a->dtype = dtype;
+    a->q = q; a->k = k; a->v = v;
+    a->alpha = alpha; a->mu = mu; a->beta = beta; a->eta = eta;
+    a->S0 = S0; a->M0 = M0;
+    a->O = O; a->ST = S_T; a->MT = M_T; a->Vt = Vtilde;
+    const size_t mat = align256((size_t)s.tiles * C * C * es);
+    a->Tmat = workspace;
+    a->Aqk = workspace ? (char*)workspace + mat : nullptr;
+    a->coef = workspace ? (float*)((char*)workspace + 2 * mat) : nullptr;
+    a->gamma = nullptr;
+    a->stream = stream;
+    return MDN_OK;
+}
+
+int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                  const void* q, const void* k, const void* v,
+                  const float* alpha, const float* mu, const float* beta, const float* eta,
+                  const float* S0, const float* M0,
+                  void* O, float* S_T, float* M_T, void* Vtilde,
+                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    mdn::ChunkArgs a;
+    bool empty = false;
+    int st = chunk_prepare(3, B, H, T, dk, dv, C, dtype, q, k, v, alpha, mu, beta, eta, S0, M0,
+                           O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
+    if (st != MDN_OK || empty) return st;
+    if (T > 0) {
+        st = hip_status(mdn::launch_chunk_intra(a));
+        if (st != MDN_OK) return st;
+    }
+    return hip_status(mdn::launch_chunk_inter(a));
+}
+
+int mdn_chunk_intra(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                    const void* q, const void* k,
+                    const float* alpha, const float* mu, const float* beta, const float* eta,
+                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    mdn::ChunkArgs a;
+    bool empty = false;
+    int st = chunk_prepare(1, B, H, T, dk, dv, C, dtype, q, k, nullptr, alpha, mu, beta, eta,
+                           nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           workspace, workspace_bytes, stream, &a, &empty);
+    if (st != MDN_OK || empty || T == 0) return st;
+    return hip_status(mdn::launch_chunk_intra(a));
+}
+
+int mdn_chunk_inter(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                    const void* q, const void* k, const void* v,
+                    const float* alpha, const float* mu, const float* beta, const float* eta,
+                    const float* S0, const float* M0,
+                    void* O, float* S_T, float* M_T, void* Vtilde,
+                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    mdn::ChunkArgs a;
+    bool empty = false;
+    int st = chunk_prepare(2, B, H, T, dk, dv, C, dtype, q, k, v, alpha, mu, beta, eta, S0, M0,
+                           O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
+    if (st != MDN_OK || empty) return st;
+    return hip_status(mdn::launch_chunk_inter(a));
+}
+
+int mdn_step(int64_t B, int64_t H, int dk, int dv, int dtype,
+             const void* q, const void* k, const void* v,
+             const float* alpha, const float* mu, const float* beta, const float* eta,
+             float* S, float* M, void* o, void* stream)
+{
+    int64_t BH, qe, ve, se, dd;
+    if (B < 0 || H < 0 || dk <= 0 || dv <= 0) return MDN_ERR_BAD_SHAPE;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, dk, &qe) || !mul_ok(BH, dv, &ve)) return MDN_ERR_BAD_SHAPE;
+    if (!mul_ok((int64_t)dk, (int64_t)dv, &dd) || !mul_ok(BH, dd, &se)) return MDN_ERR_BAD_SHAPE;
+    if (BH > INT32_MAX) return MDN_ERR_BAD_SHAPE;
+    if (!dims_supported_step(dtype, dk, dv)) return MDN_ERR_UNSUPPORTED;
+    if (BH == 0) return MDN_OK;
+    if (!q || !k || !v || !alpha || !mu || !beta || !eta || !S || !M || !o) return MDN_ERR_NULL_ARG;
+    const void* all[] = {q, k, v, alpha, mu, beta, eta, S, M, o};
+    for (const void* p : all)
+        if (!aligned16(p)) return MDN_ERR_ALIGN;
+    const int64_t es = elem_size(dtype);
+    const Range rS = range_of(S, se * 4), rM = range_of(M, se * 4), ro = range_of(o, ve * es);
+    const Range others[] = {range_of(q, qe * es), range_of(k, qe * es), range_of(v, ve * es),
+                            range_of(alpha, BH * 4), range_of(mu, BH * 4), range_of(beta, BH * 4),
+                            range_of(eta, BH * 4)};
+    if (overlap(rS, rM) || overlap(rS, ro) || overlap(rM, ro)) return MDN_ERR_ALIAS;
+    for (const Range& r : others)
+        if (overlap(rS, r) || overlap(rM, r) || overlap(ro, r)) return MDN_ERR_ALIAS;
+
+    mdn::StepArgs a;
+    a.BH = BH; a.dk = dk; a.dv = dv; a.dtype = dtype;
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.mu = mu; a.beta = beta; a.eta = eta;
+    a.S = S; a.M = M; a.o = o; a.stream = stream;
+    return hip_status(mdn::launch_step(a));
+}
+
+int mdn_chunk_coef(int64_t B, int64_t H, int64_t T, int C,
+                   const float* alpha, const float* mu, const float* beta, const float* eta,
+                   float* coef, float* gamma, void* stream)
+{
+    ChunkSizes s;
+    int st = chunk_sizes(B, H, T, 16, 16, C, &s);
+    if (st != MDN_OK) return st;
+    if (C != 16 && C != 32 && C != 64) return MDN_ERR_UNSUPPORTED;
+    if (s.tiles == 0) return MDN_OK;
+    if (!alpha || !mu || !beta || !eta || !coef) return MDN_ERR_NULL_ARG;
+    const void* all[] = {alpha, mu, beta, eta, coef, gamma};
+    for (const void* p : all)
+        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
+    const Range rc = range_of(coef, s.tiles * MDN_COEF_ROWS * C * 4);
+    const Range rg = range_of(gamma, gamma ? s.tiles * C * C * 4 : 0);
+    const Range ins[] = {range_of(alpha, s.tok * 4), range_of(mu, s.tok * 4),
+                         range_of(beta, s.tok * 4), range_of(eta, s.tok * 4)};
+    if (overlap(rc, rg)) return MDN_ERR_ALIAS;
+    for (const Range& r : ins)
+        if (overlap(rc, r) || overlap(rg, r)) return MDN_ERR_ALIAS;
+
+    mdn::ChunkArgs a;
+    memset(&a, 0, sizeof(a));
+    a.BH = s.BH; a.T = T; a.NT = s.NT; a.dk = 16; a.dv = 16; a.C = C; a.dtype = MDN_F32;
+    a.alpha = alpha; a.mu = mu; a.beta = beta; a.eta = eta;
+    a.coef = coef; a.gamma = gamma; a.stream = stream;
+    return hip_status(mdn::launch_chunk_coef(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,195 @@
+// mdn_device.h -- device-side building blocks shared by the MDN kernels (gfx950).
+//
+// Matrix-core fragments.  Every product in the chunk kernels runs on 16x16
+// output tiles:
+//   bf16 path: v_mfma_f32_16x16x32_bf16 (8 bf16 of A and of B per lane, K = 32)
+//   fp32 path: v_mfma_f32_16x16x4_f32   (1 fp32 of A and of B per lane, K = 4)
+// Accumulator layout (both): lane l, register e holds D[4*(l/16) + e][l%16].
+// Operand layout: lane l holds row (A) / column (B) l%16 and a group of K
+// values selected by l/16.  Which K index a given (lane group, slot) carries
+// only has to agree between A and B, so the kernels pick the order that lets
+// an accumulator be reused as the next product's B operand without leaving
+// registers ("slot map" below).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace mdn {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// Element traits
+// ---------------------------------------------------------------------------
+struct TraitsBf16 {
+    using elem = __bf16;
+    using frag = bf16x8;
+    static constexpr int KW = 32;   // contraction length of one matrix-core op
+
+    static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float to_f(elem x) { return (float)x; }
+    static __device__ __forceinline__ elem from_f(float x) { return (__bf16)x; }
+};
+
+struct TraitsF32 {
+    using elem = float;
+    using frag = float;
+    static constexpr int KW = 4;
+
+    static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float to_f(elem x) { return x; }
+    static __device__ __forceinline__ elem from_f(float x) { return x; }
+};
+
+// ---------------------------------------------------------------------------
+// Slot map for products whose B operand is an accumulator.
+//
+// An accumulator "column" is a stack of 16-row tiles acc[0..R/16) (rows of
+// the contraction index).  Lane group g = l/16 of tile t holds rows
+// 16t + 4g + e, e = 0..3.
+//   bf16 (K = 32 per step ks): slots 0..3 <- tile 2ks, slots 4..7 <- tile
+//   2ks+1, so slot j of group g is contraction row 32ks + 16(j/4) + 4g + j%4.
+//   fp32 (K = 4 per step ks): the single slot of group g is contraction row
+//   16(ks/4) + 4g + ks%4.
+// The A operand of the same product must present the same rows: for a
+// row-major A with the contraction index contiguous this is two 8-byte loads
+// (bf16) or one 4-byte load (fp32) per step.
+// ---------------------------------------------------------------------------
+template <typename Tr> struct Slots;
+
+template <> struct Slots<TraitsBf16> {
+    using Tr = TraitsBf16;
+    // contraction row of slot j (0..7) for step ks, lane group g
+    static __device__ __forceinline__ int row(int ks, int g, int j) {
+        return 32 * ks + 16 * (j >> 2) + 4 * g + (j & 3);
+    }
+    // B operand from accumulator tiles, optionally scaled per contraction row.
+    static __device__ __forceinline__ bf16x8 from_acc(const floatx4* acc, int ks) {
+        const floatx4 a = acc[2 * ks], b = acc[2 * ks + 1];
+        bf16x8 r;
+        r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
+        r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
+        return r;
+    }
+    static __device__ __forceinline__ bf16x8 from_acc_scaled(const floatx4* acc, int ks, const float* s) {
+        // s[j] is the scale of slot j
+        const floatx4 a = acc[2 * ks], b = acc[2 * ks + 1];
+        bf16x8 r;
+        r[0] = (__bf16)(a[0] * s[0]); r[1] = (__bf16)(a[1] * s[1]);
+        r[2] = (__bf16)(a[2] * s[2]); r[3] = (__bf16)(a[3] * s[3]);
+        r[4] = (__bf16)(b[0] * s[4]); r[5] = (__bf16)(b[1] * s[5]);
+        r[6] = (__bf16)(b[2] * s[6]); r[7] = (__bf16)(b[3] * s[7]);
+        return r;
+    }
+    static constexpr int NSLOT = 8;
+    static __device__ __forceinline__ bf16x8 zero() {
+        union { uint4 u; bf16x8 v; } f;
+        f.u = uint4{0u, 0u, 0u, 0u};
+        return f.v;
+    }
+    // A operand from a row whose contraction index is contiguous (global or LDS).
+    static __device__ __forceinline__ bf16x8 load_row(const __bf16* rowp, int ks, int g) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(rowp + 32 * ks + 4 * g);
+        const uint2 hi = *reinterpret_cast<const uint2*>(rowp + 32 * ks + 16 + 4 * g);
+        union { uint4 u; bf16x8 v; } f;
+        f.u = uint4{lo.x, lo.y, hi.x, hi.y};
+        return f.v;
+    }
+};
+
+template <> struct Slots<TraitsF32> {
+    using Tr = TraitsF32;
+    static __device__ __forceinline__ int row(int ks, int g, int /*j*/) {
+        return 16 * (ks >> 2) + 4 * g + (ks & 3);
+    }
+    static __device__ __forceinline__ float from_acc(const floatx4* acc, int ks) {
+        return acc[ks >> 2][ks & 3];
+    }
+    static __device__ __forceinline__ float from_acc_scaled(const floatx4* acc, int ks, const float* s) {
+        return acc[ks >> 2][ks & 3] * s[0];
+    }
+    static constexpr int NSLOT = 1;
+    static __device__ __forceinline__ float zero() { return 0.f; }
+    static __device__ __forceinline__ float load_row(const float* rowp, int ks, int g) {
+        return rowp[16 * (ks >> 2) + 4 * g + (ks & 3)];
+    }
+};
+
+// Operand with contiguous contraction index, natural order (both operands
+// read from memory): lane group g holds K values [KW*ks + (KW/4)*g, +KW/4).
+template <typename Tr> struct Contig;
+template <> struct Contig<TraitsBf16> {
+    static __device__ __forceinline__ bf16x8 load(const __bf16* rowp, int ks, int g) {
+        union { uint4 u; bf16x8 v; } f;
+        f.u = *reinterpret_cast<const uint4*>(rowp + 32 * ks + 8 * g);
+        return f.v;
+    }
+    static __device__ __forceinline__ bf16x8 zero() {
+        union { uint4 u; bf16x8 v; } f;
+        f.u = uint4{0u, 0u, 0u, 0u};
+        return f.v;
+    }
+};
+template <> struct Contig<TraitsF32> {
+    static __device__ __forceinline__ float load(const float* rowp, int ks, int g) {
+        return rowp[4 * ks + g];
+    }
+    static __device__ __forceinline__ float zero() { return 0.f; }
+};
+
+// ---------------------------------------------------------------------------
+// Wave-wide (64-lane) inclusive scans
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_scan_add(float x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// log(exp(a) + exp(b)) without overflow; -inf is the identity.
+__device__ __forceinline__ float log_add_exp(float a, float b) {
+    const float m = fmaxf(a, b);
+    if (m == -INFINITY) return m;
+    return m + log1pf(expf(-fabsf(a - b)));
+}
+
+__device__ __forceinline__ float wave_scan_logaddexp(float x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float y = __shfl_up(x, off, 64);
+        if (lane >= off) x = log_add_exp(x, y);
+    }
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup -> (head, column slab) map that keeps the slabs of one head on
+// one XCD.  Workgroups are dispatched round-robin over the 8 XCDs in order
+// of their linear id, so ids with equal (id % 8) share an XCD and its L2.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void xcd_head_map(int id, int slabs, int BH, int& bh, int& slab) {
+    if ((BH & 7) == 0) {
+        const int x = id & 7, l = id >> 3;
+        bh = x * (BH >> 3) + l / slabs;
+        slab = l % slabs;
+    } else {
+        bh = id / slabs;
+        slab = id % slabs;
+    }
+}
+
+}  // namespace mdn

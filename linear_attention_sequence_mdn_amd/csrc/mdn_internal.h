@@ -1,0 +1,47 @@
+// mdn_internal.h -- argument blocks passed from the validated C entry points
+// (mdn_api.cpp) to the kernel launchers (mdn_step.hip, mdn_chunk.hip).
+// Everything here has already been checked on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mdn {
+
+struct StepArgs {
+    int64_t BH;
+    int dk, dv, dtype;
+    const void *q, *k, *v;
+    const float *alpha, *mu, *beta, *eta;
+    float *S, *M;
+    void* o;
+    void* stream;
+};
+
+struct ChunkArgs {
+    int64_t BH, T, NT;
+    int dk, dv, C, dtype;
+    const void *q, *k, *v;
+    const float *alpha, *mu, *beta, *eta;
+    const float *S0, *M0;
+    void* O;
+    float *ST, *MT;
+    void* Vt;
+    // per-chunk intermediates (workspace sections)
+    void* Tmat;      // [BH*NT][C][C] elem
+    void* Aqk;       // [BH*NT][C][C] elem
+    float* coef;     // [BH*NT][8][C]
+    float* gamma;    // [BH*NT][C][C] or nullptr (diagnostic only)
+    void* stream;
+};
+
+hipError_t launch_step(const StepArgs& a);
+// coefficient + intra-chunk stage (T, (QK^T) o Gamma, coefficients)
+hipError_t launch_chunk_intra(const ChunkArgs& a);
+// coefficient stage alone (diagnostic entry point)
+hipError_t launch_chunk_coef(const ChunkArgs& a);
+// sequential inter-chunk stage (vtilde, O, state carry)
+hipError_t launch_chunk_inter(const ChunkArgs& a);
+
+}  // namespace mdn

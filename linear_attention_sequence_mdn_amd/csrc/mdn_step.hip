@@ -1,0 +1,156 @@
+// mdn_step.hip -- one recurrent decode step of Momentum DeltaNet (gfx950).
+//
+// Recurrent form used for generation (ijyty.com article on MDN, section 6;
+// update equations of the MDN summary at paper.rainbus.top, method
+// walk-through step 1), per (batch, head), in fp32:
+//     vtilde = v - alpha * S^T k
+//     M      = mu * M - eta * k vtilde^T
+//     S      = alpha * S - beta * M
+//     o      = S^T q
+// The step is bound by HBM: S and M (dk x dv fp32 each) are read once and
+// written once; everything else is a few hundred bytes per head.  One
+// workgroup owns one head and keeps its whole S and M slab in registers:
+//   thread t: column group cg = t % CG (4 adjacent columns, one float4),
+//             row group    rg = t / CG (rows rg, rg + RG, rg + 2RG, ...).
+// A wave therefore reads whole 4*dv-byte rows with dwordx4 accesses.
+// The two reductions over dk (S^T k before the update, S^T q after it) go
+// through LDS.
+#include "mdn_device.h"
+#include "mdn_internal.h"
+
+namespace mdn {
+
+template <typename Tr, int DK, int DV>
+struct StepCfg {
+    static constexpr int CG = DV / 4;                       // float4 column groups
+    static constexpr int RG = (256 / CG) < DK ? (256 / CG) : DK;  // row groups
+    static constexpr int RPT = DK / RG;                     // rows per thread
+    static constexpr int NTHR = CG * RG;
+    static_assert(DK % RG == 0, "row groups must tile dk");
+};
+
+template <typename Tr, int DK, int DV>
+__global__ __launch_bounds__(256)
+void mdn_step_kernel(const typename Tr::elem* __restrict__ q,
+                     const typename Tr::elem* __restrict__ k,
+                     const typename Tr::elem* __restrict__ v,
+                     const float* __restrict__ alpha, const float* __restrict__ mu,
+                     const float* __restrict__ beta, const float* __restrict__ eta,
+                     float* __restrict__ S, float* __restrict__ M,
+                     typename Tr::elem* __restrict__ o)
+{
+    using Cfg = StepCfg<Tr, DK, DV>;
+    constexpr int CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT;
+    __shared__ float4 red[RG][CG];
+
+    const int bh = blockIdx.x;
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+
+    float* Sh = S + (size_t)bh * DK * DV;
+    float* Mh = M + (size_t)bh * DK * DV;
+
+    // Issue the state loads first: they are the whole cost of the step.
+    float4 s[RPT], m[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        s[i] = *reinterpret_cast<const float4*>(Sh + (size_t)row * DV + 4 * cg);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        m[i] = *reinterpret_cast<const float4*>(Mh + (size_t)row * DV + 4 * cg);
+    }
+    const float a = alpha[bh], mm = mu[bh], b = beta[bh], e = eta[bh];
+    float kk[RPT], qq[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        kk[i] = Tr::to_f(k[(size_t)bh * DK + row]);
+        qq[i] = Tr::to_f(q[(size_t)bh * DK + row]);
+    }
+    float vv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vv[c] = Tr::to_f(v[(size_t)bh * DV + 4 * cg + c]);
+
+    // u = S^T k over this thread's rows, then across row groups.
+    float4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        u.x += s[i].x * kk[i]; u.y += s[i].y * kk[i];
+        u.z += s[i].z * kk[i]; u.w += s[i].w * kk[i];
+    }
+    red[rg][cg] = u;
+    __syncthreads();
+    float4 ut = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+        const float4 p = red[r][cg];
+        ut.x += p.x; ut.y += p.y; ut.z += p.z; ut.w += p.w;
+    }
+    const float vt0 = vv[0] - a * ut.x, vt1 = vv[1] - a * ut.y;
+    const float vt2 = vv[2] - a * ut.z, vt3 = vv[3] - a * ut.w;
+
+    // M <- mu M - eta k vtilde^T ;  S <- alpha S - beta M ;  partial o = S^T q
+    float4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float ek = e * kk[i];
+        float4 mn, sn;
+        mn.x = mm * m[i].x - ek * vt0; mn.y = mm * m[i].y - ek * vt1;
+        mn.z = mm * m[i].z - ek * vt2; mn.w = mm * m[i].w - ek * vt3;
+        sn.x = a * s[i].x - b * mn.x; sn.y = a * s[i].y - b * mn.y;
+        sn.z = a * s[i].z - b * mn.z; sn.w = a * s[i].w - b * mn.w;
+        const int row = rg + RG * i;
+        *reinterpret_cast<float4*>(Mh + (size_t)row * DV + 4 * cg) = mn;
+        *reinterpret_cast<float4*>(Sh + (size_t)row * DV + 4 * cg) = sn;
+        w.x += sn.x * qq[i]; w.y += sn.y * qq[i]; w.z += sn.z * qq[i]; w.w += sn.w * qq[i];
+    }
+    __syncthreads();          // every thread has read red[] for u
+    red[rg][cg] = w;
+    __syncthreads();
+    if (rg == 0) {
+        float4 ot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const float4 p = red[r][cg];
+            ot.x += p.x; ot.y += p.y; ot.z += p.z; ot.w += p.w;
+        }
+        typename Tr::elem* op = o + (size_t)bh * DV + 4 * cg;
+        op[0] = Tr::from_f(ot.x); op[1] = Tr::from_f(ot.y);
+        op[2] = Tr::from_f(ot.z); op[3] = Tr::from_f(ot.w);
+    }
+}
+
+template <typename Tr, int DK, int DV>
+static hipError_t launch_step_t(const StepArgs& a)
+{
+    using Cfg = StepCfg<Tr, DK, DV>;
+    using E = typename Tr::elem;
+    hipLaunchKernelGGL((mdn_step_kernel<Tr, DK, DV>), dim3((unsigned)a.BH), dim3(Cfg::NTHR), 0,
+                       (hipStream_t)a.stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v,
+                       a.alpha, a.mu, a.beta, a.eta, a.S, a.M, (E*)a.o);
+    return hipGetLastError();
+}
+
+template <typename Tr>
+static hipError_t launch_step_d(const StepArgs& a)
+{
+    switch (a.dk) {
+    case 16: return launch_step_t<Tr, 16, 16>(a);
+    case 32: return launch_step_t<Tr, 32, 32>(a);
+    case 64: return launch_step_t<Tr, 64, 64>(a);
+    case 128: return launch_step_t<Tr, 128, 128>(a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_step(const StepArgs& a)
+{
+    if (a.BH == 0) return hipSuccess;
+    return a.dtype == 1 ? launch_step_d<TraitsBf16>(a) : launch_step_d<TraitsF32>(a);
+}
+
+}  // namespace mdn

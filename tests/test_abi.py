@@ -1,0 +1,210 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+``include/mdn.h`` declares, and rejects bad arguments on the host before any
+HIP call (fake device addresses are never dereferenced by validation)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_sequence_mdn_amd as mdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mdn.h")
+
+OK, NULL_ARG, BAD_SHAPE, UNSUPPORTED, ALIAS, WORKSPACE, ALIGN = 0, 1, 2, 3, 4, 5, 6
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mdn.LIB_PATH):
+        pytest.fail("libmdn.so not built: run __graft_entry__.build() first")
+    return mdn.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("mdn_chunk_fwd", "mdn_step", "mdn_chunk_fwd_workspace_bytes", "mdn_chunk_intra",
+              "mdn_chunk_inter", "mdn_chunk_coef", "mdn_status_string", "mdn_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", mdn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        getattr(L, n)   # resolvable through the loader too
+
+
+def test_abi_version(L):
+    assert L.mdn_abi_version() == 2
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.mdn_status_string(s).startswith(b"MDN_")
+    assert L.mdn_status_string(99) == b"unknown mdn status"
+
+
+def test_workspace_bytes(L):
+    # T matrices + (QK^T) o Gamma (bf16, C x C per chunk) + 8 coefficient rows (fp32)
+    B, H, T, d, C = 8, 8, 4096, 128, 64
+    tiles = B * H * (T // C)
+    expect = 2 * tiles * C * C * 2 + tiles * 8 * C * 4
+    assert mdn.chunk_fwd_workspace_bytes(B, H, T, d, d, C, mdn.MDN_BF16) == expect
+    assert L.mdn_chunk_fwd_workspace_bytes(1, 1, 0, 16, 16, 16, 0) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert L.mdn_chunk_fwd_workspace_bytes(1, 1, 64, 48, 48, 16, 0) == bad
+    assert L.mdn_chunk_fwd_workspace_bytes(1, 1, 64, 16, 16, 16, 1) == bad    # bf16 needs d >= 32
+    assert L.mdn_chunk_fwd_workspace_bytes(-1, 1, 64, 16, 16, 16, 0) == bad
+
+
+# fake, 256-byte aligned, non-overlapping device addresses
+BASE = 1 << 40
+
+
+def addrs(n, stride=1 << 32):
+    return [ctypes.c_void_p(BASE + i * stride) for i in range(n)]
+
+
+def chunk_call(L, B=1, H=1, T=64, d=16, C=16, dt=0, ptrs=None, ws_bytes=None, S0=None, M0=None):
+    p = addrs(14) if ptrs is None else ptrs
+    q, k, v, a, m, b, e, s0, m0, O, ST, MT, Vt, ws = p
+    if S0 is not None:
+        s0 = S0
+    if M0 is not None:
+        m0 = M0
+    n = L.mdn_chunk_fwd_workspace_bytes(B, H, T, d, d, C, dt) if ws_bytes is None else ws_bytes
+    return L.mdn_chunk_fwd(B, H, T, d, d, C, dt, q, k, v, a, m, b, e, s0, m0, O, ST, MT, Vt,
+                           ws, n, None)
+
+
+def test_chunk_unsupported(L):
+    assert chunk_call(L, d=48) == UNSUPPORTED
+    assert chunk_call(L, C=128) == UNSUPPORTED
+    assert chunk_call(L, d=16, dt=1) == UNSUPPORTED
+    assert chunk_call(L, dt=7) == UNSUPPORTED
+    p = addrs(14)
+    assert L.mdn_chunk_fwd(1, 1, 64, 32, 64, 32, 1, *p[:13], p[13], 1 << 20, None) == UNSUPPORTED
+
+
+def test_chunk_bad_shape(L):
+    assert chunk_call(L, B=-1) == BAD_SHAPE
+    assert chunk_call(L, T=-5) == BAD_SHAPE
+    assert chunk_call(L, B=1 << 30, H=1 << 30, T=1 << 20) == BAD_SHAPE
+
+
+def test_chunk_empty_batch_is_noop(L):
+    assert chunk_call(L, B=0) == OK
+    assert chunk_call(L, H=0, ptrs=[None] * 14) == OK
+
+
+def test_chunk_null_args(L):
+    p = addrs(14)
+    for i in (0, 1, 2, 3, 4, 5, 6, 9, 10, 11, 12):
+        q = list(p)
+        q[i] = None
+        assert chunk_call(L, ptrs=q) == NULL_ARG, i
+    q = list(p)
+    q[7] = q[8] = None          # S0, M0 may be NULL (zero state)
+    assert chunk_call(L, ptrs=q, ws_bytes=0) == WORKSPACE
+
+
+def test_chunk_workspace(L):
+    need = L.mdn_chunk_fwd_workspace_bytes(1, 1, 64, 16, 16, 16, 0)
+    assert chunk_call(L, ws_bytes=need - 1) == WORKSPACE
+    q = addrs(14)
+    q[13] = None
+    assert chunk_call(L, ptrs=q) == WORKSPACE
+
+
+def test_chunk_alignment(L):
+    q = addrs(14)
+    q[4] = ctypes.c_void_p(q[4].value + 4)
+    assert chunk_call(L, ptrs=q) == ALIGN
+
+
+def test_chunk_alias(L):
+    p = addrs(14)
+    q = list(p)
+    q[9] = q[0]                 # O on top of q
+    assert chunk_call(L, ptrs=q) == ALIAS
+    q = list(p)
+    q[12] = ctypes.c_void_p(p[9].value + 256)   # Vtilde overlapping O
+    assert chunk_call(L, ptrs=q) == ALIAS
+    q = list(p)
+    q[13] = q[3]                # workspace on alpha
+    assert chunk_call(L, ptrs=q) == ALIAS
+    q = list(p)
+    q[10] = ctypes.c_void_p(p[7].value + 256)   # S_T overlapping S0 but not equal
+    assert chunk_call(L, ptrs=q) == ALIAS
+
+
+def step_call(L, B=2, H=2, d=16, dt=0, ptrs=None):
+    p = addrs(10) if ptrs is None else ptrs
+    return L.mdn_step(B, H, d, d, dt, *p, None)
+
+
+def test_step_validation(L):
+    assert step_call(L, d=8) == UNSUPPORTED
+    assert step_call(L, dt=5) == UNSUPPORTED
+    assert step_call(L, B=-2) == BAD_SHAPE
+    assert step_call(L, B=0) == OK
+    p = addrs(10)
+    for i in range(10):
+        q = list(p)
+        q[i] = None
+        assert step_call(L, ptrs=q) == NULL_ARG, i
+    q = list(p)
+    q[8] = q[7]                 # M on top of S
+    assert step_call(L, ptrs=q) == ALIAS
+    q = list(p)
+    q[9] = q[0]                 # o on top of q
+    assert step_call(L, ptrs=q) == ALIAS
+    q = list(p)
+    q[7] = ctypes.c_void_p(p[7].value + 8)
+    assert step_call(L, ptrs=q) == ALIGN
+
+
+def test_coef_validation(L):
+    p = addrs(6)
+    assert L.mdn_chunk_coef(1, 1, 64, 48, *p, None) == UNSUPPORTED
+    assert L.mdn_chunk_coef(1, 1, -1, 16, *p, None) == BAD_SHAPE
+    assert L.mdn_chunk_coef(1, 1, 0, 16, *p, None) == OK
+    q = list(p)
+    q[4] = None
+    assert L.mdn_chunk_coef(1, 1, 64, 16, *q, None) == NULL_ARG
+    q = list(p)
+    q[5] = q[4]
+    assert L.mdn_chunk_coef(1, 1, 64, 16, *q, None) == ALIAS
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mdn, "_lib", None)
+    monkeypatch.setattr(mdn, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        mdn.lib()
+
+
+def test_stage_entry_points_validate(L):
+    p = addrs(14)
+    q, k, v, a, m, b, e, s0, m0, O, ST, MT, Vt, ws = p
+    need = L.mdn_chunk_fwd_workspace_bytes(1, 1, 64, 16, 16, 16, 0)
+    assert L.mdn_chunk_intra(1, 1, 64, 16, 16, 16, 0, q, k, a, m, b, e, ws, need - 1, None) == WORKSPACE
+    assert L.mdn_chunk_intra(1, 1, 64, 16, 16, 16, 0, None, k, a, m, b, e, ws, need, None) == NULL_ARG
+    assert L.mdn_chunk_intra(1, 1, 64, 48, 48, 16, 0, q, k, a, m, b, e, ws, need, None) == UNSUPPORTED
+    assert L.mdn_chunk_intra(1, 1, 64, 16, 16, 16, 0, q, k, a, m, b, e, q, need, None) == ALIAS
+    assert L.mdn_chunk_inter(1, 1, 64, 16, 16, 16, 0, q, k, v, a, m, b, e, s0, m0, O, ST, MT, None,
+                             ws, need, None) == NULL_ARG
+    assert L.mdn_chunk_inter(1, 1, 64, 16, 16, 16, 0, q, k, v, a, m, b, e, s0, m0, O, ST, MT, O,
+                             ws, need, None) == ALIAS
