@@ -176,9 +176,195 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
 
 // ---------------------------------------------------------------------------
 // mdn_inter_kernel
+//
+// One workgroup owns a slab of 16*NCOL state columns of one head and runs
+// the chunks of that head in order.  For every 16-column tile there are two
+// waves that split the work of a chunk by state:
+//   S-wave: W = V - Diag(abar) K S + Diag(alpha b_prev) K M, vtilde = T W,
+//           S <- abar_C S - b_C M + K^T Diag(gS) vtilde        (S in registers)
+//   M-wave: Q S and Q M for the output, M <- mubar_C M - K^T Diag(gM) vtilde,
+//           O = Diag(abar) Q S - Diag(b) Q M + Aqk vtilde     (M in registers)
+// The two exchange the chunk-start states (bf16 S, fp32 M) and vtilde through
+// LDS, with two workgroup barriers per chunk.
+//
+// Every per-chunk input (K, Q, T, Aqk, the coefficient rows and the V slab)
+// is copied to LDS by direct global->LDS loads, 16 bytes per lane, into one
+// of two buffers: chunk n+1 is in flight while chunk n is computed.  K, Q, T
+// and Aqk rows are XOR-swizzled by 16-byte piece (piece p of row r lives at
+// p ^ (r mod pieces-per-row)) so that the 16 rows an operand read touches
+// fall in different LDS banks.  K^T, the A operand of the state updates, is
+// read from the row-major K tile with the LDS transpose read (bf16).
+// vtilde and O go through an LDS tile so that they leave as full 16-byte
+// stores.  Rows past the end of a ragged last chunk are copied from the last
+// valid row: they only ever meet zero weights (T and Aqk are lower
+// triangular, gS = gM = 0 there) and are never stored.
 // ---------------------------------------------------------------------------
-template <typename Tr, int DK, int DV, int C, int NW>
-__global__ __launch_bounds__(64 * NW)
+template <typename Tr, int D, int C, int NCOL, int NBUF>
+struct InterLayout {
+    using E = typename Tr::elem;
+    using frag = typename Tr::frag;
+    static constexpr int ES = sizeof(E);
+    static constexpr int PK = D * ES / 16;            // 16-byte pieces per K/Q row
+    static constexpr int PT = C * ES / 16;            // pieces per T/Aqk row
+    static constexpr int PV = 16 * NCOL * ES / 16;    // pieces per V-slab / out row
+    static constexpr int PC = MDN_COEF_ROWS * C * 4 / 16;
+    static_assert((PK & (PK - 1)) == 0 && (PT & (PT - 1)) == 0, "power-of-two rows");
+    // per-buffer regions (bytes)
+    static constexpr int K0 = 0;
+    static constexpr int Q0 = K0 + C * PK * 16;
+    static constexpr int T0 = Q0 + C * PK * 16;
+    static constexpr int A0 = T0 + C * PT * 16;
+    static constexpr int CF0 = A0 + C * PT * 16;
+    static constexpr int V0 = CF0 + PC * 16;
+    static constexpr int BUF = V0 + C * PV * 16;
+    // exchange areas, per column tile (lane-major)
+    static constexpr int KSD = D / Tr::KW;
+    static constexpr int XS_B = 64 * KSD * (int)sizeof(frag);   // bf16/fp32 S operands
+    static constexpr int XM_B = 64 * (D / 16) * 16;             // fp32 M accumulators
+    static constexpr int XV_B = 64 * (C / 16) * 16;             // fp32 vtilde accumulators
+    static constexpr int XS0 = NBUF * BUF;
+    static constexpr int XM0 = XS0 + NCOL * XS_B;
+    static constexpr int XV0 = XM0 + NCOL * XM_B;
+    static constexpr int OV0 = XV0 + NCOL * XV_B;               // vtilde out tile
+    static constexpr int OO0 = OV0 + C * PV * 16;               // O out tile
+    static constexpr int TOTAL = OO0 + C * PV * 16;
+};
+
+template <typename Tr, int D, int C>
+struct InterPick {
+    static constexpr int LIMIT = 160 * 1024;
+    static constexpr int NCOL = (D >= 32 && InterLayout<Tr, D, C, 2, 1>::TOTAL <= LIMIT) ? 2 : 1;
+    static constexpr int NBUF = InterLayout<Tr, D, C, NCOL, 2>::TOTAL <= LIMIT ? 2 : 1;
+};
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// byte offset of (row r, byte b) in a row of P 16-byte pieces, XOR-swizzled
+template <int P>
+__device__ __forceinline__ int swz(int r, int b) {
+    return r * P * 16 + ((((b >> 4) ^ (r & (P - 1)))) << 4) + (b & 15);
+}
+
+// A operand of a product whose B operand comes from accumulators (slot map),
+// from a swizzled LDS tile whose rows hold the contraction index.
+template <typename Tr, int P> struct LdsA;
+template <int P> struct LdsA<TraitsBf16, P> {
+    static __device__ __forceinline__ bf16x8 load(const char* tile, int row, int ks, int g) {
+        const int c0 = 32 * ks + 4 * g;                 // elements
+        const uint2 lo = *reinterpret_cast<const uint2*>(tile + swz<P>(row, 2 * c0));
+        const uint2 hi = *reinterpret_cast<const uint2*>(tile + swz<P>(row, 2 * (c0 + 16)));
+        union { uint4 u; bf16x8 v; } f;
+        f.u = uint4{lo.x, lo.y, hi.x, hi.y};
+        return f.v;
+    }
+};
+template <int P> struct LdsA<TraitsF32, P> {
+    static __device__ __forceinline__ float load(const char* tile, int row, int ks, int g) {
+        const int c = 16 * (ks >> 2) + 4 * g + (ks & 3);
+        return *reinterpret_cast<const float*>(tile + swz<P>(row, 4 * c));
+    }
+};
+
+// K^T operand of the state update for d-tile td, contraction step ks.
+template <typename Tr, int P> struct KtOperand;
+template <int P> struct KtOperand<TraitsBf16, P> {
+    static __device__ __forceinline__ bf16x8 load(const char* Kt, int td, int ks, int lane) {
+        // Transpose read: in each 16-lane group, result lane i takes element
+        // i%4 of source lane 4j + i/4.  Source lane s of group g points at
+        // row 32ks + 4g + s/4 (+16 for the second half), columns
+        // 16td + 4(s%4) .. +3, so lane i receives K[32ks + 4g + j][16td + i]
+        // for j = 0..3: exactly slots j (and 4 + j) of the slot map.
+        const int g = lane >> 4, s = lane & 15;
+        const int r0 = 32 * ks + 4 * g + (s >> 2);
+        const int b = 2 * (16 * td + 4 * (s & 3));
+        union { shortx4 h[2]; bf16x8 v; } f;
+        f.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(Kt + swz<P>(r0, b)));
+        f.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(Kt + swz<P>(r0 + 16, b)));
+        return f.v;
+    }
+};
+template <int P> struct KtOperand<TraitsF32, P> {
+    static __device__ __forceinline__ float load(const char* Kt, int td, int ks, int lane) {
+        const int g = lane >> 4, m = lane & 15;
+        const int r = 16 * (ks >> 2) + 4 * g + (ks & 3);
+        return *reinterpret_cast<const float*>(Kt + swz<P>(r, 4 * (16 * td + m)));
+    }
+};
+
+// Issue the direct global->LDS copies of one chunk into buffer `buf`.
+// Instruction i of a region covers its 16-byte slots [64 i, 64 i + 64).
+template <typename LT, typename E, int D, int C, int NW>
+__device__ __forceinline__ void stage_chunk(char* buf, const E* __restrict__ k, const E* __restrict__ q,
+                                            const E* __restrict__ v, const E* __restrict__ Tm,
+                                            const E* __restrict__ Aqk, const float* __restrict__ coef,
+                                            size_t rowbase, int valid, size_t tile, int col0,
+                                            int wave, int lane)
+{
+    constexpr int EPS = 16 / LT::ES;                 // elements per 16-byte piece
+    // K and Q: C rows of PK pieces, swizzled; rows past `valid` repeat the last one
+    constexpr int NK = (C * LT::PK + 63) / 64;
+    for (int i = wave; i < 2 * NK; i += NW) {
+        const bool isq = i >= NK;
+        const int s = (isq ? i - NK : i) * 64 + lane;
+        const int r = s / LT::PK, ph = s % LT::PK;
+        const int p = ph ^ (r & (LT::PK - 1));
+        const int rr = r < valid ? r : valid - 1;
+        const E* src = (isq ? q : k) + (rowbase + rr) * D + p * EPS;
+        if (s < C * LT::PK)
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + (isq ? LT::Q0 : LT::K0) + (s - lane) * 16),
+                                             16, 0, 0);
+    }
+    // T and Aqk: C rows of PT pieces, swizzled
+    constexpr int NT_ = (C * LT::PT + 63) / 64;
+    for (int i = wave; i < 2 * NT_; i += NW) {
+        const bool isa = i >= NT_;
+        const int s = (isa ? i - NT_ : i) * 64 + lane;
+        const int r = s / LT::PT, ph = s % LT::PT;
+        const int p = ph ^ (r & (LT::PT - 1));
+        const E* src = (isa ? Aqk : Tm) + tile * C * C + r * C + p * EPS;
+        if (s < C * LT::PT)
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + (isa ? LT::A0 : LT::T0) + (s - lane) * 16),
+                                             16, 0, 0);
+    }
+    // coefficient rows (plain) and the V slab (plain)
+    constexpr int NC = (LT::PC + 63) / 64;
+    constexpr int NV = (C * LT::PV + 63) / 64;
+    for (int i = wave; i < NC + NV; i += NW) {
+        if (i < NC) {
+            const int s = i * 64 + lane;
+            if (s < LT::PC)
+                __builtin_amdgcn_global_load_lds(coef + tile * MDN_COEF_ROWS * C + s * 4,
+                                                 (lds_void*)(buf + LT::CF0 + i * 64 * 16), 16, 0, 0);
+        } else {
+            const int s = (i - NC) * 64 + lane;
+            const int r = s / LT::PV, p = s % LT::PV;
+            const int rr = r < valid ? r : valid - 1;
+            if (s < C * LT::PV)
+                __builtin_amdgcn_global_load_lds(v + (rowbase + rr) * D + col0 + p * EPS,
+                                                 (lds_void*)(buf + LT::V0 + (i - NC) * 64 * 16), 16, 0, 0);
+        }
+    }
+}
+
+// Copy an out tile (C rows x 16*NCOL elements in LDS) to rows [0, valid) of
+// a row-major [.., D] output; `dst` points at the chunk's first row.
+template <typename LT, typename E, int D, int C, int NW>
+__device__ __forceinline__ void copy_out(const char* tile, E* __restrict__ dst, int valid, int col0, int tid)
+{
+    constexpr int EPS = 16 / LT::ES;
+    for (int s = tid; s < C * LT::PV; s += 64 * NW) {
+        const int r = s / LT::PV, p = s % LT::PV;
+        if (r < valid)
+            *reinterpret_cast<uint4*>(dst + (size_t)r * D + col0 + p * EPS) =
+                *reinterpret_cast<const uint4*>(tile + s * 16);
+    }
+}
+
+template <typename Tr, int D, int C, int NCOL, int NBUF>
+__global__ __launch_bounds__(128 * NCOL)
 void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                       const typename Tr::elem* __restrict__ k,
                       const typename Tr::elem* __restrict__ v,
@@ -193,168 +379,221 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 {
     using E = typename Tr::elem;
     using SL = Slots<Tr>;
+    using LT = InterLayout<Tr, D, C, NCOL, NBUF>;
     using frag = typename Tr::frag;
-    constexpr int KW = Tr::KW, NSL = SL::NSLOT;
-    constexpr int NDT = DK / 16, NCT = C / 16, KSD = DK / KW, KSC = C / KW;
-    constexpr int KTS = C + 8;                       // row stride of the K^T tile
-    constexpr int VEC = 16 / sizeof(E);              // elements per 16-byte load
-    constexpr int SLABS = DV / (16 * NW);
-    __shared__ __attribute__((aligned(16))) E sKt[DK * KTS];
+    constexpr int NSL = SL::NSLOT;
+    constexpr int NW = 2 * NCOL;
+    constexpr int NDT = D / 16, NCT = C / 16, KSD = D / Tr::KW, KSC = C / Tr::KW;
+    constexpr int SLABS = D / (16 * NCOL);
+    constexpr int OW = 16 * NCOL;                     // out-tile row length (elements)
+    __shared__ __attribute__((aligned(16))) char smem[LT::TOTAL];
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, nn = lane & 15;
+    const bool swave = wave < NCOL;                   // S-wave or M-wave
+    const int ct = swave ? wave : wave - NCOL;        // column tile within the slab
     int bh, slab;
     xcd_head_map(blockIdx.x, SLABS, BH, bh, slab);
-    const int col = (slab * NW + wave) * 16 + nn;
+    const int col0 = slab * OW;
+    const int col = col0 + 16 * ct + nn;
 
-    const size_t sbase = (size_t)bh * DK * DV;
-    floatx4 S[NDT], M[NDT];
+    frag* XS = reinterpret_cast<frag*>(smem + LT::XS0 + ct * LT::XS_B) + lane * KSD;
+    floatx4* XM = reinterpret_cast<floatx4*>(smem + LT::XM0 + ct * LT::XM_B) + lane * NDT;
+    floatx4* XV = reinterpret_cast<floatx4*>(smem + LT::XV0 + ct * LT::XV_B) + lane * NCT;
+    E* OVt = reinterpret_cast<E*>(smem + LT::OV0);
+    E* OOt = reinterpret_cast<E*>(smem + LT::OO0);
+
+    // the wave's own state: S (S-wave) or M (M-wave)
+    const size_t sbase = (size_t)bh * D * D;
+    const float* X0 = swave ? S0 : M0;
+    floatx4 X[NDT];
+    if (X0) {
 #pragma unroll
-    for (int td = 0; td < NDT; ++td)
+        for (int td = 0; td < NDT; ++td)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const size_t off = sbase + (size_t)(16 * td + 4 * g + e) * DV + col;
-            S[td][e] = S0 ? S0[off] : 0.f;
-            M[td][e] = M0 ? M0[off] : 0.f;
-        }
+            for (int e = 0; e < 4; ++e) X[td][e] = X0[sbase + (size_t)(16 * td + 4 * g + e) * D + col];
+    } else {
+#pragma unroll
+        for (int td = 0; td < NDT; ++td) X[td] = zero4();
+    }
+    if (swave) {
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) XS[ks] = SL::from_acc(X, ks);
+    } else {
+#pragma unroll
+        for (int td = 0; td < NDT; ++td) XM[td] = X[td];
+    }
+
+    auto valid_of = [&](int64_t n) { return (int)((T - n * C) < C ? (T - n * C) : C); };
+    if (NT > 0 && NBUF == 2)
+        stage_chunk<LT, E, D, C, NW>(smem, k, q, v, Tm, Aqk, coef, (size_t)bh * T, valid_of(0),
+                                     (size_t)bh * NT, col0, wave, lane);
 
     for (int64_t n = 0; n < NT; ++n) {
-        const int64_t t0 = n * C;
-        const int valid = (int)((T - t0) < C ? (T - t0) : C);
+        const int valid = valid_of(n);
         const size_t tile = (size_t)bh * NT + n;
-        const size_t rowbase = (size_t)bh * T + t0;
-        const float* cf = coef + tile * MDN_COEF_ROWS * C;
-        const E* kc = k + rowbase * DK;
-        const E* qc = q + rowbase * DK;
-
-        // K chunk -> LDS, transposed: sKt[d][c] = K[c][d]
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < C * (DK / VEC); idx += 64 * NW) {
-            const int c = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
-            union { uint4 u; E x[VEC]; } ld;
-            ld.u = c < valid ? *reinterpret_cast<const uint4*>(kc + (size_t)c * DK + d0)
-                             : uint4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) sKt[(d0 + i) * KTS + c] = ld.x[i];
+        const size_t rowbase = (size_t)bh * T + n * C;
+        const char* cur = smem + (NBUF == 2 ? (int)(n & 1) * LT::BUF : 0);
+        if constexpr (NBUF == 2) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();                    // B0: chunk n staged, exchanges of n-1 visible
+            if (n + 1 < NT)
+                stage_chunk<LT, E, D, C, NW>(smem + (int)((n + 1) & 1) * LT::BUF, k, q, v, Tm, Aqk, coef,
+                                             rowbase + C, valid_of(n + 1), tile + 1, col0, wave, lane);
+        } else {
+            __syncthreads();
+            stage_chunk<LT, E, D, C, NW>(smem, k, q, v, Tm, Aqk, coef, rowbase, valid, tile, col0, wave, lane);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();                    // B0
         }
-        __syncthreads();
+        if (n > 0)                              // O of chunk n-1 (written before B0)
+            copy_out<LT, E, D, C, NW>(smem + LT::OO0, O + (rowbase - C) * D, C, col0, tid);
 
-        // state as B operands (contraction over the dk rows)
+        const char* Kl = cur + LT::K0;
+        const char* Ql = cur + LT::Q0;
+        const char* Tl = cur + LT::T0;
+        const char* Al = cur + LT::A0;
+        const float* cf = reinterpret_cast<const float*>(cur + LT::CF0);
+        const E* Vl = reinterpret_cast<const E*>(cur + LT::V0) + 16 * ct + nn;
+
+        // chunk-start states as B operands
         frag Sb[KSD], Mb[KSD];
+        floatx4 Mf[NDT];
+        if (swave) {
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) { Sb[ks] = SL::from_acc(S, ks); Mb[ks] = SL::from_acc(M, ks); }
-
-        // W = V - Diag(abar) K S + Diag(alpha b_prev) K M
-        floatx4 W[NCT];
+            for (int td = 0; td < NDT; ++td) Mf[td] = XM[td];
 #pragma unroll
-        for (int tc = 0; tc < NCT; ++tc) {
-            const int r = 16 * tc + nn;
-            floatx4 ks_ = zero4(), km_ = zero4();
+            for (int ks = 0; ks < KSD; ++ks) { Sb[ks] = SL::from_acc(X, ks); Mb[ks] = SL::from_acc(Mf, ks); }
+        } else {
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                const frag a = r < valid ? SL::load_row(kc + (size_t)r * DK, ks, g) : SL::zero();
-                ks_ = Tr::mma(a, Sb[ks], ks_);
-                km_ = Tr::mma(a, Mb[ks], km_);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * tc + 4 * g + e;
-                const float vv = rr < valid ? Tr::to_f(v[(rowbase + rr) * DV + col]) : 0.f;
-                W[tc][e] = vv - cf[MDN_COEF_ABAR * C + rr] * ks_[e] + cf[MDN_COEF_ABP * C + rr] * km_[e];
-            }
+            for (int ks = 0; ks < KSD; ++ks) { Sb[ks] = XS[ks]; Mb[ks] = SL::from_acc(X, ks); }
         }
 
-        // vtilde = T W
-        frag Wb[KSC];
+        floatx4 Vx[NCT];      // S-wave: vtilde
+        floatx4 Op[NCT];      // M-wave: Diag(abar) Q S - Diag(b) Q M
+        if (swave) {
+            // W = V - Diag(abar) K S + Diag(alpha b_prev) K M
+            floatx4 W[NCT];
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) Wb[ks] = SL::from_acc(W, ks);
-        floatx4 Vx[NCT];
-        const E* Tt = Tm + tile * C * C;
+            for (int tc = 0; tc < NCT; ++tc) {
+                floatx4 ks_ = zero4(), km_ = zero4();
 #pragma unroll
-        for (int tc = 0; tc < NCT; ++tc) {
-            floatx4 acc = zero4();
+                for (int ks = 0; ks < KSD; ++ks) {
+                    const frag a = LdsA<Tr, LT::PK>::load(Kl, 16 * tc + nn, ks, g);
+                    ks_ = Tr::mma(a, Sb[ks], ks_);
+                    km_ = Tr::mma(a, Mb[ks], km_);
+                }
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks)
-                acc = Tr::mma(SL::load_row(Tt + (16 * tc + nn) * C, ks, g), Wb[ks], acc);
-            Vx[tc] = acc;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * tc + 4 * g + e;
-                if (rr < valid) Vt[(rowbase + rr) * DV + col] = Tr::from_f(acc[e]);
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = 16 * tc + 4 * g + e;
+                    W[tc][e] = Tr::to_f(Vl[rr * OW]) - cf[MDN_COEF_ABAR * C + rr] * ks_[e]
+                               + cf[MDN_COEF_ABP * C + rr] * km_[e];
+                }
             }
-        }
-
-        // O = Diag(abar) Q S - Diag(b) Q M + Aqk vtilde   (chunk-start S, M)
-        frag Vb[KSC];
+            // vtilde = T W
+            frag Wb[KSC];
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) Vb[ks] = SL::from_acc(Vx, ks);
-        const E* Aq = Aqk + tile * C * C;
+            for (int ks = 0; ks < KSC; ++ks) Wb[ks] = SL::from_acc(W, ks);
 #pragma unroll
-        for (int tc = 0; tc < NCT; ++tc) {
-            const int r = 16 * tc + nn;
-            floatx4 qs = zero4(), qm = zero4(), ai = zero4();
+            for (int tc = 0; tc < NCT; ++tc) {
+                floatx4 acc = zero4();
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                const frag a = r < valid ? SL::load_row(qc + (size_t)r * DK, ks, g) : SL::zero();
-                qs = Tr::mma(a, Sb[ks], qs);
-                qm = Tr::mma(a, Mb[ks], qm);
+                for (int ks = 0; ks < KSC; ++ks)
+                    acc = Tr::mma(LdsA<Tr, LT::PT>::load(Tl, 16 * tc + nn, ks, g), Wb[ks], acc);
+                Vx[tc] = acc;
+                XV[tc] = acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) OVt[(16 * tc + 4 * g + e) * OW + 16 * ct + nn] = Tr::from_f(acc[e]);
             }
+        } else {
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks)
-                ai = Tr::mma(SL::load_row(Aq + (16 * tc + nn) * C, ks, g), Vb[ks], ai);
+            for (int tc = 0; tc < NCT; ++tc) {
+                floatx4 qs = zero4(), qm = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * tc + 4 * g + e;
-                if (rr < valid) {
-                    const float o = cf[MDN_COEF_ABAR * C + rr] * qs[e] - cf[MDN_COEF_B * C + rr] * qm[e] + ai[e];
-                    O[(rowbase + rr) * DV + col] = Tr::from_f(o);
+                for (int ks = 0; ks < KSD; ++ks) {
+                    const frag a = LdsA<Tr, LT::PK>::load(Ql, 16 * tc + nn, ks, g);
+                    qs = Tr::mma(a, Sb[ks], qs);
+                    qm = Tr::mma(a, Mb[ks], qm);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = 16 * tc + 4 * g + e;
+                    Op[tc][e] = cf[MDN_COEF_ABAR * C + rr] * qs[e] - cf[MDN_COEF_B * C + rr] * qm[e];
                 }
             }
         }
+        __syncthreads();                        // B1: vtilde of chunk n visible
+        copy_out<LT, E, D, C, NW>(smem + LT::OV0, Vt + rowbase * D, valid, col0, tid);
 
-        // S <- abar_C S - b_C M + K^T Diag(gS) vtilde ; M <- mubar_C M - K^T Diag(gM) vtilde
         const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
         const float bC = cf[MDN_COEF_B * C + C - 1];
         const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
-        frag VS[KSC], VM[KSC];
-#pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) {
-            float sS[NSL], sM[NSL];
-#pragma unroll
-            for (int j = 0; j < NSL; ++j) {
-                const int rr = SL::row(ks, g, j);
-                sS[j] = cf[MDN_COEF_GS * C + rr];
-                sM[j] = -cf[MDN_COEF_GM * C + rr];
-            }
-            VS[ks] = SL::from_acc_scaled(Vx, ks, sS);
-            VM[ks] = SL::from_acc_scaled(Vx, ks, sM);
-        }
-#pragma unroll
-        for (int td = 0; td < NDT; ++td) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float s_ = abarC * S[td][e] - bC * M[td][e];
-                M[td][e] = mubarC * M[td][e];
-                S[td][e] = s_;
-            }
-            const E* ktr = sKt + (16 * td + nn) * KTS;
+        if (swave) {
+            // S <- abar_C S - b_C M + K^T Diag(gS) vtilde
+            frag VS[KSC];
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
-                const frag a = SL::load_row(ktr, ks, g);
-                S[td] = Tr::mma(a, VS[ks], S[td]);
-                M[td] = Tr::mma(a, VM[ks], M[td]);
+                float sc[NSL];
+#pragma unroll
+                for (int j = 0; j < NSL; ++j) sc[j] = cf[MDN_COEF_GS * C + SL::row(ks, g, j)];
+                VS[ks] = SL::from_acc_scaled(Vx, ks, sc);
+            }
+#pragma unroll
+            for (int td = 0; td < NDT; ++td) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) X[td][e] = abarC * X[td][e] - bC * Mf[td][e];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks)
+                    X[td] = Tr::mma(KtOperand<Tr, LT::PK>::load(Kl, td, ks, lane), VS[ks], X[td]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) XS[ks] = SL::from_acc(X, ks);
+        } else {
+            floatx4 Vv[NCT];
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc) Vv[tc] = XV[tc];
+            frag VM[KSC], Vb[KSC];
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                float sc[NSL];
+#pragma unroll
+                for (int j = 0; j < NSL; ++j) sc[j] = -cf[MDN_COEF_GM * C + SL::row(ks, g, j)];
+                VM[ks] = SL::from_acc_scaled(Vv, ks, sc);
+                Vb[ks] = SL::from_acc(Vv, ks);
+            }
+            // M <- mubar_C M - K^T Diag(gM) vtilde
+#pragma unroll
+            for (int td = 0; td < NDT; ++td) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) X[td][e] = mubarC * X[td][e];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks)
+                    X[td] = Tr::mma(KtOperand<Tr, LT::PK>::load(Kl, td, ks, lane), VM[ks], X[td]);
+            }
+#pragma unroll
+            for (int td = 0; td < NDT; ++td) XM[td] = X[td];
+            // O = Op + Aqk vtilde
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc) {
+                floatx4 acc = Op[tc];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks)
+                    acc = Tr::mma(LdsA<Tr, LT::PT>::load(Al, 16 * tc + nn, ks, g), Vb[ks], acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) OOt[(16 * tc + 4 * g + e) * OW + 16 * ct + nn] = Tr::from_f(acc[e]);
             }
         }
     }
+    __syncthreads();
+    if (NT > 0)
+        copy_out<LT, E, D, C, NW>(smem + LT::OO0, O + ((size_t)bh * T + (NT - 1) * C) * D, valid_of(NT - 1),
+                                  col0, tid);
 
+    float* Xo = swave ? ST : MT;
 #pragma unroll
     for (int td = 0; td < NDT; ++td)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const size_t off = sbase + (size_t)(16 * td + 4 * g + e) * DV + col;
-            ST[off] = S[td][e];
-            MT[off] = M[td][e];
-        }
+        for (int e = 0; e < 4; ++e) Xo[sbase + (size_t)(16 * td + 4 * g + e) * D + col] = X[td][e];
 }
 
 // ---------------------------------------------------------------------------
@@ -372,28 +611,18 @@ static hipError_t launch_intra_t(const ChunkArgs& a)
     return hipGetLastError();
 }
 
-template <typename Tr, int DK, int C, int NW>
-static hipError_t launch_inter_t(const ChunkArgs& a)
+template <typename Tr, int D, int C>
+static hipError_t launch_inter_nw(const ChunkArgs& a)
 {
     using E = typename Tr::elem;
-    const int64_t grid = a.BH * (a.dv / (16 * NW));
-    hipLaunchKernelGGL((mdn_inter_kernel<Tr, DK, DK, C, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
+    using P = InterPick<Tr, D, C>;
+    constexpr int NCOL = P::NCOL, NBUF = P::NBUF;
+    const int64_t grid = a.BH * (D / (16 * NCOL));
+    hipLaunchKernelGGL((mdn_inter_kernel<Tr, D, C, NCOL, NBUF>), dim3((unsigned)grid), dim3(128 * NCOL), 0,
                        (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v,
                        (const E*)a.Tmat, (const E*)a.Aqk, a.coef, a.S0, a.M0,
                        (E*)a.O, a.ST, a.MT, (E*)a.Vt, a.T, a.NT, (int)a.BH);
     return hipGetLastError();
-}
-
-// Workgroups of two waves share one staged K^T tile; fall back to one wave
-// per workgroup when two-wave slabs would leave fewer than 256 workgroups
-// (one per compute unit) or the head has a single 16-column slab.
-template <typename Tr, int DK, int C>
-static hipError_t launch_inter_nw(const ChunkArgs& a)
-{
-    if constexpr (DK >= 32) {
-        if (a.BH * (DK / 32) >= 256) return launch_inter_t<Tr, DK, C, 2>(a);
-    }
-    return launch_inter_t<Tr, DK, C, 1>(a);
 }
 
 template <typename Tr, bool COEF_ONLY>
