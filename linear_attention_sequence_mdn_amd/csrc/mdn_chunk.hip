@@ -209,7 +209,7 @@ struct InterLayout {
     static constexpr int PV = 16 * NCOL * ES / 16;    // pieces per V-slab / out row
     static constexpr int PC = MDN_COEF_ROWS * C * 4 / 16;
     static_assert((PK & (PK - 1)) == 0 && (PT & (PT - 1)) == 0, "power-of-two rows");
-    // per-buffer regions (bytes)
+    // regions of one stage buffer (bytes)
     static constexpr int K0 = 0;
     static constexpr int Q0 = K0 + C * PK * 16;
     static constexpr int T0 = Q0 + C * PK * 16;
@@ -217,22 +217,16 @@ struct InterLayout {
     static constexpr int CF0 = A0 + C * PT * 16;
     static constexpr int V0 = CF0 + PC * 16;
     static constexpr int BUF = V0 + C * PV * 16;
-    // exchange areas, per column tile (lane-major)
+    // exchange areas and out tiles
     static constexpr int KSD = D / Tr::KW;
-    static constexpr int XS_B = 64 * KSD * (int)sizeof(frag);   // bf16/fp32 S operands
-    static constexpr int XM_B = 64 * (D / 16) * 16;             // fp32 M accumulators
-    static constexpr int XV_B = 64 * (C / 16) * 16;             // fp32 vtilde accumulators
-    static constexpr int XS0 = NBUF * BUF;
-    static constexpr int XM0 = XS0 + NCOL * XS_B;
-    static constexpr int XV0 = XM0 + NCOL * XM_B;
-    static constexpr int OV0 = XV0 + NCOL * XV_B;               // vtilde out tile
-    static constexpr int OO0 = OV0 + C * PV * 16;               // O out tile
-    static constexpr int TOTAL = OO0 + C * PV * 16;
+    static constexpr int XCH = NCOL * 64 * (KSD * (int)sizeof(frag) + (D / 16) * 16 + (C / 16) * 16);
+    static constexpr int OUT = 2 * C * PV * 16;
+    static constexpr int TOTAL = NBUF * BUF + XCH + OUT;
 };
 
 template <typename Tr, int D, int C>
 struct InterPick {
-    static constexpr int LIMIT = 160 * 1024;
+    static constexpr int LIMIT = 160 * 1024 - 1024;
     static constexpr int NCOL = (D >= 32 && InterLayout<Tr, D, C, 2, 1>::TOTAL <= LIMIT) ? 2 : 1;
     static constexpr int NBUF = InterLayout<Tr, D, C, NCOL, 2>::TOTAL <= LIMIT ? 2 : 1;
 };
@@ -240,22 +234,36 @@ struct InterPick {
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// byte offset of (row r, byte b) in a row of P 16-byte pieces, XOR-swizzled
+// Workgroup barrier that orders LDS only.  __syncthreads() would also wait
+// for every outstanding global load and store (including the next chunk's
+// LDS prefetch); here the chunk-boundary wait is explicit instead.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Swizzle key of row r for rows of P 16-byte pieces: the 16 rows an operand
+// read touches (perm of 16 consecutive accumulator rows, or the 4 x 4
+// row/column pattern of the transpose read) get distinct keys.
+template <int P>
+__device__ __forceinline__ int swz_key(int r) {
+    return ((r & 3) * (P / 4)) | ((r >> 3) & (P / 4 - 1));
+}
+
+// byte offset of (row r, byte b) in a row of P 16-byte pieces; piece p of
+// row r is stored at piece p ^ key(r)
 template <int P>
 __device__ __forceinline__ int swz(int r, int b) {
-    return r * P * 16 + ((((b >> 4) ^ (r & (P - 1)))) << 4) + (b & 15);
+    return r * P * 16 + ((((b >> 4) ^ swz_key<P>(r))) << 4) + (b & 15);
 }
 
 // A operand of a product whose B operand comes from accumulators (slot map),
 // from a swizzled LDS tile whose rows hold the contraction index.
 template <typename Tr, int P> struct LdsA;
 template <int P> struct LdsA<TraitsBf16, P> {
+    // slots of lane group g are the contiguous columns 32ks + 8g .. +7
     static __device__ __forceinline__ bf16x8 load(const char* tile, int row, int ks, int g) {
-        const int c0 = 32 * ks + 4 * g;                 // elements
-        const uint2 lo = *reinterpret_cast<const uint2*>(tile + swz<P>(row, 2 * c0));
-        const uint2 hi = *reinterpret_cast<const uint2*>(tile + swz<P>(row, 2 * (c0 + 16)));
         union { uint4 u; bf16x8 v; } f;
-        f.u = uint4{lo.x, lo.y, hi.x, hi.y};
+        f.u = *reinterpret_cast<const uint4*>(tile + swz<P>(row, 2 * (32 * ks + 8 * g)));
         return f.v;
     }
 };
@@ -272,17 +280,18 @@ template <int P> struct KtOperand<TraitsBf16, P> {
     static __device__ __forceinline__ bf16x8 load(const char* Kt, int td, int ks, int lane) {
         // Transpose read: in each 16-lane group, result lane i takes element
         // i%4 of source lane 4j + i/4.  Source lane s of group g points at
-        // row 32ks + 4g + s/4 (+16 for the second half), columns
-        // 16td + 4(s%4) .. +3, so lane i receives K[32ks + 4g + j][16td + i]
-        // for j = 0..3: exactly slots j (and 4 + j) of the slot map.
+        // row 32ks + 8g + s/4 (+4 for the second half) and columns
+        // perm(16td) + 8(s%4) .. +3, so lane i receives
+        // K[32ks + 8g + j][perm(16td + i)] for j = 0..3: the contraction
+        // slots j (and 4 + j) of lane group g, for state row 16td + i.
         const int g = lane >> 4, s = lane & 15;
-        const int r0 = 32 * ks + 4 * g + (s >> 2);
-        const int b = 2 * (16 * td + 4 * (s & 3));
+        const int r0 = 32 * ks + 8 * g + (s >> 2);
+        const int b = 2 * (Slots<TraitsBf16>::perm(16 * td) + 8 * (s & 3));
         union { shortx4 h[2]; bf16x8 v; } f;
         f.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) shortx4*)(Kt + swz<P>(r0, b)));
         f.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)(Kt + swz<P>(r0 + 16, b)));
+            (__attribute__((address_space(3))) shortx4*)(Kt + swz<P>(r0 + 4, b)));
         return f.v;
     }
 };
@@ -294,68 +303,75 @@ template <int P> struct KtOperand<TraitsF32, P> {
     }
 };
 
-// Issue the direct global->LDS copies of one chunk into buffer `buf`.
-// Instruction i of a region covers its 16-byte slots [64 i, 64 i + 64).
-template <typename LT, typename E, int D, int C, int NW>
+// Copy one tile of R rows x P 16-byte pieces from global memory into LDS,
+// swizzled (piece p of row r lands at piece p ^ key(r)), by one wave.
+// Instruction i covers rows [i*64/P, (i+1)*64/P): lane l takes row
+// i*64/P + l/P and physical piece l%P, so its source offset is a per-lane
+// constant plus a per-instruction constant.  `rowoff(r)` gives the byte
+// offset of global row r relative to `base`.
+template <int R, int P, typename RowOff>
+__device__ __forceinline__ void dma_tile(char* dst, const char* __restrict__ base, RowOff rowoff, int lane)
+{
+    static_assert(P <= 64 && 64 % P == 0, "rows of at most 64 pieces");
+    constexpr int RPI = 64 / P;                       // rows per instruction
+    constexpr int NI = (R * P + 63) / 64;
+    const unsigned lr = (unsigned)lane / P, lp = (unsigned)lane % P;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const unsigned r = i * RPI + lr;
+        const unsigned p = lp ^ (unsigned)swz_key<P>((int)r);
+        if (R * P % 64 == 0 || r < (unsigned)R)
+            __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(dst + i * 1024), 16, 0, 0);
+    }
+}
+
+// Copy R rows of P plain 16-byte pieces (no swizzle).
+template <int R, int P, typename RowOff>
+__device__ __forceinline__ void dma_plain(char* dst, const char* __restrict__ base, RowOff rowoff, int lane)
+{
+    constexpr int NI = (R * P + 63) / 64;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const unsigned s = i * 64 + (unsigned)lane;
+        const unsigned r = s / P, p = s % P;
+        if (R * P % 64 == 0 || r < (unsigned)R)
+            __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(dst + i * 1024), 16, 0, 0);
+    }
+}
+
+// Issue the direct global->LDS copies of one chunk into buffer `buf`, by one
+// wave.  PART 0: K and Q; PART 1: T, Aqk, the coefficients and the V slab.
+// Rows past `valid` (ragged last chunk) repeat the last valid row.
+template <typename LT, typename E, int D, int C, int PART>
 __device__ __forceinline__ void stage_chunk(char* buf, const E* __restrict__ k, const E* __restrict__ q,
                                             const E* __restrict__ v, const E* __restrict__ Tm,
                                             const E* __restrict__ Aqk, const float* __restrict__ coef,
-                                            size_t rowbase, int valid, size_t tile, int col0,
-                                            int wave, int lane)
+                                            size_t rowbase, int valid, size_t tile, int col0, int lane)
 {
-    constexpr int EPS = 16 / LT::ES;                 // elements per 16-byte piece
-    // K and Q: C rows of PK pieces, swizzled; rows past `valid` repeat the last one
-    constexpr int NK = (C * LT::PK + 63) / 64;
-    for (int i = wave; i < 2 * NK; i += NW) {
-        const bool isq = i >= NK;
-        const int s = (isq ? i - NK : i) * 64 + lane;
-        const int r = s / LT::PK, ph = s % LT::PK;
-        const int p = ph ^ (r & (LT::PK - 1));
-        const int rr = r < valid ? r : valid - 1;
-        const E* src = (isq ? q : k) + (rowbase + rr) * D + p * EPS;
-        if (s < C * LT::PK)
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + (isq ? LT::Q0 : LT::K0) + (s - lane) * 16),
-                                             16, 0, 0);
-    }
-    // T and Aqk: C rows of PT pieces, swizzled
-    constexpr int NT_ = (C * LT::PT + 63) / 64;
-    for (int i = wave; i < 2 * NT_; i += NW) {
-        const bool isa = i >= NT_;
-        const int s = (isa ? i - NT_ : i) * 64 + lane;
-        const int r = s / LT::PT, ph = s % LT::PT;
-        const int p = ph ^ (r & (LT::PT - 1));
-        const E* src = (isa ? Aqk : Tm) + tile * C * C + r * C + p * EPS;
-        if (s < C * LT::PT)
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + (isa ? LT::A0 : LT::T0) + (s - lane) * 16),
-                                             16, 0, 0);
-    }
-    // coefficient rows (plain) and the V slab (plain)
-    constexpr int NC = (LT::PC + 63) / 64;
-    constexpr int NV = (C * LT::PV + 63) / 64;
-    for (int i = wave; i < NC + NV; i += NW) {
-        if (i < NC) {
-            const int s = i * 64 + lane;
-            if (s < LT::PC)
-                __builtin_amdgcn_global_load_lds(coef + tile * MDN_COEF_ROWS * C + s * 4,
-                                                 (lds_void*)(buf + LT::CF0 + i * 64 * 16), 16, 0, 0);
-        } else {
-            const int s = (i - NC) * 64 + lane;
-            const int r = s / LT::PV, p = s % LT::PV;
-            const int rr = r < valid ? r : valid - 1;
-            if (s < C * LT::PV)
-                __builtin_amdgcn_global_load_lds(v + (rowbase + rr) * D + col0 + p * EPS,
-                                                 (lds_void*)(buf + LT::V0 + (i - NC) * 64 * 16), 16, 0, 0);
-        }
+    constexpr unsigned RB = D * LT::ES;              // bytes per K/Q/V row
+    const unsigned vlast = (unsigned)valid - 1;
+    if constexpr (PART == 0) {
+        auto kq_row = [&](unsigned r) { return (r < vlast ? r : vlast) * RB; };
+        dma_tile<C, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rowbase * D), kq_row, lane);
+        dma_tile<C, LT::PK>(buf + LT::Q0, reinterpret_cast<const char*>(q + rowbase * D), kq_row, lane);
+    } else {
+        auto t_row = [](unsigned r) { return r * (unsigned)(C * LT::ES); };
+        dma_tile<C, LT::PT>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
+        dma_tile<C, LT::PT>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
+        dma_plain<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
+                             [](unsigned) { return 0u; }, lane);
+        auto v_row = [&](unsigned r) { return (r < vlast ? r : vlast) * RB; };
+        dma_plain<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), v_row, lane);
     }
 }
 
 // Copy an out tile (C rows x 16*NCOL elements in LDS) to rows [0, valid) of
-// a row-major [.., D] output; `dst` points at the chunk's first row.
-template <typename LT, typename E, int D, int C, int NW>
-__device__ __forceinline__ void copy_out(const char* tile, E* __restrict__ dst, int valid, int col0, int tid)
+// a row-major [.., D] output, by one wave; `dst` points at the chunk's first row.
+template <typename LT, typename E, int D, int C>
+__device__ __forceinline__ void copy_out(const char* tile, E* __restrict__ dst, int valid, int col0, int lane)
 {
     constexpr int EPS = 16 / LT::ES;
-    for (int s = tid; s < C * LT::PV; s += 64 * NW) {
+    for (int s = lane; s < C * LT::PV; s += 64) {
         const int r = s / LT::PV, p = s % LT::PV;
         if (r < valid)
             *reinterpret_cast<uint4*>(dst + (size_t)r * D + col0 + p * EPS) =
@@ -364,7 +380,7 @@ __device__ __forceinline__ void copy_out(const char* tile, E* __restrict__ dst, 
 }
 
 template <typename Tr, int D, int C, int NCOL, int NBUF>
-__global__ __launch_bounds__(128 * NCOL)
+__global__ __launch_bounds__(64 * (2 * NCOL + 1))
 void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                       const typename Tr::elem* __restrict__ k,
                       const typename Tr::elem* __restrict__ v,
@@ -382,26 +398,79 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     using LT = InterLayout<Tr, D, C, NCOL, NBUF>;
     using frag = typename Tr::frag;
     constexpr int NSL = SL::NSLOT;
-    constexpr int NW = 2 * NCOL;
+    constexpr int NW = 2 * NCOL;                      // compute waves; wave NW is the loader
     constexpr int NDT = D / 16, NCT = C / 16, KSD = D / Tr::KW, KSC = C / Tr::KW;
     constexpr int SLABS = D / (16 * NCOL);
     constexpr int OW = 16 * NCOL;                     // out-tile row length (elements)
-    __shared__ __attribute__((aligned(16))) char smem[LT::TOTAL];
+    // Distinct LDS objects, so that the compiler can tell the buffer being
+    // prefetched from every buffer being read.
+    __shared__ __attribute__((aligned(16))) char stA[LT::BUF];
+    __shared__ __attribute__((aligned(16))) char stB[NBUF == 2 ? LT::BUF : 16];
+    __shared__ __attribute__((aligned(16))) frag xs[NCOL][KSD][64];      // S operands (S-wave -> M-wave)
+    __shared__ __attribute__((aligned(16))) floatx4 xm[NCOL][NDT][64];   // M accumulators (M -> S)
+    __shared__ __attribute__((aligned(16))) floatx4 xv[NCOL][NCT][64];   // vtilde (S -> M)
+    __shared__ __attribute__((aligned(16))) E ov[C * OW];                // vtilde out tile
+    __shared__ __attribute__((aligned(16))) E oo[C * OW];                // O out tile
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, nn = lane & 15;
-    const bool swave = wave < NCOL;                   // S-wave or M-wave
-    const int ct = swave ? wave : wave - NCOL;        // column tile within the slab
     int bh, slab;
     xcd_head_map(blockIdx.x, SLABS, BH, bh, slab);
     const int col0 = slab * OW;
-    const int col = col0 + 16 * ct + nn;
+    auto valid_of = [&](int64_t n) { return (int)((T - n * C) < C ? (T - n * C) : C); };
 
-    frag* XS = reinterpret_cast<frag*>(smem + LT::XS0 + ct * LT::XS_B) + lane * KSD;
-    floatx4* XM = reinterpret_cast<floatx4*>(smem + LT::XM0 + ct * LT::XM_B) + lane * NDT;
-    floatx4* XV = reinterpret_cast<floatx4*>(smem + LT::XV0 + ct * LT::XV_B) + lane * NCT;
-    E* OVt = reinterpret_cast<E*>(smem + LT::OV0);
-    E* OOt = reinterpret_cast<E*>(smem + LT::OO0);
+    if (wave == NW) {
+        // ---- loader wave: every global->LDS copy and every output store ----
+        if (NBUF == 2 && NT > 0) {
+            stage_chunk<LT, E, D, C, 0>(stA, k, q, v, Tm, Aqk, coef, (size_t)bh * T, valid_of(0), (size_t)bh * NT,
+                                        col0, lane);
+            stage_chunk<LT, E, D, C, 1>(stA, k, q, v, Tm, Aqk, coef, (size_t)bh * T, valid_of(0), (size_t)bh * NT,
+                                        col0, lane);
+        }
+        auto load = [&](char* cur, char* nxt, int64_t n) __attribute__((always_inline)) {
+            const size_t tile = (size_t)bh * NT + n;
+            const size_t rowbase = (size_t)bh * T + n * C;
+            const bool more = n + 1 < NT;
+            if constexpr (NBUF == 2) {
+                __builtin_amdgcn_s_waitcnt(0);          // chunk n has landed (and earlier stores left)
+                lds_barrier();                          // B0
+                if (more)
+                    stage_chunk<LT, E, D, C, 0>(nxt, k, q, v, Tm, Aqk, coef, rowbase + C, valid_of(n + 1),
+                                                tile + 1, col0, lane);
+            } else {
+                lds_barrier();                          // B0': the previous chunk's reads are done
+                stage_chunk<LT, E, D, C, 0>(cur, k, q, v, Tm, Aqk, coef, rowbase, valid_of(n), tile, col0, lane);
+                stage_chunk<LT, E, D, C, 1>(cur, k, q, v, Tm, Aqk, coef, rowbase, valid_of(n), tile, col0, lane);
+                __builtin_amdgcn_s_waitcnt(0);
+                lds_barrier();                          // B0
+            }
+            if (n > 0)                                  // O of chunk n-1 (written before B0)
+                copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + (rowbase - C) * D, C, col0, lane);
+            lds_barrier();                              // B1
+            if (NBUF == 2 && more)
+                stage_chunk<LT, E, D, C, 1>(nxt, k, q, v, Tm, Aqk, coef, rowbase + C, valid_of(n + 1),
+                                            tile + 1, col0, lane);
+            copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + rowbase * D, valid_of(n), col0, lane);
+        };
+        if constexpr (NBUF == 2) {
+            for (int64_t n = 0; n < NT; n += 2) {
+                load(stA, stB, n);
+                if (n + 1 < NT) load(stB, stA, n + 1);
+            }
+        } else {
+            for (int64_t n = 0; n < NT; ++n) load(stA, stA, n);
+        }
+        lds_barrier();
+        if (NT > 0)
+            copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + ((size_t)bh * T + (NT - 1) * C) * D,
+                                  valid_of(NT - 1), col0, lane);
+        return;
+    }
+
+    // ---- compute waves ----
+    const bool swave = wave < NCOL;                   // S-wave or M-wave
+    const int ct = swave ? wave : wave - NCOL;        // column tile within the slab
+    const int col = col0 + 16 * ct + nn;
 
     // the wave's own state: S (S-wave) or M (M-wave)
     const size_t sbase = (size_t)bh * D * D;
@@ -411,43 +480,23 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
         for (int td = 0; td < NDT; ++td)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) X[td][e] = X0[sbase + (size_t)(16 * td + 4 * g + e) * D + col];
+            for (int e = 0; e < 4; ++e) X[td][e] = X0[sbase + (size_t)SL::perm(16 * td + 4 * g + e) * D + col];
     } else {
 #pragma unroll
         for (int td = 0; td < NDT; ++td) X[td] = zero4();
     }
     if (swave) {
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) XS[ks] = SL::from_acc(X, ks);
+        for (int ks = 0; ks < KSD; ++ks) xs[ct][ks][lane] = SL::from_acc(X, ks);
     } else {
 #pragma unroll
-        for (int td = 0; td < NDT; ++td) XM[td] = X[td];
+        for (int td = 0; td < NDT; ++td) xm[ct][td][lane] = X[td];
     }
 
-    auto valid_of = [&](int64_t n) { return (int)((T - n * C) < C ? (T - n * C) : C); };
-    if (NT > 0 && NBUF == 2)
-        stage_chunk<LT, E, D, C, NW>(smem, k, q, v, Tm, Aqk, coef, (size_t)bh * T, valid_of(0),
-                                     (size_t)bh * NT, col0, wave, lane);
-
-    for (int64_t n = 0; n < NT; ++n) {
-        const int valid = valid_of(n);
-        const size_t tile = (size_t)bh * NT + n;
-        const size_t rowbase = (size_t)bh * T + n * C;
-        const char* cur = smem + (NBUF == 2 ? (int)(n & 1) * LT::BUF : 0);
-        if constexpr (NBUF == 2) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();                    // B0: chunk n staged, exchanges of n-1 visible
-            if (n + 1 < NT)
-                stage_chunk<LT, E, D, C, NW>(smem + (int)((n + 1) & 1) * LT::BUF, k, q, v, Tm, Aqk, coef,
-                                             rowbase + C, valid_of(n + 1), tile + 1, col0, wave, lane);
-        } else {
-            __syncthreads();
-            stage_chunk<LT, E, D, C, NW>(smem, k, q, v, Tm, Aqk, coef, rowbase, valid, tile, col0, wave, lane);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();                    // B0
-        }
-        if (n > 0)                              // O of chunk n-1 (written before B0)
-            copy_out<LT, E, D, C, NW>(smem + LT::OO0, O + (rowbase - C) * D, C, col0, tid);
+    // One chunk.  `cur` holds chunk n.
+    auto chunk = [&](const char* cur, int64_t n) __attribute__((always_inline)) {
+        if constexpr (NBUF == 1) lds_barrier();         // B0'
+        lds_barrier();                                  // B0: chunk n staged, exchanges visible
 
         const char* Kl = cur + LT::K0;
         const char* Ql = cur + LT::Q0;
@@ -455,39 +504,50 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         const char* Al = cur + LT::A0;
         const float* cf = reinterpret_cast<const float*>(cur + LT::CF0);
         const E* Vl = reinterpret_cast<const E*>(cur + LT::V0) + 16 * ct + nn;
+        // coefficient of accumulator rows perm(16tc + 4g) + e, e = 0..3 (contiguous)
+        auto crow = [&](int which, int tc) __attribute__((always_inline)) {
+            return *reinterpret_cast<const floatx4*>(cf + which * C + SL::perm(16 * tc + 4 * g));
+        };
 
-        // chunk-start states as B operands
         frag Sb[KSD], Mb[KSD];
-        floatx4 Mf[NDT];
-        if (swave) {
-#pragma unroll
-            for (int td = 0; td < NDT; ++td) Mf[td] = XM[td];
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) { Sb[ks] = SL::from_acc(X, ks); Mb[ks] = SL::from_acc(Mf, ks); }
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) { Sb[ks] = XS[ks]; Mb[ks] = SL::from_acc(X, ks); }
-        }
-
         floatx4 Vx[NCT];      // S-wave: vtilde
         floatx4 Op[NCT];      // M-wave: Diag(abar) Q S - Diag(b) Q M
         if (swave) {
+            floatx4 Mf[NDT];
+#pragma unroll
+            for (int td = 0; td < NDT; ++td) Mf[td] = xm[ct][td][lane];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) { Sb[ks] = SL::from_acc(X, ks); Mb[ks] = SL::from_acc(Mf, ks); }
+            {   // first half of the S update: abar_C S - b_C M (the chunk-start M is no longer needed)
+                const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
+                const float bC = cf[MDN_COEF_B * C + C - 1];
+#pragma unroll
+                for (int td = 0; td < NDT; ++td)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) X[td][e] = abarC * X[td][e] - bC * Mf[td][e];
+            }
             // W = V - Diag(abar) K S + Diag(alpha b_prev) K M
-            floatx4 W[NCT];
+            floatx4 W[NCT], KSa[NCT], KMa[NCT];
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc) { KSa[tc] = zero4(); KMa[tc] = zero4(); }
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                frag a[NCT];
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) a[tc] = LdsA<Tr, LT::PK>::load(Kl, SL::perm(16 * tc + nn), ks, g);
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) {
+                    KSa[tc] = Tr::mma(a[tc], Sb[ks], KSa[tc]);
+                    KMa[tc] = Tr::mma(a[tc], Mb[ks], KMa[tc]);
+                }
+            }
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc) {
-                floatx4 ks_ = zero4(), km_ = zero4();
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) {
-                    const frag a = LdsA<Tr, LT::PK>::load(Kl, 16 * tc + nn, ks, g);
-                    ks_ = Tr::mma(a, Sb[ks], ks_);
-                    km_ = Tr::mma(a, Mb[ks], km_);
-                }
+                const floatx4 ca = crow(MDN_COEF_ABAR, tc), cb = crow(MDN_COEF_ABP, tc);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int rr = 16 * tc + 4 * g + e;
-                    W[tc][e] = Tr::to_f(Vl[rr * OW]) - cf[MDN_COEF_ABAR * C + rr] * ks_[e]
-                               + cf[MDN_COEF_ABP * C + rr] * km_[e];
+                    const float vv = Tr::to_f(Vl[(SL::perm(16 * tc + 4 * g) + e) * OW]);
+                    W[tc][e] = vv - ca[e] * KSa[tc][e] + cb[e] * KMa[tc][e];
                 }
             }
             // vtilde = T W
@@ -495,41 +555,50 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) Wb[ks] = SL::from_acc(W, ks);
 #pragma unroll
+            for (int tc = 0; tc < NCT; ++tc) Vx[tc] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                frag a[NCT];
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) a[tc] = LdsA<Tr, LT::PT>::load(Tl, SL::perm(16 * tc + nn), ks, g);
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) Vx[tc] = Tr::mma(a[tc], Wb[ks], Vx[tc]);
+            }
+#pragma unroll
             for (int tc = 0; tc < NCT; ++tc) {
-                floatx4 acc = zero4();
+                xv[ct][tc][lane] = Vx[tc];
 #pragma unroll
-                for (int ks = 0; ks < KSC; ++ks)
-                    acc = Tr::mma(LdsA<Tr, LT::PT>::load(Tl, 16 * tc + nn, ks, g), Wb[ks], acc);
-                Vx[tc] = acc;
-                XV[tc] = acc;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) OVt[(16 * tc + 4 * g + e) * OW + 16 * ct + nn] = Tr::from_f(acc[e]);
+                for (int e = 0; e < 4; ++e)
+                    ov[(SL::perm(16 * tc + 4 * g) + e) * OW + 16 * ct + nn] = Tr::from_f(Vx[tc][e]);
             }
         } else {
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) {
-                floatx4 qs = zero4(), qm = zero4();
+            for (int ks = 0; ks < KSD; ++ks) { Sb[ks] = xs[ct][ks][lane]; Mb[ks] = SL::from_acc(X, ks); }
+            floatx4 QSa[NCT], QMa[NCT];
 #pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) {
-                    const frag a = LdsA<Tr, LT::PK>::load(Ql, 16 * tc + nn, ks, g);
-                    qs = Tr::mma(a, Sb[ks], qs);
-                    qm = Tr::mma(a, Mb[ks], qm);
-                }
+            for (int tc = 0; tc < NCT; ++tc) { QSa[tc] = zero4(); QMa[tc] = zero4(); }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int rr = 16 * tc + 4 * g + e;
-                    Op[tc][e] = cf[MDN_COEF_ABAR * C + rr] * qs[e] - cf[MDN_COEF_B * C + rr] * qm[e];
+            for (int ks = 0; ks < KSD; ++ks) {
+                frag a[NCT];
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) a[tc] = LdsA<Tr, LT::PK>::load(Ql, SL::perm(16 * tc + nn), ks, g);
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) {
+                    QSa[tc] = Tr::mma(a[tc], Sb[ks], QSa[tc]);
+                    QMa[tc] = Tr::mma(a[tc], Mb[ks], QMa[tc]);
                 }
             }
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc) {
+                const floatx4 ca = crow(MDN_COEF_ABAR, tc), cb = crow(MDN_COEF_B, tc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Op[tc][e] = ca[e] * QSa[tc][e] - cb[e] * QMa[tc][e];
+            }
         }
-        __syncthreads();                        // B1: vtilde of chunk n visible
-        copy_out<LT, E, D, C, NW>(smem + LT::OV0, Vt + rowbase * D, valid, col0, tid);
+        lds_barrier();                                  // B1: vtilde and the states of chunk n visible
 
-        const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
-        const float bC = cf[MDN_COEF_B * C + C - 1];
-        const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
         if (swave) {
-            // S <- abar_C S - b_C M + K^T Diag(gS) vtilde
+            // S <- (abar_C S - b_C M) + K^T Diag(gS) vtilde
             frag VS[KSC];
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
@@ -539,19 +608,19 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 VS[ks] = SL::from_acc_scaled(Vx, ks, sc);
             }
 #pragma unroll
-            for (int td = 0; td < NDT; ++td) {
+            for (int ks = 0; ks < KSC; ++ks) {
+                frag a[NDT];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) X[td][e] = abarC * X[td][e] - bC * Mf[td][e];
+                for (int td = 0; td < NDT; ++td) a[td] = KtOperand<Tr, LT::PK>::load(Kl, td, ks, lane);
 #pragma unroll
-                for (int ks = 0; ks < KSC; ++ks)
-                    X[td] = Tr::mma(KtOperand<Tr, LT::PK>::load(Kl, td, ks, lane), VS[ks], X[td]);
+                for (int td = 0; td < NDT; ++td) X[td] = Tr::mma(a[td], VS[ks], X[td]);
             }
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) XS[ks] = SL::from_acc(X, ks);
+            for (int ks = 0; ks < KSD; ++ks) xs[ct][ks][lane] = SL::from_acc(X, ks);
         } else {
             floatx4 Vv[NCT];
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) Vv[tc] = XV[tc];
+            for (int tc = 0; tc < NCT; ++tc) Vv[tc] = xv[ct][tc][lane];
             frag VM[KSC], Vb[KSC];
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
@@ -562,38 +631,53 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 Vb[ks] = SL::from_acc(Vv, ks);
             }
             // M <- mubar_C M - K^T Diag(gM) vtilde
+            const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
 #pragma unroll
-            for (int td = 0; td < NDT; ++td) {
+            for (int td = 0; td < NDT; ++td)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) X[td][e] = mubarC * X[td][e];
 #pragma unroll
-                for (int ks = 0; ks < KSC; ++ks)
-                    X[td] = Tr::mma(KtOperand<Tr, LT::PK>::load(Kl, td, ks, lane), VM[ks], X[td]);
+            for (int ks = 0; ks < KSC; ++ks) {
+                frag a[NDT];
+#pragma unroll
+                for (int td = 0; td < NDT; ++td) a[td] = KtOperand<Tr, LT::PK>::load(Kl, td, ks, lane);
+#pragma unroll
+                for (int td = 0; td < NDT; ++td) X[td] = Tr::mma(a[td], VM[ks], X[td]);
             }
 #pragma unroll
-            for (int td = 0; td < NDT; ++td) XM[td] = X[td];
+            for (int td = 0; td < NDT; ++td) xm[ct][td][lane] = X[td];
             // O = Op + Aqk vtilde
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) {
-                floatx4 acc = Op[tc];
+            for (int ks = 0; ks < KSC; ++ks) {
+                frag a[NCT];
 #pragma unroll
-                for (int ks = 0; ks < KSC; ++ks)
-                    acc = Tr::mma(LdsA<Tr, LT::PT>::load(Al, 16 * tc + nn, ks, g), Vb[ks], acc);
+                for (int tc = 0; tc < NCT; ++tc) a[tc] = LdsA<Tr, LT::PT>::load(Al, SL::perm(16 * tc + nn), ks, g);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) OOt[(16 * tc + 4 * g + e) * OW + 16 * ct + nn] = Tr::from_f(acc[e]);
+                for (int tc = 0; tc < NCT; ++tc) Op[tc] = Tr::mma(a[tc], Vb[ks], Op[tc]);
             }
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    oo[(SL::perm(16 * tc + 4 * g) + e) * OW + 16 * ct + nn] = Tr::from_f(Op[tc][e]);
         }
+    };
+
+    if constexpr (NBUF == 2) {
+        for (int64_t n = 0; n < NT; n += 2) {
+            chunk(stA, n);
+            if (n + 1 < NT) chunk(stB, n + 1);
+        }
+    } else {
+        for (int64_t n = 0; n < NT; ++n) chunk(stA, n);
     }
-    __syncthreads();
-    if (NT > 0)
-        copy_out<LT, E, D, C, NW>(smem + LT::OO0, O + ((size_t)bh * T + (NT - 1) * C) * D, valid_of(NT - 1),
-                                  col0, tid);
+    lds_barrier();
 
     float* Xo = swave ? ST : MT;
 #pragma unroll
     for (int td = 0; td < NDT; ++td)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Xo[sbase + (size_t)(16 * td + 4 * g + e) * D + col] = X[td][e];
+        for (int e = 0; e < 4; ++e) Xo[sbase + (size_t)SL::perm(16 * td + 4 * g + e) * D + col] = X[td][e];
 }
 
 // ---------------------------------------------------------------------------
@@ -618,7 +702,7 @@ static hipError_t launch_inter_nw(const ChunkArgs& a)
     using P = InterPick<Tr, D, C>;
     constexpr int NCOL = P::NCOL, NBUF = P::NBUF;
     const int64_t grid = a.BH * (D / (16 * NCOL));
-    hipLaunchKernelGGL((mdn_inter_kernel<Tr, D, C, NCOL, NBUF>), dim3((unsigned)grid), dim3(128 * NCOL), 0,
+    hipLaunchKernelGGL((mdn_inter_kernel<Tr, D, C, NCOL, NBUF>), dim3((unsigned)grid), dim3(64 * (2 * NCOL + 1)), 0,
                        (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v,
                        (const E*)a.Tmat, (const E*)a.Aqk, a.coef, a.S0, a.M0,
                        (E*)a.O, a.ST, a.MT, (E*)a.Vt, a.T, a.NT, (int)a.BH);

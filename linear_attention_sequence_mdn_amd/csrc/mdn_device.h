@@ -55,26 +55,30 @@ struct TraitsF32 {
 // ---------------------------------------------------------------------------
 // Slot map for products whose B operand is an accumulator.
 //
-// An accumulator "column" is a stack of 16-row tiles acc[0..R/16) (rows of
-// the contraction index).  Lane group g = l/16 of tile t holds rows
-// 16t + 4g + e, e = 0..3.
+// An accumulator "column" is a stack of 16-row tiles acc[0..R/16) along the
+// contraction dimension.  Lane group g = l/16 of tile t holds accumulator
+// rows 16t + 4g + e, e = 0..3.
 //   bf16 (K = 32 per step ks): slots 0..3 <- tile 2ks, slots 4..7 <- tile
-//   2ks+1, so slot j of group g is contraction row 32ks + 16(j/4) + 4g + j%4.
-//   fp32 (K = 4 per step ks): the single slot of group g is contraction row
-//   16(ks/4) + 4g + ks%4.
-// The A operand of the same product must present the same rows: for a
-// row-major A with the contraction index contiguous this is two 8-byte loads
-// (bf16) or one 4-byte load (fp32) per step.
+//   2ks+1.  Accumulator row x does not stand for index x of the dimension
+//   but for perm(x) = 32(x/32) + 8((x/4)%4) + 4((x/16)%2) + x%4, which maps
+//   the 8 rows slot-feeding lane group g onto the contiguous indices
+//   32ks + 8g .. 32ks + 8g + 7.  A row-major A operand (contraction index
+//   contiguous) is then a single 16-byte read.  Every producer and consumer
+//   of such a dimension (state rows, chunk rows) applies the same perm.
+//   fp32 (K = 4 per step ks): the single slot of group g is accumulator row
+//   16(ks/4) + 4g + ks%4, and perm is the identity.
 // ---------------------------------------------------------------------------
 template <typename Tr> struct Slots;
 
 template <> struct Slots<TraitsBf16> {
     using Tr = TraitsBf16;
-    // contraction row of slot j (0..7) for step ks, lane group g
-    static __device__ __forceinline__ int row(int ks, int g, int j) {
-        return 32 * ks + 16 * (j >> 2) + 4 * g + (j & 3);
+    static constexpr int NSLOT = 8;
+    static __device__ __forceinline__ int perm(int x) {
+        return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3);
     }
-    // B operand from accumulator tiles, optionally scaled per contraction row.
+    // index (after perm) carried by slot j of step ks, lane group g
+    static __device__ __forceinline__ int row(int ks, int g, int j) { return 32 * ks + 8 * g + j; }
+    // B operand from accumulator tiles
     static __device__ __forceinline__ bf16x8 from_acc(const floatx4* acc, int ks) {
         const floatx4 a = acc[2 * ks], b = acc[2 * ks + 1];
         bf16x8 r;
@@ -82,8 +86,8 @@ template <> struct Slots<TraitsBf16> {
         r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
         return r;
     }
+    // same, each slot j scaled by s[j]
     static __device__ __forceinline__ bf16x8 from_acc_scaled(const floatx4* acc, int ks, const float* s) {
-        // s[j] is the scale of slot j
         const floatx4 a = acc[2 * ks], b = acc[2 * ks + 1];
         bf16x8 r;
         r[0] = (__bf16)(a[0] * s[0]); r[1] = (__bf16)(a[1] * s[1]);
@@ -92,24 +96,17 @@ template <> struct Slots<TraitsBf16> {
         r[6] = (__bf16)(b[2] * s[6]); r[7] = (__bf16)(b[3] * s[7]);
         return r;
     }
-    static constexpr int NSLOT = 8;
     static __device__ __forceinline__ bf16x8 zero() {
         union { uint4 u; bf16x8 v; } f;
         f.u = uint4{0u, 0u, 0u, 0u};
-        return f.v;
-    }
-    // A operand from a row whose contraction index is contiguous (global or LDS).
-    static __device__ __forceinline__ bf16x8 load_row(const __bf16* rowp, int ks, int g) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(rowp + 32 * ks + 4 * g);
-        const uint2 hi = *reinterpret_cast<const uint2*>(rowp + 32 * ks + 16 + 4 * g);
-        union { uint4 u; bf16x8 v; } f;
-        f.u = uint4{lo.x, lo.y, hi.x, hi.y};
         return f.v;
     }
 };
 
 template <> struct Slots<TraitsF32> {
     using Tr = TraitsF32;
+    static constexpr int NSLOT = 1;
+    static __device__ __forceinline__ int perm(int x) { return x; }
     static __device__ __forceinline__ int row(int ks, int g, int /*j*/) {
         return 16 * (ks >> 2) + 4 * g + (ks & 3);
     }
@@ -119,11 +116,7 @@ template <> struct Slots<TraitsF32> {
     static __device__ __forceinline__ float from_acc_scaled(const floatx4* acc, int ks, const float* s) {
         return acc[ks >> 2][ks & 3] * s[0];
     }
-    static constexpr int NSLOT = 1;
     static __device__ __forceinline__ float zero() { return 0.f; }
-    static __device__ __forceinline__ float load_row(const float* rowp, int ks, int g) {
-        return rowp[16 * (ks >> 2) + 4 * g + (ks & 3)];
-    }
 };
 
 // Operand with contiguous contraction index, natural order (both operands
