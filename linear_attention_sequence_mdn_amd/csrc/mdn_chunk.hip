@@ -23,156 +23,18 @@
 //     M     <- mubar_{C-1} M - K^T Diag(gM) vtilde
 //
 // Kernel split:
-//   mdn_intra_kernel  one workgroup per chunk tile (fully parallel): the
-//                     coefficient scans, Gamma, the two C x C score products
-//                     on the matrix cores, T by forward substitution in LDS;
-//                     writes T, Aqk and the coefficient rows.
-//   mdn_inter_kernel  one workgroup per (head, slab of 16*NW state columns),
-//                     sequential over the chunks: vtilde, O (fused) and the
-//                     fp32 S/M carry.  State columns are independent, so the
-//                     slab split needs no communication.
+//   mdn_intra_kernel  (mdn_intra.hip) one workgroup per chunk tile, fully
+//                     parallel: coefficients, Gamma, T, Aqk.
+//   mdn_inter_kernel  (this file) one workgroup per (head, slab of state
+//                     columns), sequential over the chunks: vtilde, O (fused)
+//                     and the fp32 S/M carry.  State columns are independent,
+//                     so the slab split needs no communication.
 #include "mdn_device.h"
 #include "mdn_internal.h"
+#include "mdn_lds.h"
 #include "../../include/mdn.h"
 
 namespace mdn {
-
-// ---------------------------------------------------------------------------
-// mdn_intra_kernel
-// ---------------------------------------------------------------------------
-template <typename Tr, int DK, int C, bool COEF_ONLY>
-__global__ __launch_bounds__(256)
-void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
-                      const typename Tr::elem* __restrict__ k,
-                      const float* __restrict__ alpha, const float* __restrict__ mu,
-                      const float* __restrict__ beta, const float* __restrict__ eta,
-                      int64_t T, int64_t NT,
-                      typename Tr::elem* __restrict__ Tout,
-                      typename Tr::elem* __restrict__ Aqk,
-                      float* __restrict__ coef,
-                      float* __restrict__ gamma)
-{
-    using E = typename Tr::elem;
-    constexpr int NCT = C / 16;
-    constexpr int NJOB = NCT * (NCT + 1) / 2;      // lower-triangular 16x16 tiles
-    constexpr int KSD = DK / Tr::KW;
-    constexpr int GS = C + 4;                       // LDS row stride (floats)
-    __shared__ float sA[C * GS];                    // A = (P K^T) o Gamma^-
-    __shared__ float sG[C * GS];                    // Gamma
-    __shared__ float sa[C], sbt[C], slm[C], se[C];
-
-    const int64_t tile = blockIdx.x;
-    const int64_t bh = tile / NT, n = tile % NT;
-    const int64_t t0 = n * C;
-    const int valid = (int)((T - t0) < C ? (T - t0) : C);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, nn = lane & 15;
-    float* cf = coef + tile * MDN_COEF_ROWS * C;
-
-    // -- coefficient scans (wave 0, lane r = token r) ----------------------
-    if (wave == 0) {
-        float a = 1.f, m = 1.f, bt = 0.f, e = 0.f;   // neutral padding
-        if (lane < valid) {
-            const size_t gi = (size_t)(bh * T + t0 + lane);
-            a = alpha[gi]; m = mu[gi]; bt = beta[gi]; e = eta[gi];
-        }
-        const float la = wave_scan_add(logf(a), lane);
-        const float lm = wave_scan_add(logf(m), lane);
-        const float x = logf(bt) + lm - la;          // log beta_j + LM_j - LA_j
-        const float lc = wave_scan_logaddexp(x, lane);
-        const float b = expf(la + lc);
-        float bprev = __shfl_up(b, 1, 64);
-        if (lane == 0) bprev = 0.f;
-        if (lane < C) {
-            sa[lane] = a; sbt[lane] = bt; slm[lane] = lm; se[lane] = e;
-            cf[MDN_COEF_ABAR * C + lane] = expf(la);
-            cf[MDN_COEF_ABP * C + lane] = a * bprev;
-            cf[MDN_COEF_B * C + lane] = b;
-            cf[MDN_COEF_LA * C + lane] = la;
-            cf[MDN_COEF_LM * C + lane] = lm;
-            cf[MDN_COEF_LOGC * C + lane] = lc;
-        }
-    }
-    __syncthreads();
-
-    // -- Gamma, one column per lane (wave 0) --------------------------------
-    // gamma_{r,i} = alpha_r gamma_{r-1,i} + beta_r exp(LM_r - LM_i), r >= i:
-    // the mu ratio is a broadcast difference of the log cumsum (exponent
-    // <= 0), the alpha ratio is applied as the running decay, and every term
-    // is non-negative, so nothing overflows or cancels.
-    if (wave == 0 && lane < C) {
-        const float lmi = slm[lane], ei = se[lane];
-        float gam = 0.f;
-        for (int r = 0; r < C; ++r) {
-            const float w = (r >= lane) ? expf(slm[r] - lmi) : 0.f;
-            gam = sa[r] * gam + sbt[r] * w;
-            sG[r * GS + lane] = ei * gam;
-        }
-        cf[MDN_COEF_GS * C + lane] = ei * gam;
-        cf[MDN_COEF_GM * C + lane] = ei * expf(slm[C - 1] - lmi);
-    }
-    __syncthreads();
-
-    if (gamma) {
-        float* gp = gamma + tile * C * C;
-        for (int idx = tid; idx < C * C; idx += 256) gp[idx] = sG[(idx / C) * GS + (idx % C)];
-    }
-    if constexpr (COEF_ONLY) return;
-
-    // -- score products on the matrix cores ---------------------------------
-    // job < NJOB: K K^T tile -> A (LDS);  job >= NJOB: Q K^T tile -> Aqk.
-    const E* qh = q + (size_t)(bh * T + t0) * DK;
-    const E* kh = k + (size_t)(bh * T + t0) * DK;
-    E* Aq = Aqk + tile * C * C;
-    for (int job = wave; job < 2 * NJOB; job += 4) {
-        const int mat = job / NJOB;
-        int idx = job % NJOB, tr = 0;
-        while (idx > tr) { idx -= tr + 1; ++tr; }
-        const int tc = idx;
-        const int ra = 16 * tr + nn, rb = 16 * tc + nn;
-        const E* xa = (mat == 0 ? kh : qh) + (size_t)ra * DK;
-        const E* xb = kh + (size_t)rb * DK;
-        floatx4 acc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-            const auto fa = ra < valid ? Contig<Tr>::load(xa, ks, g) : Contig<Tr>::zero();
-            const auto fb = rb < valid ? Contig<Tr>::load(xb, ks, g) : Contig<Tr>::zero();
-            acc = Tr::mma(fa, fb, acc);
-        }
-        const int i = 16 * tc + nn;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * tr + 4 * g + e;
-            if (mat == 0) {
-                sA[r * GS + i] = (i < r) ? sa[r] * acc[e] * sG[(r - 1) * GS + i] : 0.f;
-            } else {
-                Aq[r * C + i] = Tr::from_f((i <= r) ? acc[e] * sG[r * GS + i] : 0.f);
-            }
-        }
-    }
-    // upper tiles of Aqk are zero
-    for (int idx = tid; idx < C * C; idx += 256) {
-        const int r = idx / C, i = idx % C;
-        if ((i >> 4) > (r >> 4)) Aq[idx] = Tr::from_f(0.f);
-    }
-    __syncthreads();
-
-    // -- T = (I + A)^{-1} by forward substitution (wave 0, lane = column) ---
-    // T[r][j] = delta_rj - sum_{i<r} A[r][i] T[i][j]
-    if (wave == 0) {
-        E* Tt = Tout + tile * C * C;
-        float tcol[C];
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float s = (r == lane) ? 1.f : 0.f;
-            const float* Ar = sA + r * GS;
-#pragma unroll
-            for (int i = 0; i < r; ++i) s = fmaf(-Ar[i], tcol[i], s);
-            tcol[r] = s;
-            if (lane < C) Tt[r * C + lane] = Tr::from_f(s);
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // mdn_inter_kernel
@@ -231,49 +93,6 @@ struct InterPick {
     static constexpr int NBUF = InterLayout<Tr, D, C, NCOL, 2>::TOTAL <= LIMIT ? 2 : 1;
 };
 
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Workgroup barrier that orders LDS only.  __syncthreads() would also wait
-// for every outstanding global load and store (including the next chunk's
-// LDS prefetch); here the chunk-boundary wait is explicit instead.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Swizzle key of row r for rows of P 16-byte pieces: the 16 rows an operand
-// read touches (perm of 16 consecutive accumulator rows, or the 4 x 4
-// row/column pattern of the transpose read) get distinct keys.
-template <int P>
-__device__ __forceinline__ int swz_key(int r) {
-    return ((r & 3) * (P / 4)) | ((r >> 3) & (P / 4 - 1));
-}
-
-// byte offset of (row r, byte b) in a row of P 16-byte pieces; piece p of
-// row r is stored at piece p ^ key(r)
-template <int P>
-__device__ __forceinline__ int swz(int r, int b) {
-    return r * P * 16 + ((((b >> 4) ^ swz_key<P>(r))) << 4) + (b & 15);
-}
-
-// A operand of a product whose B operand comes from accumulators (slot map),
-// from a swizzled LDS tile whose rows hold the contraction index.
-template <typename Tr, int P> struct LdsA;
-template <int P> struct LdsA<TraitsBf16, P> {
-    // slots of lane group g are the contiguous columns 32ks + 8g .. +7
-    static __device__ __forceinline__ bf16x8 load(const char* tile, int row, int ks, int g) {
-        union { uint4 u; bf16x8 v; } f;
-        f.u = *reinterpret_cast<const uint4*>(tile + swz<P>(row, 2 * (32 * ks + 8 * g)));
-        return f.v;
-    }
-};
-template <int P> struct LdsA<TraitsF32, P> {
-    static __device__ __forceinline__ float load(const char* tile, int row, int ks, int g) {
-        const int c = 16 * (ks >> 2) + 4 * g + (ks & 3);
-        return *reinterpret_cast<const float*>(tile + swz<P>(row, 4 * c));
-    }
-};
-
 // K^T operand of the state update for d-tile td, contraction step ks.
 template <typename Tr, int P> struct KtOperand;
 template <int P> struct KtOperand<TraitsBf16, P> {
@@ -303,65 +122,31 @@ template <int P> struct KtOperand<TraitsF32, P> {
     }
 };
 
-// Copy one tile of R rows x P 16-byte pieces from global memory into LDS,
-// swizzled (piece p of row r lands at piece p ^ key(r)), by one wave.
-// Instruction i covers rows [i*64/P, (i+1)*64/P): lane l takes row
-// i*64/P + l/P and physical piece l%P, so its source offset is a per-lane
-// constant plus a per-instruction constant.  `rowoff(r)` gives the byte
-// offset of global row r relative to `base`.
-template <int R, int P, typename RowOff>
-__device__ __forceinline__ void dma_tile(char* dst, const char* __restrict__ base, RowOff rowoff, int lane)
-{
-    static_assert(P <= 64 && 64 % P == 0, "rows of at most 64 pieces");
-    constexpr int RPI = 64 / P;                       // rows per instruction
-    constexpr int NI = (R * P + 63) / 64;
-    const unsigned lr = (unsigned)lane / P, lp = (unsigned)lane % P;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const unsigned r = i * RPI + lr;
-        const unsigned p = lp ^ (unsigned)swz_key<P>((int)r);
-        if (R * P % 64 == 0 || r < (unsigned)R)
-            __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(dst + i * 1024), 16, 0, 0);
-    }
-}
-
-// Copy R rows of P plain 16-byte pieces (no swizzle).
-template <int R, int P, typename RowOff>
-__device__ __forceinline__ void dma_plain(char* dst, const char* __restrict__ base, RowOff rowoff, int lane)
-{
-    constexpr int NI = (R * P + 63) / 64;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const unsigned s = i * 64 + (unsigned)lane;
-        const unsigned r = s / P, p = s % P;
-        if (R * P % 64 == 0 || r < (unsigned)R)
-            __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(dst + i * 1024), 16, 0, 0);
-    }
-}
-
-// Issue the direct global->LDS copies of one chunk into buffer `buf`, by one
-// wave.  PART 0: K and Q; PART 1: T, Aqk, the coefficients and the V slab.
-// Rows past `valid` (ragged last chunk) repeat the last valid row.
+// Issue part of the direct global->LDS copies of one chunk into the buffer at
+// LDS byte address `buf`, by one wave: PART 0 K, PART 1 Q, PART 2 T and the coefficients,
+// PART 3 Aqk and the V slab.  Rows past `valid` (ragged last chunk) repeat
+// the last valid row.
 template <typename LT, typename E, int D, int C, int PART>
-__device__ __forceinline__ void stage_chunk(char* buf, const E* __restrict__ k, const E* __restrict__ q,
+__device__ __forceinline__ void stage_chunk(uint32_t buf, const E* __restrict__ k, const E* __restrict__ q,
                                             const E* __restrict__ v, const E* __restrict__ Tm,
                                             const E* __restrict__ Aqk, const float* __restrict__ coef,
                                             size_t rowbase, int valid, size_t tile, int col0, int lane)
 {
     constexpr unsigned RB = D * LT::ES;              // bytes per K/Q/V row
     const unsigned vlast = (unsigned)valid - 1;
+    auto seq_row = [&](unsigned r) { return (r < vlast ? r : vlast) * RB; };
+    auto t_row = [](unsigned r) { return r * (unsigned)(C * LT::ES); };
     if constexpr (PART == 0) {
-        auto kq_row = [&](unsigned r) { return (r < vlast ? r : vlast) * RB; };
-        dma_tile<C, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rowbase * D), kq_row, lane);
-        dma_tile<C, LT::PK>(buf + LT::Q0, reinterpret_cast<const char*>(q + rowbase * D), kq_row, lane);
-    } else {
-        auto t_row = [](unsigned r) { return r * (unsigned)(C * LT::ES); };
+        dma_tile<C, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rowbase * D), seq_row, lane);
+    } else if constexpr (PART == 1) {
+        dma_tile<C, LT::PK>(buf + LT::Q0, reinterpret_cast<const char*>(q + rowbase * D), seq_row, lane);
+    } else if constexpr (PART == 2) {
         dma_tile<C, LT::PT>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
-        dma_tile<C, LT::PT>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
         dma_plain<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
                              [](unsigned) { return 0u; }, lane);
-        auto v_row = [&](unsigned r) { return (r < vlast ? r : vlast) * RB; };
-        dma_plain<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), v_row, lane);
+    } else {
+        dma_tile<C, LT::PT>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
+        dma_plain<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), seq_row, lane);
     }
 }
 
@@ -380,7 +165,7 @@ __device__ __forceinline__ void copy_out(const char* tile, E* __restrict__ dst, 
 }
 
 template <typename Tr, int D, int C, int NCOL, int NBUF>
-__global__ __launch_bounds__(64 * (2 * NCOL + 1))
+__global__ __launch_bounds__(64 * (2 * NCOL + 2))
 void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                       const typename Tr::elem* __restrict__ k,
                       const typename Tr::elem* __restrict__ v,
@@ -398,7 +183,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     using LT = InterLayout<Tr, D, C, NCOL, NBUF>;
     using frag = typename Tr::frag;
     constexpr int NSL = SL::NSLOT;
-    constexpr int NW = 2 * NCOL;                      // compute waves; wave NW is the loader
+    constexpr int NW = 2 * NCOL;                      // compute waves; waves NW, NW+1 load
     constexpr int NDT = D / 16, NCT = C / 16, KSD = D / Tr::KW, KSC = C / Tr::KW;
     constexpr int SLABS = D / (16 * NCOL);
     constexpr int OW = 16 * NCOL;                     // out-tile row length (elements)
@@ -419,49 +204,60 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     const int col0 = slab * OW;
     auto valid_of = [&](int64_t n) { return (int)((T - n * C) < C ? (T - n * C) : C); };
 
-    if (wave == NW) {
-        // ---- loader wave: every global->LDS copy and every output store ----
+    if (wave >= NW) {
+        // ---- two loader waves: every global->LDS copy and every output store ----
+        // Loader 0 copies K (before the mid-chunk barrier), then T and the
+        // coefficients, and writes O; loader 1 copies Q, then Aqk and the V
+        // slab, and writes vtilde.
+        const int lw = wave - NW;
+        auto issue = [&](uint32_t buf, int64_t m, int half) __attribute__((always_inline)) {
+            const size_t tile = (size_t)bh * NT + m;
+            const size_t rb = (size_t)bh * T + m * C;
+            const int vm = valid_of(m);
+            if (half == 0) {
+                if (lw == 0) stage_chunk<LT, E, D, C, 0>(buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
+                else stage_chunk<LT, E, D, C, 1>(buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
+            } else {
+                if (lw == 0) stage_chunk<LT, E, D, C, 2>(buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
+                else stage_chunk<LT, E, D, C, 3>(buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
+            }
+        };
+        const uint32_t aA = lds_addr(stA), aB = lds_addr(stB);
         if (NBUF == 2 && NT > 0) {
-            stage_chunk<LT, E, D, C, 0>(stA, k, q, v, Tm, Aqk, coef, (size_t)bh * T, valid_of(0), (size_t)bh * NT,
-                                        col0, lane);
-            stage_chunk<LT, E, D, C, 1>(stA, k, q, v, Tm, Aqk, coef, (size_t)bh * T, valid_of(0), (size_t)bh * NT,
-                                        col0, lane);
+            issue(aA, 0, 0);
+            issue(aA, 0, 1);
         }
-        auto load = [&](char* cur, char* nxt, int64_t n) __attribute__((always_inline)) {
-            const size_t tile = (size_t)bh * NT + n;
+        auto load = [&](uint32_t cur, uint32_t nxt, int64_t n) __attribute__((always_inline)) {
             const size_t rowbase = (size_t)bh * T + n * C;
             const bool more = n + 1 < NT;
             if constexpr (NBUF == 2) {
                 __builtin_amdgcn_s_waitcnt(0);          // chunk n has landed (and earlier stores left)
                 lds_barrier();                          // B0
-                if (more)
-                    stage_chunk<LT, E, D, C, 0>(nxt, k, q, v, Tm, Aqk, coef, rowbase + C, valid_of(n + 1),
-                                                tile + 1, col0, lane);
+                if (more) issue(nxt, n + 1, 0);
             } else {
                 lds_barrier();                          // B0': the previous chunk's reads are done
-                stage_chunk<LT, E, D, C, 0>(cur, k, q, v, Tm, Aqk, coef, rowbase, valid_of(n), tile, col0, lane);
-                stage_chunk<LT, E, D, C, 1>(cur, k, q, v, Tm, Aqk, coef, rowbase, valid_of(n), tile, col0, lane);
+                issue(cur, n, 0);
+                issue(cur, n, 1);
                 __builtin_amdgcn_s_waitcnt(0);
                 lds_barrier();                          // B0
             }
-            if (n > 0)                                  // O of chunk n-1 (written before B0)
+            if (lw == 0 && n > 0)                       // O of chunk n-1 (written before B0)
                 copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + (rowbase - C) * D, C, col0, lane);
             lds_barrier();                              // B1
-            if (NBUF == 2 && more)
-                stage_chunk<LT, E, D, C, 1>(nxt, k, q, v, Tm, Aqk, coef, rowbase + C, valid_of(n + 1),
-                                            tile + 1, col0, lane);
-            copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + rowbase * D, valid_of(n), col0, lane);
+            if (NBUF == 2 && more) issue(nxt, n + 1, 1);
+            if (lw == 1)
+                copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + rowbase * D, valid_of(n), col0, lane);
         };
         if constexpr (NBUF == 2) {
             for (int64_t n = 0; n < NT; n += 2) {
-                load(stA, stB, n);
-                if (n + 1 < NT) load(stB, stA, n + 1);
+                load(aA, aB, n);
+                if (n + 1 < NT) load(aB, aA, n + 1);
             }
         } else {
-            for (int64_t n = 0; n < NT; ++n) load(stA, stA, n);
+            for (int64_t n = 0; n < NT; ++n) load(aA, aA, n);
         }
         lds_barrier();
-        if (NT > 0)
+        if (lw == 0 && NT > 0)
             copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + ((size_t)bh * T + (NT - 1) * C) * D,
                                   valid_of(NT - 1), col0, lane);
         return;
@@ -493,7 +289,6 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         for (int td = 0; td < NDT; ++td) xm[ct][td][lane] = X[td];
     }
 
-    // One chunk.  `cur` holds chunk n.
     auto chunk = [&](const char* cur, int64_t n) __attribute__((always_inline)) {
         if constexpr (NBUF == 1) lds_barrier();         // B0'
         lds_barrier();                                  // B0: chunk n staged, exchanges visible
@@ -501,7 +296,6 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         const char* Kl = cur + LT::K0;
         const char* Ql = cur + LT::Q0;
         const char* Tl = cur + LT::T0;
-        const char* Al = cur + LT::A0;
         const float* cf = reinterpret_cast<const float*>(cur + LT::CF0);
         const E* Vl = reinterpret_cast<const E*>(cur + LT::V0) + 16 * ct + nn;
         // coefficient of accumulator rows perm(16tc + 4g) + e, e = 0..3 (contiguous)
@@ -647,6 +441,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
             for (int td = 0; td < NDT; ++td) xm[ct][td][lane] = X[td];
             // O = Op + Aqk vtilde
+            const char* Al = cur + LT::A0;
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
                 frag a[NCT];
@@ -683,18 +478,6 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename Tr, int DK, int C, bool COEF_ONLY>
-static hipError_t launch_intra_t(const ChunkArgs& a)
-{
-    using E = typename Tr::elem;
-    const int64_t tiles = a.BH * a.NT;
-    hipLaunchKernelGGL((mdn_intra_kernel<Tr, DK, C, COEF_ONLY>), dim3((unsigned)tiles), dim3(256), 0,
-                       (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k,
-                       a.alpha, a.mu, a.beta, a.eta, a.T, a.NT,
-                       (E*)a.Tmat, (E*)a.Aqk, a.coef, a.gamma);
-    return hipGetLastError();
-}
-
 template <typename Tr, int D, int C>
 static hipError_t launch_inter_nw(const ChunkArgs& a)
 {
@@ -702,43 +485,11 @@ static hipError_t launch_inter_nw(const ChunkArgs& a)
     using P = InterPick<Tr, D, C>;
     constexpr int NCOL = P::NCOL, NBUF = P::NBUF;
     const int64_t grid = a.BH * (D / (16 * NCOL));
-    hipLaunchKernelGGL((mdn_inter_kernel<Tr, D, C, NCOL, NBUF>), dim3((unsigned)grid), dim3(64 * (2 * NCOL + 1)), 0,
+    hipLaunchKernelGGL((mdn_inter_kernel<Tr, D, C, NCOL, NBUF>), dim3((unsigned)grid), dim3(64 * (2 * NCOL + 2)), 0,
                        (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v,
                        (const E*)a.Tmat, (const E*)a.Aqk, a.coef, a.S0, a.M0,
                        (E*)a.O, a.ST, a.MT, (E*)a.Vt, a.T, a.NT, (int)a.BH);
     return hipGetLastError();
-}
-
-template <typename Tr, bool COEF_ONLY>
-static hipError_t intra_dispatch(const ChunkArgs& a)
-{
-    if constexpr (std::is_same<Tr, TraitsBf16>::value) {
-        switch (a.dk * 1000 + a.C) {
-        case 32032: return launch_intra_t<Tr, 32, 32, COEF_ONLY>(a);
-        case 32064: return launch_intra_t<Tr, 32, 64, COEF_ONLY>(a);
-        case 64032: return launch_intra_t<Tr, 64, 32, COEF_ONLY>(a);
-        case 64064: return launch_intra_t<Tr, 64, 64, COEF_ONLY>(a);
-        case 128032: return launch_intra_t<Tr, 128, 32, COEF_ONLY>(a);
-        case 128064: return launch_intra_t<Tr, 128, 64, COEF_ONLY>(a);
-        default: return hipErrorInvalidValue;
-        }
-    } else {
-        switch (a.dk * 1000 + a.C) {
-        case 16016: return launch_intra_t<Tr, 16, 16, COEF_ONLY>(a);
-        case 16032: return launch_intra_t<Tr, 16, 32, COEF_ONLY>(a);
-        case 16064: return launch_intra_t<Tr, 16, 64, COEF_ONLY>(a);
-        case 32016: return launch_intra_t<Tr, 32, 16, COEF_ONLY>(a);
-        case 32032: return launch_intra_t<Tr, 32, 32, COEF_ONLY>(a);
-        case 32064: return launch_intra_t<Tr, 32, 64, COEF_ONLY>(a);
-        case 64016: return launch_intra_t<Tr, 64, 16, COEF_ONLY>(a);
-        case 64032: return launch_intra_t<Tr, 64, 32, COEF_ONLY>(a);
-        case 64064: return launch_intra_t<Tr, 64, 64, COEF_ONLY>(a);
-        case 128016: return launch_intra_t<Tr, 128, 16, COEF_ONLY>(a);
-        case 128032: return launch_intra_t<Tr, 128, 32, COEF_ONLY>(a);
-        case 128064: return launch_intra_t<Tr, 128, 64, COEF_ONLY>(a);
-        default: return hipErrorInvalidValue;
-        }
-    }
 }
 
 template <typename Tr>
@@ -770,26 +521,6 @@ static hipError_t inter_dispatch(const ChunkArgs& a)
         case 128064: return launch_inter_nw<Tr, 128, 64>(a);
         default: return hipErrorInvalidValue;
         }
-    }
-}
-
-hipError_t launch_chunk_intra(const ChunkArgs& a)
-{
-    if (a.BH * a.NT == 0) return hipSuccess;
-    return a.dtype == MDN_BF16 ? intra_dispatch<TraitsBf16, false>(a) : intra_dispatch<TraitsF32, false>(a);
-}
-
-hipError_t launch_chunk_coef(const ChunkArgs& a)
-{
-    if (a.BH * a.NT == 0) return hipSuccess;
-    // coefficients do not depend on dk or the element type
-    ChunkArgs b = a;
-    b.dk = 16;
-    switch (a.C) {
-    case 16: return launch_intra_t<TraitsF32, 16, 16, true>(b);
-    case 32: return launch_intra_t<TraitsF32, 16, 32, true>(b);
-    case 64: return launch_intra_t<TraitsF32, 16, 64, true>(b);
-    default: return hipErrorInvalidValue;
     }
 }
 

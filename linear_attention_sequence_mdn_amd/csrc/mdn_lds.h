@@ -1,0 +1,99 @@
+// mdn_lds.h -- LDS staging helpers shared by the chunk kernels (gfx950):
+// LDS addresses and barriers, the XOR swizzle of 16-byte pieces, matrix-core
+// operand reads from swizzled tiles, and direct global->LDS tile copies.
+#pragma once
+
+#include "mdn_device.h"
+
+namespace mdn {
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() would also wait
+// for every outstanding global load and store (including the next chunk's
+// LDS prefetch); here the chunk-boundary wait is explicit instead.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Swizzle key of row r for rows of P 16-byte pieces: the 16 rows an operand
+// read touches (perm of 16 consecutive accumulator rows, or the 4 x 4
+// row/column pattern of the transpose read) get distinct keys.
+template <int P>
+__device__ __forceinline__ int swz_key(int r) {
+    return ((r & 3) * (P / 4)) | ((r >> 3) & (P / 4 - 1));
+}
+
+// byte offset of (row r, byte b) in a row of P 16-byte pieces; piece p of
+// row r is stored at piece p ^ key(r)
+template <int P>
+__device__ __forceinline__ int swz(int r, int b) {
+    return r * P * 16 + ((((b >> 4) ^ swz_key<P>(r))) << 4) + (b & 15);
+}
+
+// A operand of a product whose B operand comes from accumulators (slot map),
+// from a swizzled LDS tile whose rows hold the contraction index.
+template <typename Tr, int P> struct LdsA;
+template <int P> struct LdsA<TraitsBf16, P> {
+    // slots of lane group g are the contiguous columns 32ks + 8g .. +7
+    static __device__ __forceinline__ bf16x8 load(const char* tile, int row, int ks, int g) {
+        union { uint4 u; bf16x8 v; } f;
+        f.u = *reinterpret_cast<const uint4*>(tile + swz<P>(row, 2 * (32 * ks + 8 * g)));
+        return f.v;
+    }
+};
+template <int P> struct LdsA<TraitsF32, P> {
+    static __device__ __forceinline__ float load(const char* tile, int row, int ks, int g) {
+        const int c = 16 * (ks >> 2) + 4 * g + (ks & 3);
+        return *reinterpret_cast<const float*>(tile + swz<P>(row, 4 * c));
+    }
+};
+
+// Copy rows [r0, r0 + R) of a tile of P 16-byte pieces per row from global
+// memory into LDS, swizzled (piece p of row r lands at piece p ^ key(r)), by
+// one wave; `dst` is the LDS byte address of the tile's row 0.  Instruction
+// i covers rows r0 + [i*64/P, (i+1)*64/P): lane l takes row r0 + i*64/P + l/P
+// and physical piece l%P, so its source offset is a per-lane constant plus a
+// per-instruction constant.  `rowoff(r)` gives the byte offset of global row
+// r relative to `base`.
+template <int R, int P, typename RowOff>
+__device__ __forceinline__ void dma_tile(uint32_t dst, const char* __restrict__ base, RowOff rowoff, int lane,
+                                         int r0 = 0)
+{
+    static_assert(P <= 64 && 64 % P == 0, "rows of at most 64 pieces");
+    constexpr int RPI = 64 / P;                       // rows per instruction
+    constexpr int NI = (R * P + 63) / 64;
+    const unsigned lr = (unsigned)lane / P, lp = (unsigned)lane % P;
+    const uint32_t d0 = dst + (uint32_t)r0 * P * 16;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const unsigned rl = i * RPI + lr;             // row within the copied range
+        const unsigned r = (unsigned)r0 + rl;
+        const unsigned p = lp ^ (unsigned)swz_key<P>((int)r);
+        if (R * P % 64 == 0 || rl < (unsigned)R)
+            __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(uintptr_t)(d0 + i * 1024), 16, 0, 0);
+    }
+}
+
+// Copy R rows of P plain 16-byte pieces (no swizzle).
+template <int R, int P, typename RowOff>
+__device__ __forceinline__ void dma_plain(uint32_t dst, const char* __restrict__ base, RowOff rowoff, int lane)
+{
+    constexpr int NI = (R * P + 63) / 64;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const unsigned s = i * 64 + (unsigned)lane;
+        const unsigned r = s / P, p = s % P;
+        if (R * P % 64 == 0 || r < (unsigned)R)
+            __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(uintptr_t)(dst + i * 1024), 16, 0, 0);
+    }
+}
+
+
+}  // namespace mdn
