@@ -16,7 +16,7 @@ Indexing: a chunk holds tokens r = 1..C (arrays are 0-based, so array row r-1
 is token r).  All cumulative quantities restart at every chunk; S and M below
 are the states at the start of the chunk.
 
-Readings of the pages used here (each also listed in the design doc):
+Readings of the pages used here:
 
 * eta_i multiplies every rank-1 term of the expansion in step 2; the printed
   expansion omits it, and without it the expansion does not reproduce the
