@@ -142,31 +142,45 @@ template <> struct Contig<TraitsF32> {
 };
 
 // ---------------------------------------------------------------------------
-// Wave-wide (64-lane) inclusive scans
+// Wave-wide (64-lane) inclusive scans on DPP lane moves: row_shr 1, 2, 4, 8
+// inside each 16-lane row, then the broadcasts of lane 15 into rows 1 and 3
+// and of lane 31 into rows 2 and 3.  A lane whose source lies outside its
+// row, or whose row is masked off, receives the identity `ident`.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_scan_add(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_move(float x, float ident) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(x), CTRL, ROWS, 0xf,
+                                                      false));
+}
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+__device__ __forceinline__ float wave_scan_add(float x) {
+    x += dpp_move<DPP_ROW_SHR1>(x, 0.f);
+    x += dpp_move<DPP_ROW_SHR2>(x, 0.f);
+    x += dpp_move<DPP_ROW_SHR4>(x, 0.f);
+    x += dpp_move<DPP_ROW_SHR8>(x, 0.f);
+    x += dpp_move<DPP_ROW_BCAST15, 0xa>(x, 0.f);
+    x += dpp_move<DPP_ROW_BCAST31, 0xc>(x, 0.f);
     return x;
 }
 
-// log(exp(a) + exp(b)) without overflow; -inf is the identity.
-__device__ __forceinline__ float log_add_exp(float a, float b) {
-    const float m = fmaxf(a, b);
-    if (m == -INFINITY) return m;
-    return m + log1pf(expf(-fabsf(a - b)));
+// Inclusive scan of the affine maps x -> A x + B in lane order: afterwards
+// lane r holds the composition of the maps of lanes 0..r (applied in that
+// order), so B is the value reached from x = 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ void affine_step(float& A, float& B) {
+    const float Ap = dpp_move<CTRL, ROWS>(A, 1.f), Bp = dpp_move<CTRL, ROWS>(B, 0.f);
+    B = fmaf(A, Bp, B);
+    A *= Ap;
 }
-
-__device__ __forceinline__ float wave_scan_logaddexp(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float y = __shfl_up(x, off, 64);
-        if (lane >= off) x = log_add_exp(x, y);
-    }
-    return x;
+__device__ __forceinline__ void wave_scan_affine(float& A, float& B) {
+    affine_step<DPP_ROW_SHR1>(A, B);
+    affine_step<DPP_ROW_SHR2>(A, B);
+    affine_step<DPP_ROW_SHR4>(A, B);
+    affine_step<DPP_ROW_SHR8>(A, B);
+    affine_step<DPP_ROW_BCAST15, 0xa>(A, B);
+    affine_step<DPP_ROW_BCAST31, 0xc>(A, B);
 }
 
 // ---------------------------------------------------------------------------

@@ -38,6 +38,39 @@
 
 namespace mdn {
 
+// A operand read straight from a global row, in the contraction order of
+// LdsA (bf16: lane group g of step ks holds columns 32ks + 8g .. +7; fp32:
+// column 16(ks/4) + 4g + ks%4).
+template <typename Tr, int KSD> struct RowA;
+template <int KSD> struct RowA<TraitsBf16, KSD> {
+    static __device__ __forceinline__ void load(bf16x8 (&a)[KSD], const __bf16* row, int g) {
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            union { uint4 u; bf16x8 v; } f;
+            f.u = *reinterpret_cast<const uint4*>(row + 32 * ks + 8 * g);
+            a[ks] = f.v;
+        }
+    }
+    static __device__ __forceinline__ void zero(bf16x8 (&a)[KSD]) {
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) a[ks] = Slots<TraitsBf16>::zero();
+    }
+};
+template <int KSD> struct RowA<TraitsF32, KSD> {
+    static __device__ __forceinline__ void load(float (&a)[KSD], const float* row, int g) {
+#pragma unroll
+        for (int m = 0; m < KSD / 4; ++m) {
+            const floatx4 v = *reinterpret_cast<const floatx4*>(row + 16 * m + 4 * g);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a[4 * m + u] = v[u];
+        }
+    }
+    static __device__ __forceinline__ void zero(float (&a)[KSD]) {
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) a[ks] = 0.f;
+    }
+};
+
 template <typename Tr, int DK, int C>
 struct IntraLayout {
     using E = typename Tr::elem;
@@ -48,12 +81,19 @@ struct IntraLayout {
     static constexpr int AS = C + 4;                 // row stride of A (floats)
     static constexpr int ABYTES = C * AS * 4;
     static constexpr int OUT = C * C * ES;           // one out tile (T or Aqk)
-    static constexpr int DS = 20;                    // row stride of a diagonal inverse (floats)
+    static constexpr int DS = 16;                    // row stride of a diagonal inverse (floats)
     static constexpr int TD = NCT * 16 * DS * 4;
-    // region X: K, Q tiles; then A (fp32) and the Aqk out tile
-    static constexpr int RX = 2 * KT > ABYTES + OUT ? 2 * KT : ABYTES + OUT;
-    // region Y: Gamma (fp32); then the T out tile and the diagonal inverses
-    static constexpr int RY = C * C * 4 > OUT + 2 * TD ? C * C * 4 : OUT + 2 * TD;
+    // Gamma, column-major: column i at floats [i*GS, (i+1)*GS), 4 zeros then
+    // rows 0..C-1, so that rows r-4..r-1 (the shifted Gamma^-) sit just
+    // before rows r..r+3 and both are aligned 16-byte reads
+    static constexpr int GS = C + 4;
+    static constexpr int GBYTES = C * GS * 4;
+    // region X: the K tile; then the T out tile, the diagonal inverses and
+    // the Aqk out tile
+    static constexpr int OT = 0, OD = OUT, OQ = OUT + TD;
+    static constexpr int RX = KT > 2 * OUT + TD ? KT : 2 * OUT + TD;
+    // region Y: Gamma; then A (fp32)
+    static constexpr int RY = GBYTES > ABYTES ? GBYTES : ABYTES;
     // Gamma scan: NB row blocks of RB rows, one thread per (block, column)
     static constexpr int NB = 256 / C;
     static constexpr int RB = C / NB;
@@ -76,13 +116,16 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
     using SL = Slots<Tr>;
     using L = IntraLayout<Tr, DK, C>;
     using frag = typename Tr::frag;
-    constexpr int NCT = L::NCT, KSD = DK / Tr::KW, NB = L::NB, RB = L::RB;
+    constexpr int NCT = L::NCT, KSD = DK / Tr::KW, NB = L::NB, RB = L::RB, GS = L::GS;
     constexpr bool BF16 = std::is_same<Tr, TraitsBf16>::value;
 
     __shared__ __attribute__((aligned(16))) char rx[COEF_ONLY ? 16 : L::RX];
     __shared__ __attribute__((aligned(16))) char ry[L::RY];
-    __shared__ float sa[C], sbt[C], slm[C], sla[C], se[C];
-    __shared__ float xe[NB][C];                      // Gamma block carries
+    __shared__ __attribute__((aligned(16))) floatx4 sg[C];     // (alpha, beta, mu, eta) per row
+    __shared__ __attribute__((aligned(16))) float sal[C];      // alpha per row
+    __shared__ float slm[C];                                   // LM (cumulative log mu)
+    __shared__ float xe[NB][C];                                // Gamma scan: block ends
+    __shared__ float xd[NB];                                   // Gamma scan: alpha product per block
 
     const int64_t tile = blockIdx.x;
     const int64_t bh = tile / NT, n = tile % NT;
@@ -93,22 +136,38 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
     const int g = lane >> 4, nn = lane & 15;
     float* cf = coef + tile * MDN_COEF_ROWS * C;
 
-    // ---- 1. K, Q -> LDS (waves 1-3); gates and scans (wave 0) ----------------
+    // Product roles.  Accumulator row x of block t stands for chunk row
+    // perm(16t + x) (bf16 slot map; identity for fp32), so the 16 rows of an
+    // operand read get distinct swizzle keys.  With four row blocks wave w
+    // owns row block w of K K^T and row block 3-w of Q K^T (equal numbers of
+    // lower tiles); otherwise wave w owns row block w % NCT of product w / NCT.
+    constexpr bool BOTH = NCT >= 4;
+    const int trK = BOTH ? wave : wave % NCT;
+    const int trQ = BOTH ? NCT - 1 - wave : wave % NCT;
+    const int mat = BOTH ? 0 : wave / NCT;
+    const bool doK = BOTH || mat == 0, doQ = BOTH || mat == 1;
+    // The Q rows of a wave's block are used by that wave alone: they go
+    // straight from global memory into A-operand registers (zero past the end).
+    frag aQ[KSD];
+    auto load_q = [&]() __attribute__((always_inline)) {
+        const int row = SL::perm(16 * trQ + nn);
+        if (row < valid) RowA<Tr, KSD>::load(aQ, q + (rowbase + row) * DK, g);
+        else RowA<Tr, KSD>::zero(aQ);
+    };
+
+    // ---- 1. K -> LDS (waves 1-3), Q -> registers; gates and scans (wave 0) ---
     if constexpr (!COEF_ONLY) {
         if (wave > 0) {
-            // 2*NCT blocks of 16 rows (K blocks, then Q blocks), dealt to waves 1-3;
-            // rows past `valid` repeat the last valid row (zeroed below)
+            // NCT blocks of 16 K rows, dealt to waves 1-3; rows past `valid`
+            // repeat the last valid row (zeroed below)
             const unsigned vlast = (unsigned)valid - 1;
             auto seq_row = [&](unsigned r) { return (r < vlast ? r : vlast) * (unsigned)(DK * L::ES); };
             const uint32_t base = lds_addr(rx);
 #pragma unroll
-            for (int j = 0; j < 2 * NCT; ++j) {
-                if (j % 3 == wave - 1) {
-                    const E* src = (j < NCT ? k : q) + rowbase * DK;
-                    dma_tile<16, L::PK>(base + (j < NCT ? 0 : L::KT), reinterpret_cast<const char*>(src), seq_row,
-                                        lane, 16 * (j % NCT));
-                }
-            }
+            for (int j = 0; j < NCT; ++j)
+                if (j % 3 == wave - 1)
+                    dma_tile<16, L::PK>(base, reinterpret_cast<const char*>(k + rowbase * DK), seq_row, lane, 16 * j);
+            if (doQ) load_q();
         }
     }
     if (wave == 0) {
@@ -117,59 +176,75 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
             const size_t gi = rowbase + lane;
             a = alpha[gi]; m = mu[gi]; bt = beta[gi]; e = eta[gi];
         }
-        const float la = wave_scan_add(logf(a), lane);
-        const float lm = wave_scan_add(logf(m), lane);
-        const float lc = wave_scan_logaddexp(logf(bt) + lm - la, lane);
-        const float b = expf(la + lc);
+        if constexpr (!COEF_ONLY)
+            if (doQ) load_q();                       // after the gate loads
+        const float la = wave_scan_add(logf(a));
+        const float lm = wave_scan_add(logf(m));
+        // b_r = alpha_r b_{r-1} + beta_r mubar_r (b_{-1} = 0): a scan of the
+        // affine maps x -> A x + B, every term non-negative
+        float A = a, Bv = bt * expf(lm);
+        wave_scan_affine(A, Bv);
+        const float b = Bv;
         float bprev = __shfl_up(b, 1, 64);
         if (lane == 0) bprev = 0.f;
         if (lane < C) {
-            sa[lane] = a; sbt[lane] = bt; slm[lane] = lm; sla[lane] = la; se[lane] = e;
+            sg[lane] = floatx4{a, bt, m, e};
+            sal[lane] = a;
+            slm[lane] = lm;
             cf[MDN_COEF_ABAR * C + lane] = expf(la);
             cf[MDN_COEF_ABP * C + lane] = a * bprev;
             cf[MDN_COEF_B * C + lane] = b;
             cf[MDN_COEF_LA * C + lane] = la;
             cf[MDN_COEF_LM * C + lane] = lm;
-            cf[MDN_COEF_LOGC * C + lane] = lc;
+            cf[MDN_COEF_LOGC * C + lane] = logf(b) - la;   // log c_r = log(b_r / abar_r)
         }
     }
     lds_barrier();
 
-    // ---- 2. Gamma (fp32, row-major C x C in region Y) ------------------------
-    float* Gm = reinterpret_cast<float*>(ry);
+    // ---- 2. Gamma: column i, rows [r0, r0 + RB) per thread -------------------
+    // gamma_{r,i} = alpha_r gamma_{r-1,i} + beta_r w_{r,i},  w_{r,i} = mubar_r / mubar_i
+    // (w_{i,i} = 1, w_{r,i} = mu_r w_{r-1,i}).  Each thread runs the recurrence
+    // from zero over its block; the carry gamma_{r0-1,i} from the earlier
+    // blocks enters scaled by the running product of alpha.
+    float* Gt = reinterpret_cast<float*>(ry);
     {
         const int i = tid % C, bk = tid / C, r0 = bk * RB;
-        const float lmi = slm[i], ei = se[i];
-        float lv[RB];
-        float loc = 0.f;
+        const float lmi = slm[i], ei = sg[i][3];
+        float w = (r0 > i) ? expf(slm[r0 > 0 ? r0 - 1 : 0] - lmi) : 0.f;
+        float loc = 0.f, d = 1.f;
+        float lv[RB], dv[RB];
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
-            const int r = r0 + j;
-            loc = sa[r] * loc + (r >= i ? sbt[r] * expf(slm[r] - lmi) : 0.f);
+            const floatx4 gr = sg[r0 + j];
+            w = (r0 + j == i) ? 1.f : w * gr[2];
+            loc = fmaf(gr[0], loc, gr[1] * w);
+            d *= gr[0];
             lv[j] = loc;
+            dv[j] = d;
         }
         xe[bk][i] = loc;
+        if (i == 0) xd[bk] = d;
         lds_barrier();
-        // gamma_{r0-1,i}: carries of the earlier blocks, each decayed by the
-        // product of alpha over the next block
-        float G = 0.f, lprev = 0.f;
+        float G = 0.f;
 #pragma unroll
-        for (int bb = 0; bb < NB - 1; ++bb) {
-            if (bb < bk) {
-                const float lend = sla[bb * RB + RB - 1];
-                G = expf(lend - lprev) * G + xe[bb][i];
-                lprev = lend;
+        for (int bb = 0; bb < NB - 1; ++bb)
+            if (bb < bk) G = fmaf(xd[bb], G, xe[bb][i]);
+        float* col = Gt + i * GS + 4 + r0;
+        if (bk == 0) *reinterpret_cast<floatx4*>(Gt + i * GS) = zero4();   // Gamma^- of row 0
+        if constexpr (RB % 4 == 0) {
+#pragma unroll
+            for (int j = 0; j < RB; j += 4) {
+                floatx4 o;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o[u] = ei * fmaf(dv[j + u], G, lv[j + u]);
+                *reinterpret_cast<floatx4*>(col + j) = o;
             }
-        }
-        float last = 0.f;
+        } else {
 #pragma unroll
-        for (int j = 0; j < RB; ++j) {
-            const int r = r0 + j;
-            last = ei * (lv[j] + expf(sla[r] - lprev) * G);
-            Gm[r * C + i] = last;
+            for (int j = 0; j < RB; ++j) col[j] = ei * fmaf(dv[j], G, lv[j]);
         }
         if (bk == NB - 1) {                          // this thread holds row C-1
-            cf[MDN_COEF_GS * C + i] = last;
+            cf[MDN_COEF_GS * C + i] = ei * fmaf(dv[RB - 1], G, lv[RB - 1]);
             cf[MDN_COEF_GM * C + i] = ei * expf(slm[C - 1] - lmi);
         }
     }
@@ -177,7 +252,7 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
         lds_barrier();
         if (gamma) {
             float* gp = gamma + tile * C * C;
-            for (int idx = tid; idx < C * C; idx += 256) gp[idx] = Gm[idx];
+            for (int idx = tid; idx < C * C; idx += 256) gp[idx] = Gt[(idx % C) * GS + 4 + idx / C];
         }
         return;
     }
@@ -185,117 +260,131 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
     __builtin_amdgcn_s_waitcnt(0);                   // this wave's K/Q copies have landed
     lds_barrier();                                   // Gamma and the K/Q tiles visible
     const char* Kl = rx;
-    const char* Ql = rx + L::KT;
-    if (valid < C) {                                 // ragged last chunk: zero rows past the end
+    if (valid < C) {                                 // ragged last chunk: zero K rows past the end
         constexpr int W = L::PK;                     // 16-byte words per row
-        for (int w = valid * W + tid; w < C * W; w += 256) {
+        for (int w = valid * W + tid; w < C * W; w += 256)
             reinterpret_cast<uint4*>(rx)[w] = uint4{0u, 0u, 0u, 0u};
-            reinterpret_cast<uint4*>(rx + L::KT)[w] = uint4{0u, 0u, 0u, 0u};
-        }
         lds_barrier();
     }
 
     // ---- 3. K K^T and Q K^T on the matrix cores --------------------------------
-    // Accumulator row x of block t stands for chunk row perm(16t + x) (bf16
-    // slot map; identity for fp32), so the 16 rows of an operand read get
-    // distinct swizzle keys.  With four or more row blocks a wave owns row
-    // block `tr` of both products; otherwise wave w owns product w / NCT.
-    constexpr bool BOTH = NCT >= 4;
-    const int tr = BOTH ? wave : wave % NCT;
-    const int mat = BOTH ? 0 : wave / NCT;
-    const bool doK = BOTH || mat == 0, doQ = BOTH || mat == 1;
     auto lower = [&](int rb, int cb) { return BF16 ? ((cb >> 1) <= (rb >> 1)) : (cb <= rb); };
     floatx4 accK[NCT], accQ[NCT];
 #pragma unroll
     for (int tc = 0; tc < NCT; ++tc) { accK[tc] = zero4(); accQ[tc] = zero4(); }
+    const int RK = SL::perm(16 * trK + 4 * g), RQ = SL::perm(16 * trQ + 4 * g);   // first of 4 rows
     if (doK || doQ) {
-        frag aK[KSD], aQ[KSD];
+        frag aK[KSD];
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-            if (doK) aK[ks] = LdsA<Tr, L::PK>::load(Kl, SL::perm(16 * tr + nn), ks, g);
-            if (doQ) aQ[ks] = LdsA<Tr, L::PK>::load(Ql, SL::perm(16 * tr + nn), ks, g);
-        }
+        for (int ks = 0; ks < KSD; ++ks)
+            if (doK) aK[ks] = LdsA<Tr, L::PK>::load(Kl, SL::perm(16 * trK + nn), ks, g);
 #pragma unroll
         for (int tc = 0; tc < NCT; ++tc) {
-            if (lower(tr, tc)) {
+            const bool uk = doK && lower(trK, tc), uq = doQ && lower(trQ, tc);
+            if (uk || uq) {
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks) {
                     const frag bk = LdsA<Tr, L::PK>::load(Kl, SL::perm(16 * tc + nn), ks, g);
-                    if (doK) accK[tc] = Tr::mma(aK[ks], bk, accK[tc]);
-                    if (doQ) accQ[tc] = Tr::mma(aQ[ks], bk, accQ[tc]);
+                    if (uk) accK[tc] = Tr::mma(aK[ks], bk, accK[tc]);
+                    if (uq) accQ[tc] = Tr::mma(aQ[ks], bk, accQ[tc]);
                 }
             }
         }
-        // apply the decay weights (Gamma is still in region Y)
+        // decay weights (Gamma is still in region Y):
+        //   A_{r,i}   = alpha_r (K K^T)_{r,i} Gamma_{r-1,i}   (i < r)
+        //   Aqk_{r,i} = (Q K^T)_{r,i} Gamma_{r,i}             (i <= r)
+        const floatx4 al = *reinterpret_cast<const floatx4*>(sal + RK);
 #pragma unroll
         for (int tc = 0; tc < NCT; ++tc) {
             const int i = SL::perm(16 * tc + nn);
+            const float* gc = Gt + i * GS + 4;
+            if (doK && lower(trK, tc)) {
+                const floatx4 g4 = *reinterpret_cast<const floatx4*>(gc + RK);
+                const floatx4 gp = *reinterpret_cast<const floatx4*>(gc + RK - 4);
+                const floatx4 gm = floatx4{gp[3], g4[0], g4[1], g4[2]};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = SL::perm(16 * tr + 4 * g) + e;
-                accK[tc][e] = (i < r) ? sa[r] * accK[tc][e] * Gm[(r > 0 ? r - 1 : 0) * C + i] : 0.f;
-                accQ[tc][e] = (i <= r) ? accQ[tc][e] * Gm[r * C + i] : 0.f;
+                for (int e = 0; e < 4; ++e) accK[tc][e] = (i < RK + e) ? al[e] * accK[tc][e] * gm[e] : 0.f;
+            }
+            if (doQ && lower(trQ, tc)) {
+                const floatx4 g4 = *reinterpret_cast<const floatx4*>(gc + RQ);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) accQ[tc][e] = (i <= RQ + e) ? accQ[tc][e] * g4[e] : 0.f;
             }
         }
     }
-    lds_barrier();                                   // K, Q and Gamma reads done
+    lds_barrier();                                   // K and Gamma reads done
 
-    float* sA = reinterpret_cast<float*>(rx);        // A, fp32, row stride AS
-    E* oAq = reinterpret_cast<E*>(rx + L::ABYTES);   // Aqk out tile, row-major C x C
-    E* oT = reinterpret_cast<E*>(ry);                // T out tile, row-major C x C
-    float* sTd = reinterpret_cast<float*>(ry + L::OUT);   // T_aa, row-major, stride DS
-    float* sTt = sTd + NCT * 16 * L::DS;                  // T_aa transposed
+    float* sA = reinterpret_cast<float*>(ry);        // A, fp32, row stride AS
+    E* oT = reinterpret_cast<E*>(rx + L::OT);        // T out tile, row-major C x C
+    float* sTd = reinterpret_cast<float*>(rx + L::OD);    // T_aa, row-major, stride DS
+    E* oAq = reinterpret_cast<E*>(rx + L::OQ);       // Aqk out tile, row-major C x C
     if (doK || doQ) {
 #pragma unroll
         for (int tc = 0; tc < NCT; ++tc) {
             const int i = SL::perm(16 * tc + nn);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = SL::perm(16 * tr + 4 * g) + e;
-                if (doK) sA[r * L::AS + i] = accK[tc][e];
-                if (doQ) oAq[r * C + i] = Tr::from_f(accQ[tc][e]);
+                if (doK) sA[(RK + e) * L::AS + i] = accK[tc][e];
+                if (doQ) oAq[(RQ + e) * C + i] = Tr::from_f(accQ[tc][e]);
             }
         }
     }
     lds_barrier();
 
-    // ---- 4a. diagonal blocks of T: forward substitution, lane = column -------
-    if (wave < NCT) {
-        const int a = wave, j = nn;
-        float tcol[16];
+    // ---- 4a. diagonal blocks of T (wave 0, lane = 16 * block + column) --------
+    // forward substitution T[r][j] = delta_rj - sum_{i<r} A[r][i] T[i][j]
+    if (wave == 0) {
+        const int a = g, j = nn;
+        if (a < NCT) {
+            const float* Ab = sA + 16 * a * L::AS + 16 * a;
+            float tcol[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float* Ar = sA + (16 * a + r) * L::AS + 16 * a;
-            float s = (r == j) ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) {
+                float s = (r == j) ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 0; i < r; ++i) s = fmaf(-Ar[i], tcol[i], s);
-            tcol[r] = s;
-        }
-        if (g == 0) {
+                for (int m4 = 0; m4 < (r + 3) / 4; ++m4) {
+                    const floatx4 a4 = *reinterpret_cast<const floatx4*>(Ab + r * L::AS + 4 * m4);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (4 * m4 + u < r) s = fmaf(-a4[u], tcol[4 * m4 + u], s);
+                }
+                tcol[r] = s;
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 sTd[(16 * a + r) * L::DS + j] = tcol[r];
-                sTt[(16 * a + j) * L::DS + r] = tcol[r];
                 oT[(16 * a + r) * C + 16 * a + j] = Tr::from_f(tcol[r]);
             }
         }
-    }
-    for (int idx = tid; idx < C * C; idx += 256) {   // strictly upper blocks are zero
-        const int r = idx / C, c = idx % C;
-        if ((r >> 4) < (c >> 4)) oT[idx] = Tr::from_f(0.f);
+    } else {
+        // strictly upper blocks (a < b) of T are zero: waves 1-3, 16-byte stores
+        constexpr int PB = 16 * L::ES / 16;          // 16-byte pieces per block row
+        constexpr int NU = NCT * (NCT - 1) / 2;
+        for (int idx = tid - 64; idx < NU * 16 * PB; idx += 192) {
+            int blk = idx / (16 * PB), a = 0;
+            while (blk >= NCT - 1 - a) { blk -= NCT - 1 - a; ++a; }
+            const int b = a + 1 + blk, rem = idx % (16 * PB);
+            const int row = 16 * a + rem / PB;
+            *reinterpret_cast<uint4*>(reinterpret_cast<char*>(oT) + (row * C + 16 * b) * L::ES + (rem % PB) * 16) =
+                uint4{0u, 0u, 0u, 0u};
+        }
     }
     lds_barrier();
 
     // ---- 4b. column block b of T below the diagonal (fp32 matrix cores) -------
-    // Contraction slot map: in step ks, lane group g carries inner index
-    // 4g + ks of the 16-block, so an accumulator (rows 4g + e) is the next
-    // product's B operand as it stands.
-    if (wave < NCT - 1) {
-        const int b = wave;
+    // Wave w >= 1 owns column block b = NCT-1-w.  Contraction slot map: in
+    // step ks, lane group g carries inner index 4g + ks of the 16-block, so
+    // an accumulator (rows 4g + e) is the next product's B operand as it stands.
+    if (wave >= 1 && wave < NCT) {
+        const int b = NCT - 1 - wave;
         floatx4 Tc[NCT];
 #pragma unroll
-        for (int c = 0; c < NCT; ++c)
-            Tc[c] = (c == b) ? *reinterpret_cast<const floatx4*>(sTt + (16 * c + nn) * L::DS + 4 * g) : zero4();
+        for (int c = 0; c < NCT; ++c) {
+            Tc[c] = zero4();
+            if (c == b)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Tc[c][e] = sTd[(16 * c + 4 * g + e) * L::DS + nn];
+        }
 #pragma unroll
         for (int a = 1; a < NCT; ++a) {
             if (a > b) {
