@@ -81,23 +81,86 @@ struct IntraLayout {
     static constexpr int AS = C + 4;                 // row stride of A (floats)
     static constexpr int ABYTES = C * AS * 4;
     static constexpr int OUT = C * C * ES;           // one out tile (T or Aqk)
-    static constexpr int DS = 16;                    // row stride of a diagonal inverse (floats)
-    static constexpr int TD = NCT * 16 * DS * 4;
     // Gamma, column-major: column i at floats [i*GS, (i+1)*GS), 4 zeros then
     // rows 0..C-1, so that rows r-4..r-1 (the shifted Gamma^-) sit just
     // before rows r..r+3 and both are aligned 16-byte reads
     static constexpr int GS = C + 4;
     static constexpr int GBYTES = C * GS * 4;
-    // region X: the K tile; then the T out tile, the diagonal inverses and
-    // the Aqk out tile
-    static constexpr int OT = 0, OD = OUT, OQ = OUT + TD;
-    static constexpr int RX = KT > 2 * OUT + TD ? KT : 2 * OUT + TD;
-    // region Y: Gamma; then A (fp32)
+    // region X: the K tile; then the T out tile and the Aqk out tile
+    static constexpr int OT = 0, OQ = OUT;
+    static constexpr int RX = KT > 2 * OUT ? KT : 2 * OUT;
+    // region Y: Gamma; then A (fp32), whose diagonal blocks are replaced by
+    // the inverses T_aa once those are known
     static constexpr int RY = GBYTES > ABYTES ? GBYTES : ABYTES;
     // Gamma scan: NB row blocks of RB rows, one thread per (block, column)
     static constexpr int NB = 256 / C;
     static constexpr int RB = C / NB;
+    static constexpr int KSD = DK / Tr::KW;
     static_assert(NB * C == 256 && RB * NB == C, "256 threads cover the C x C Gamma scan");
+};
+
+// One wave's share of K K^T and Q K^T: row block TRK of K K^T (if DOK) and
+// row block TRQ of Q K^T (if DOQ), over the column blocks of the lower
+// triangle, then the decay weights
+//   A_{r,i}   = alpha_r (K K^T)_{r,i} Gamma_{r-1,i}   (i < r)
+//   Aqk_{r,i} = (Q K^T)_{r,i} Gamma_{r,i}             (i <= r).
+// Accumulator row x of block t stands for chunk row perm(16t + x) (bf16
+// slot map; identity for fp32), so the 16 rows of an operand read get
+// distinct swizzle keys.  The B operands (K rows of column block tc) are
+// read once and serve both products.  Gamma is column-major (see
+// IntraLayout), so the four rows of a lane are one 16-byte read.
+template <typename Tr, typename L>
+struct IntraProducts {
+    using frag = typename Tr::frag;
+    using SL = Slots<Tr>;
+    static constexpr int NCT = L::NCT, KSD = L::KSD;
+    static constexpr bool lower(int rb, int cb) {
+        return std::is_same<Tr, TraitsBf16>::value ? ((cb >> 1) <= (rb >> 1)) : (cb <= rb);
+    }
+    template <int TRK, int TRQ, bool DOK, bool DOQ>
+    static __device__ __forceinline__ void run(const char* Kl, const frag (&aQ)[KSD], const float* Gt,
+                                               const float* sal, int g, int nn,
+                                               floatx4 (&accK)[NCT], floatx4 (&accQ)[NCT]) {
+        frag aK[KSD];
+        if constexpr (DOK) {
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) aK[ks] = LdsA<Tr, L::PK>::load(Kl, SL::perm(16 * TRK + nn), ks, g);
+        }
+#pragma unroll
+        for (int tc = 0; tc < NCT; ++tc) {
+            const bool uk = DOK && lower(TRK, tc), uq = DOQ && lower(TRQ, tc);
+            if (uk || uq) {
+                frag bk[KSD];
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) bk[ks] = LdsA<Tr, L::PK>::load(Kl, SL::perm(16 * tc + nn), ks, g);
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) {
+                    if (uk) accK[tc] = Tr::mma(aK[ks], bk[ks], accK[tc]);
+                    if (uq) accQ[tc] = Tr::mma(aQ[ks], bk[ks], accQ[tc]);
+                }
+            }
+        }
+        constexpr int GS = L::GS;
+        const int RK = SL::perm(16 * TRK + 4 * g), RQ = SL::perm(16 * TRQ + 4 * g);
+        const floatx4 al = *reinterpret_cast<const floatx4*>(sal + RK);
+#pragma unroll
+        for (int tc = 0; tc < NCT; ++tc) {
+            const int i = SL::perm(16 * tc + nn);
+            const float* gc = Gt + i * GS + 4;
+            if (DOK && lower(TRK, tc)) {
+                const floatx4 g4 = *reinterpret_cast<const floatx4*>(gc + RK);
+                const floatx4 gp = *reinterpret_cast<const floatx4*>(gc + RK - 4);
+                const floatx4 gm = floatx4{gp[3], g4[0], g4[1], g4[2]};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) accK[tc][e] = (i < RK + e) ? al[e] * accK[tc][e] * gm[e] : 0.f;
+            }
+            if (DOQ && lower(TRQ, tc)) {
+                const floatx4 g4 = *reinterpret_cast<const floatx4*>(gc + RQ);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) accQ[tc][e] = (i <= RQ + e) ? accQ[tc][e] * g4[e] : 0.f;
+            }
+        }
+    }
 };
 
 template <typename Tr, int DK, int C, bool COEF_ONLY>
@@ -117,7 +180,6 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
     using L = IntraLayout<Tr, DK, C>;
     using frag = typename Tr::frag;
     constexpr int NCT = L::NCT, KSD = DK / Tr::KW, NB = L::NB, RB = L::RB, GS = L::GS;
-    constexpr bool BF16 = std::is_same<Tr, TraitsBf16>::value;
 
     __shared__ __attribute__((aligned(16))) char rx[COEF_ONLY ? 16 : L::RX];
     __shared__ __attribute__((aligned(16))) char ry[L::RY];
@@ -268,55 +330,37 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
     }
 
     // ---- 3. K K^T and Q K^T on the matrix cores --------------------------------
-    auto lower = [&](int rb, int cb) { return BF16 ? ((cb >> 1) <= (rb >> 1)) : (cb <= rb); };
+    // The role of each wave is a template argument, so that the product code
+    // is straight-line (no uniform branches between the matrix-core ops).
     floatx4 accK[NCT], accQ[NCT];
 #pragma unroll
     for (int tc = 0; tc < NCT; ++tc) { accK[tc] = zero4(); accQ[tc] = zero4(); }
     const int RK = SL::perm(16 * trK + 4 * g), RQ = SL::perm(16 * trQ + 4 * g);   // first of 4 rows
-    if (doK || doQ) {
-        frag aK[KSD];
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks)
-            if (doK) aK[ks] = LdsA<Tr, L::PK>::load(Kl, SL::perm(16 * trK + nn), ks, g);
-#pragma unroll
-        for (int tc = 0; tc < NCT; ++tc) {
-            const bool uk = doK && lower(trK, tc), uq = doQ && lower(trQ, tc);
-            if (uk || uq) {
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) {
-                    const frag bk = LdsA<Tr, L::PK>::load(Kl, SL::perm(16 * tc + nn), ks, g);
-                    if (uk) accK[tc] = Tr::mma(aK[ks], bk, accK[tc]);
-                    if (uq) accQ[tc] = Tr::mma(aQ[ks], bk, accQ[tc]);
-                }
+    {
+        using P = IntraProducts<Tr, L>;
+        if constexpr (NCT >= 4) {
+            switch (wave) {
+            case 0: P::template run<0, 3, true, true>(Kl, aQ, Gt, sal, g, nn, accK, accQ); break;
+            case 1: P::template run<1, 2, true, true>(Kl, aQ, Gt, sal, g, nn, accK, accQ); break;
+            case 2: P::template run<2, 1, true, true>(Kl, aQ, Gt, sal, g, nn, accK, accQ); break;
+            default: P::template run<3, 0, true, true>(Kl, aQ, Gt, sal, g, nn, accK, accQ); break;
             }
-        }
-        // decay weights (Gamma is still in region Y):
-        //   A_{r,i}   = alpha_r (K K^T)_{r,i} Gamma_{r-1,i}   (i < r)
-        //   Aqk_{r,i} = (Q K^T)_{r,i} Gamma_{r,i}             (i <= r)
-        const floatx4 al = *reinterpret_cast<const floatx4*>(sal + RK);
-#pragma unroll
-        for (int tc = 0; tc < NCT; ++tc) {
-            const int i = SL::perm(16 * tc + nn);
-            const float* gc = Gt + i * GS + 4;
-            if (doK && lower(trK, tc)) {
-                const floatx4 g4 = *reinterpret_cast<const floatx4*>(gc + RK);
-                const floatx4 gp = *reinterpret_cast<const floatx4*>(gc + RK - 4);
-                const floatx4 gm = floatx4{gp[3], g4[0], g4[1], g4[2]};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) accK[tc][e] = (i < RK + e) ? al[e] * accK[tc][e] * gm[e] : 0.f;
+        } else if constexpr (NCT == 2) {
+            switch (wave) {
+            case 0: P::template run<0, 0, true, false>(Kl, aQ, Gt, sal, g, nn, accK, accQ); break;
+            case 1: P::template run<1, 1, true, false>(Kl, aQ, Gt, sal, g, nn, accK, accQ); break;
+            case 2: P::template run<0, 0, false, true>(Kl, aQ, Gt, sal, g, nn, accK, accQ); break;
+            default: P::template run<1, 1, false, true>(Kl, aQ, Gt, sal, g, nn, accK, accQ); break;
             }
-            if (doQ && lower(trQ, tc)) {
-                const floatx4 g4 = *reinterpret_cast<const floatx4*>(gc + RQ);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) accQ[tc][e] = (i <= RQ + e) ? accQ[tc][e] * g4[e] : 0.f;
-            }
+        } else {
+            if (wave == 0) P::template run<0, 0, true, false>(Kl, aQ, Gt, sal, g, nn, accK, accQ);
+            else if (wave == 1) P::template run<0, 0, false, true>(Kl, aQ, Gt, sal, g, nn, accK, accQ);
         }
     }
     lds_barrier();                                   // K and Gamma reads done
 
-    float* sA = reinterpret_cast<float*>(ry);        // A, fp32, row stride AS
+    float* sA = reinterpret_cast<float*>(ry);        // A, fp32, row stride AS (then T_aa on the diagonal)
     E* oT = reinterpret_cast<E*>(rx + L::OT);        // T out tile, row-major C x C
-    float* sTd = reinterpret_cast<float*>(rx + L::OD);    // T_aa, row-major, stride DS
     E* oAq = reinterpret_cast<E*>(rx + L::OQ);       // Aqk out tile, row-major C x C
     if (doK || doQ) {
 #pragma unroll
@@ -350,9 +394,10 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
                 }
                 tcol[r] = s;
             }
+            // every lane of the group has read all of A_aa: overwrite it with T_aa
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                sTd[(16 * a + r) * L::DS + j] = tcol[r];
+                sA[(16 * a + r) * L::AS + 16 * a + j] = tcol[r];
                 oT[(16 * a + r) * C + 16 * a + j] = Tr::from_f(tcol[r]);
             }
         }
@@ -383,7 +428,7 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
             Tc[c] = zero4();
             if (c == b)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Tc[c][e] = sTd[(16 * c + 4 * g + e) * L::DS + nn];
+                for (int e = 0; e < 4; ++e) Tc[c][e] = sA[(16 * c + 4 * g + e) * L::AS + 16 * c + nn];
         }
 #pragma unroll
         for (int a = 1; a < NCT; ++a) {
@@ -397,7 +442,7 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
                         for (int ks = 0; ks < 4; ++ks) X = TraitsF32::mma(Ao[ks], Tc[c][ks], X);
                     }
                 }
-                const floatx4 To = *reinterpret_cast<const floatx4*>(sTd + (16 * a + nn) * L::DS + 4 * g);
+                const floatx4 To = *reinterpret_cast<const floatx4*>(sA + (16 * a + nn) * L::AS + 16 * a + 4 * g);
                 floatx4 Y = zero4();
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) Y = TraitsF32::mma(To[ks], X[ks], Y);
