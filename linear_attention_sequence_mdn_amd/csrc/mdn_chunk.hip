@@ -40,28 +40,34 @@ namespace mdn {
 // mdn_inter_kernel
 //
 // One workgroup owns a slab of 16*NCOL state columns of one head and runs
-// the chunks of that head in order.  For every 16-column tile there are two
-// waves that split the work of a chunk by state:
-//   S-wave: W = V - Diag(abar) K S + Diag(alpha b_prev) K M, vtilde = T W,
-//           S <- abar_C S - b_C M + K^T Diag(gS) vtilde        (S in registers)
-//   M-wave: Q S and Q M for the output, M <- mubar_C M - K^T Diag(gM) vtilde,
-//           O = Diag(abar) Q S - Diag(b) Q M + Aqk vtilde     (M in registers)
-// The two exchange the chunk-start states (bf16 S, fp32 M) and vtilde through
-// LDS, with two workgroup barriers per chunk.
+// the chunks of that head in order.  State columns are independent.  For
+// every 16-column tile, RS compute waves split the dk state rows into RS
+// halves: wave (ct, h) holds rows [h*D/RS, (h+1)*D/RS) of both S and M for
+// column tile ct in fp32 registers.  Per chunk:
+//   phase 1: partial products over its own state rows,
+//              P_h = -Diag(abar) K S_h + Diag(alpha b_prev) K M_h,
+//              R_h =  Diag(abar) Q S_h - Diag(b) Q M_h,
+//            exchanged with the partner wave (one barrier);
+//   phase 2: W = V + P_0 + P_1 and vtilde = T W (both waves, so that no
+//            second exchange is needed), the output rows the wave owns,
+//            O = R_0 + R_1 + Aqk vtilde, and the updates of its own rows
+//            S_h <- abar_C S_h - b_C M_h + K_h^T Diag(gS) vtilde,
+//            M_h <- mubar_C M_h - K_h^T Diag(gM) vtilde,
+//            which need nothing from the partner.
+// With RS = 1 one wave does all of it and nothing is exchanged.
 //
-// Every per-chunk input (K, Q, T, Aqk, the coefficient rows and the V slab)
-// is copied to LDS by direct global->LDS loads, 16 bytes per lane, into one
-// of two buffers: chunk n+1 is in flight while chunk n is computed.  K, Q, T
-// and Aqk rows are XOR-swizzled by 16-byte piece (piece p of row r lives at
-// p ^ (r mod pieces-per-row)) so that the 16 rows an operand read touches
-// fall in different LDS banks.  K^T, the A operand of the state updates, is
-// read from the row-major K tile with the LDS transpose read (bf16).
-// vtilde and O go through an LDS tile so that they leave as full 16-byte
-// stores.  Rows past the end of a ragged last chunk are copied from the last
-// valid row: they only ever meet zero weights (T and Aqk are lower
-// triangular, gS = gM = 0 there) and are never stored.
+// Four loader waves issue every global->LDS copy (K, Q, T, Aqk, the
+// coefficient rows and the V slab of the next chunk, 16 bytes per lane, into
+// one of two buffers) and every output store (O and vtilde through LDS out
+// tiles, 16-byte stores).  K, Q, T and Aqk rows are XOR-swizzled by 16-byte
+// piece so that the 16 rows an operand read touches fall in different LDS
+// banks.  K^T, the A operand of the state updates, is read from the
+// row-major K tile with the LDS transpose read (bf16).  Rows past the end of
+// a ragged last chunk are copies of the last valid row: they only ever meet
+// zero weights (T and Aqk are lower triangular, gS = gM = 0 there) and are
+// never stored.
 // ---------------------------------------------------------------------------
-template <typename Tr, int D, int C, int NCOL, int NBUF>
+template <typename Tr, int D, int C, int NCOL, int RS, int NBUF>
 struct InterLayout {
     using E = typename Tr::elem;
     using frag = typename Tr::frag;
@@ -79,9 +85,10 @@ struct InterLayout {
     static constexpr int CF0 = A0 + C * PT * 16;
     static constexpr int V0 = CF0 + PC * 16;
     static constexpr int BUF = V0 + C * PV * 16;
-    // exchange areas and out tiles
-    static constexpr int KSD = D / Tr::KW;
-    static constexpr int XCH = NCOL * 64 * (KSD * (int)sizeof(frag) + (D / 16) * 16 + (C / 16) * 16);
+    // partial-product exchange (RS = 2): P for every row tile, R for the
+    // partner's output row tiles
+    static constexpr int NCT = C / 16;
+    static constexpr int XCH = RS == 2 ? NCOL * 2 * (NCT + NCT / 2) * 64 * 16 : 0;
     static constexpr int OUT = 2 * C * PV * 16;
     static constexpr int TOTAL = NBUF * BUF + XCH + OUT;
 };
@@ -89,8 +96,11 @@ struct InterLayout {
 template <typename Tr, int D, int C>
 struct InterPick {
     static constexpr int LIMIT = 160 * 1024 - 1024;
-    static constexpr int NCOL = (D >= 32 && InterLayout<Tr, D, C, 2, 1>::TOTAL <= LIMIT) ? 2 : 1;
-    static constexpr int NBUF = InterLayout<Tr, D, C, NCOL, 2>::TOTAL <= LIMIT ? 2 : 1;
+    // a row half must hold whole contraction steps of the state products
+    // and each of the two waves some output row tiles
+    static constexpr int RS = ((std::is_same<Tr, TraitsBf16>::value ? D >= 64 : D >= 32) && C >= 32) ? 2 : 1;
+    static constexpr int NCOL = (D >= 32 && InterLayout<Tr, D, C, 2, RS, 1>::TOTAL <= LIMIT) ? 2 : 1;
+    static constexpr int NBUF = InterLayout<Tr, D, C, NCOL, RS, 2>::TOTAL <= LIMIT ? 2 : 1;
 };
 
 // K^T operand of the state update for d-tile td, contraction step ks.
@@ -122,31 +132,49 @@ template <int P> struct KtOperand<TraitsF32, P> {
     }
 };
 
-// Issue part of the direct global->LDS copies of one chunk into the buffer at
-// LDS byte address `buf`, by one wave: PART 0 K, PART 1 Q, PART 2 T and the coefficients,
-// PART 3 Aqk and the V slab.  Rows past `valid` (ragged last chunk) repeat
-// the last valid row.
-template <typename LT, typename E, int D, int C, int PART>
-__device__ __forceinline__ void stage_chunk(uint32_t buf, const E* __restrict__ k, const E* __restrict__ q,
+// Issue one loader wave's share of the direct global->LDS copies of one
+// chunk into the buffer at LDS byte address `buf`.  HALF 0 (needed first):
+// the K and Q rows, split by rows over the NLD loaders; HALF 1: T, Aqk, the
+// V slab and the coefficient rows.  A single wave sustains only a fraction
+// of a CU's L2 bandwidth, so the copies are spread over all loaders.  Rows
+// past `valid` (ragged last chunk) repeat the last valid row.
+template <typename LT, typename E, int D, int C, int NLD, int HALF>
+__device__ __forceinline__ void stage_chunk(int lw, uint32_t buf, const E* __restrict__ k, const E* __restrict__ q,
                                             const E* __restrict__ v, const E* __restrict__ Tm,
                                             const E* __restrict__ Aqk, const float* __restrict__ coef,
                                             size_t rowbase, int valid, size_t tile, int col0, int lane)
 {
+    static_assert(NLD == 2 || NLD == 4, "two or four loader waves");
     constexpr unsigned RB = D * LT::ES;              // bytes per K/Q/V row
     const unsigned vlast = (unsigned)valid - 1;
     auto seq_row = [&](unsigned r) { return (r < vlast ? r : vlast) * RB; };
     auto t_row = [](unsigned r) { return r * (unsigned)(C * LT::ES); };
-    if constexpr (PART == 0) {
-        dma_tile<C, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rowbase * D), seq_row, lane);
-    } else if constexpr (PART == 1) {
-        dma_tile<C, LT::PK>(buf + LT::Q0, reinterpret_cast<const char*>(q + rowbase * D), seq_row, lane);
-    } else if constexpr (PART == 2) {
-        dma_tile<C, LT::PT>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
-        dma_plain<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
-                             [](unsigned) { return 0u; }, lane);
+    auto cf_row = [](unsigned) { return 0u; };
+    if constexpr (HALF == 0) {
+        constexpr int NH = NLD / 2, RPL = C / NH;    // loaders per matrix, rows per loader
+        const bool isq = lw >= NH;
+        const int part = lw % NH;
+        dma_tile<RPL, LT::PK>(buf + (isq ? LT::Q0 : LT::K0), reinterpret_cast<const char*>((isq ? q : k) + rowbase * D),
+                              seq_row, lane, part * RPL);
+    } else if constexpr (NLD == 2) {
+        if (lw == 0) {
+            dma_tile<C, LT::PT>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
+            dma_plain<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
+                                 cf_row, lane);
+        } else {
+            dma_tile<C, LT::PT>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
+            dma_plain<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), seq_row, lane);
+        }
     } else {
-        dma_tile<C, LT::PT>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
-        dma_plain<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), seq_row, lane);
+        if (lw == 0)
+            dma_tile<C, LT::PT>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
+        else if (lw == 1)
+            dma_tile<C, LT::PT>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
+        else if (lw == 2)
+            dma_plain<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), seq_row, lane);
+        else
+            dma_plain<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
+                                 cf_row, lane);
     }
 }
 
@@ -164,8 +192,8 @@ __device__ __forceinline__ void copy_out(const char* tile, E* __restrict__ dst, 
     }
 }
 
-template <typename Tr, int D, int C, int NCOL, int NBUF>
-__global__ __launch_bounds__(64 * (2 * NCOL + 2))
+template <typename Tr, int D, int C, int NCOL, int RS, int NBUF, int NLD>
+__global__ __launch_bounds__(64 * (NCOL * RS + NLD))
 void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                       const typename Tr::elem* __restrict__ k,
                       const typename Tr::elem* __restrict__ v,
@@ -180,20 +208,23 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 {
     using E = typename Tr::elem;
     using SL = Slots<Tr>;
-    using LT = InterLayout<Tr, D, C, NCOL, NBUF>;
+    using LT = InterLayout<Tr, D, C, NCOL, RS, NBUF>;
     using frag = typename Tr::frag;
     constexpr int NSL = SL::NSLOT;
-    constexpr int NW = 2 * NCOL;                      // compute waves; waves NW, NW+1 load
-    constexpr int NDT = D / 16, NCT = C / 16, KSD = D / Tr::KW, KSC = C / Tr::KW;
+    constexpr int NW = NCOL * RS;                     // compute waves; waves NW .. NW+NLD-1 load
+    constexpr int NCT = C / 16, KSC = C / Tr::KW;
+    constexpr int DH = D / RS;                        // state rows per compute wave
+    constexpr int NDH = DH / 16, KSH = DH / Tr::KW;   // its accumulator tiles / contraction steps
+    constexpr int NOT = NCT / RS;                     // output row tiles per compute wave
     constexpr int SLABS = D / (16 * NCOL);
     constexpr int OW = 16 * NCOL;                     // out-tile row length (elements)
+    static_assert(DH % 16 == 0 && DH % Tr::KW == 0 && NCT % RS == 0, "row split");
     // Distinct LDS objects, so that the compiler can tell the buffer being
     // prefetched from every buffer being read.
     __shared__ __attribute__((aligned(16))) char stA[LT::BUF];
     __shared__ __attribute__((aligned(16))) char stB[NBUF == 2 ? LT::BUF : 16];
-    __shared__ __attribute__((aligned(16))) frag xs[NCOL][KSD][64];      // S operands (S-wave -> M-wave)
-    __shared__ __attribute__((aligned(16))) floatx4 xm[NCOL][NDT][64];   // M accumulators (M -> S)
-    __shared__ __attribute__((aligned(16))) floatx4 xv[NCOL][NCT][64];   // vtilde (S -> M)
+    __shared__ __attribute__((aligned(16))) floatx4 xp[RS == 2 ? NCOL * 2 * NCT * 64 : 1];   // P_h
+    __shared__ __attribute__((aligned(16))) floatx4 xr[RS == 2 ? NCOL * 2 * NOT * 64 : 1];   // R_h
     __shared__ __attribute__((aligned(16))) E ov[C * OW];                // vtilde out tile
     __shared__ __attribute__((aligned(16))) E oo[C * OW];                // O out tile
 
@@ -205,22 +236,24 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     auto valid_of = [&](int64_t n) { return (int)((T - n * C) < C ? (T - n * C) : C); };
 
     if (wave >= NW) {
-        // ---- two loader waves: every global->LDS copy and every output store ----
-        // Loader 0 copies K (before the mid-chunk barrier), then T and the
-        // coefficients, and writes O; loader 1 copies Q, then Aqk and the V
-        // slab, and writes vtilde.
-        const int lw = wave - NW;
+        // ---- loader waves: every global->LDS copy and every output store ----
+        // The K and Q rows of chunk n+1 are issued right after the chunk
+        // barrier, T, Aqk, the V slab and the coefficients after the
+        // mid-chunk barrier.  Loader 0 writes O and loader 1 vtilde: the out
+        // tiles of chunk n are written in phase 2 of chunk n and copied out
+        // between the next chunk's two barriers, before they are written again.
+        const int lw = __builtin_amdgcn_readfirstlane(wave - NW);
         auto issue = [&](uint32_t buf, int64_t m, int half) __attribute__((always_inline)) {
             const size_t tile = (size_t)bh * NT + m;
             const size_t rb = (size_t)bh * T + m * C;
             const int vm = valid_of(m);
-            if (half == 0) {
-                if (lw == 0) stage_chunk<LT, E, D, C, 0>(buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
-                else stage_chunk<LT, E, D, C, 1>(buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
-            } else {
-                if (lw == 0) stage_chunk<LT, E, D, C, 2>(buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
-                else stage_chunk<LT, E, D, C, 3>(buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
-            }
+            if (half == 0) stage_chunk<LT, E, D, C, NLD, 0>(lw, buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
+            else stage_chunk<LT, E, D, C, NLD, 1>(lw, buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
+        };
+        auto copy_prev = [&](int64_t m) __attribute__((always_inline)) {   // out tiles of chunk m
+            const size_t rb = (size_t)bh * T + m * C;
+            if (lw == 0) copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + rb * D, valid_of(m), col0, lane);
+            else if (lw == 1) copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + rb * D, valid_of(m), col0, lane);
         };
         const uint32_t aA = lds_addr(stA), aB = lds_addr(stB);
         if (NBUF == 2 && NT > 0) {
@@ -228,7 +261,6 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             issue(aA, 0, 1);
         }
         auto load = [&](uint32_t cur, uint32_t nxt, int64_t n) __attribute__((always_inline)) {
-            const size_t rowbase = (size_t)bh * T + n * C;
             const bool more = n + 1 < NT;
             if constexpr (NBUF == 2) {
                 __builtin_amdgcn_s_waitcnt(0);          // chunk n has landed (and earlier stores left)
@@ -241,12 +273,9 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 __builtin_amdgcn_s_waitcnt(0);
                 lds_barrier();                          // B0
             }
-            if (lw == 0 && n > 0)                       // O of chunk n-1 (written before B0)
-                copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + (rowbase - C) * D, C, col0, lane);
-            lds_barrier();                              // B1
+            if (n > 0) copy_prev(n - 1);
+            lds_barrier();                              // X
             if (NBUF == 2 && more) issue(nxt, n + 1, 1);
-            if (lw == 1)
-                copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + rowbase * D, valid_of(n), col0, lane);
         };
         if constexpr (NBUF == 2) {
             for (int64_t n = 0; n < NT; n += 2) {
@@ -257,97 +286,118 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             for (int64_t n = 0; n < NT; ++n) load(aA, aA, n);
         }
         lds_barrier();
-        if (lw == 0 && NT > 0)
-            copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + ((size_t)bh * T + (NT - 1) * C) * D,
-                                  valid_of(NT - 1), col0, lane);
+        if (NT > 0) copy_prev(NT - 1);
         return;
     }
 
     // ---- compute waves ----
-    const bool swave = wave < NCOL;                   // S-wave or M-wave
-    const int ct = swave ? wave : wave - NCOL;        // column tile within the slab
+    const int cw = __builtin_amdgcn_readfirstlane(wave);
+    const int ct = cw / RS, h = cw % RS;              // column tile, row half (wave-uniform)
     const int col = col0 + 16 * ct + nn;
+    const int td0 = h * NDH, ks0 = h * KSH;           // first state tile / contraction step owned
 
-    // the wave's own state: S (S-wave) or M (M-wave)
+    // the wave's rows of S and M (fp32 accumulators; tile t holds state rows perm(16 (td0 + t) + 4g + e))
     const size_t sbase = (size_t)bh * D * D;
-    const float* X0 = swave ? S0 : M0;
-    floatx4 X[NDT];
-    if (X0) {
+    floatx4 XS[NDH], XM[NDH];
 #pragma unroll
-        for (int td = 0; td < NDT; ++td)
+    for (int t = 0; t < NDH; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) X[td][e] = X0[sbase + (size_t)SL::perm(16 * td + 4 * g + e) * D + col];
-    } else {
-#pragma unroll
-        for (int td = 0; td < NDT; ++td) X[td] = zero4();
-    }
-    if (swave) {
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) xs[ct][ks][lane] = SL::from_acc(X, ks);
-    } else {
-#pragma unroll
-        for (int td = 0; td < NDT; ++td) xm[ct][td][lane] = X[td];
-    }
+        for (int e = 0; e < 4; ++e) {
+            const size_t off = sbase + (size_t)SL::perm(16 * (td0 + t) + 4 * g + e) * D + col;
+            XS[t][e] = S0 ? S0[off] : 0.f;
+            XM[t][e] = M0 ? M0[off] : 0.f;
+        }
 
-    auto chunk = [&](const char* cur, int64_t n) __attribute__((always_inline)) {
+    auto chunk = [&](const char* cur) __attribute__((always_inline)) {
         if constexpr (NBUF == 1) lds_barrier();         // B0'
-        lds_barrier();                                  // B0: chunk n staged, exchanges visible
+        lds_barrier();                                  // B0: chunk n staged, exchange areas free
 
         const char* Kl = cur + LT::K0;
         const char* Ql = cur + LT::Q0;
-        const char* Tl = cur + LT::T0;
         const float* cf = reinterpret_cast<const float*>(cur + LT::CF0);
-        const E* Vl = reinterpret_cast<const E*>(cur + LT::V0) + 16 * ct + nn;
         // coefficient of accumulator rows perm(16tc + 4g) + e, e = 0..3 (contiguous)
         auto crow = [&](int which, int tc) __attribute__((always_inline)) {
             return *reinterpret_cast<const floatx4*>(cf + which * C + SL::perm(16 * tc + 4 * g));
         };
 
-        frag Sb[KSD], Mb[KSD];
-        floatx4 Vx[NCT];      // S-wave: vtilde
-        floatx4 Op[NCT];      // M-wave: Diag(abar) Q S - Diag(b) Q M
-        if (swave) {
-            floatx4 Mf[NDT];
+        // -- phase 1: partial products over the wave's state rows --
+        floatx4 P[NCT], R[NCT];
+        {
+            frag Sb[KSH], Mb[KSH];
 #pragma unroll
-            for (int td = 0; td < NDT; ++td) Mf[td] = xm[ct][td][lane];
+            for (int ks = 0; ks < KSH; ++ks) { Sb[ks] = SL::from_acc(XS, ks); Mb[ks] = SL::from_acc(XM, ks); }
+            floatx4 KSa[NCT], KMa[NCT], QSa[NCT], QMa[NCT];
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) { Sb[ks] = SL::from_acc(X, ks); Mb[ks] = SL::from_acc(Mf, ks); }
-            {   // first half of the S update: abar_C S - b_C M (the chunk-start M is no longer needed)
-                const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
-                const float bC = cf[MDN_COEF_B * C + C - 1];
+            for (int tc = 0; tc < NCT; ++tc) { KSa[tc] = zero4(); KMa[tc] = zero4(); QSa[tc] = zero4(); QMa[tc] = zero4(); }
 #pragma unroll
-                for (int td = 0; td < NDT; ++td)
+            for (int ks = 0; ks < KSH; ++ks) {
+                frag a[NCT], b[NCT];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) X[td][e] = abarC * X[td][e] - bC * Mf[td][e];
-            }
-            // W = V - Diag(abar) K S + Diag(alpha b_prev) K M
-            floatx4 W[NCT], KSa[NCT], KMa[NCT];
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) { KSa[tc] = zero4(); KMa[tc] = zero4(); }
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                frag a[NCT];
-#pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) a[tc] = LdsA<Tr, LT::PK>::load(Kl, SL::perm(16 * tc + nn), ks, g);
+                for (int tc = 0; tc < NCT; ++tc) {
+                    a[tc] = LdsA<Tr, LT::PK>::load(Kl, SL::perm(16 * tc + nn), ks0 + ks, g);
+                    b[tc] = LdsA<Tr, LT::PK>::load(Ql, SL::perm(16 * tc + nn), ks0 + ks, g);
+                }
 #pragma unroll
                 for (int tc = 0; tc < NCT; ++tc) {
                     KSa[tc] = Tr::mma(a[tc], Sb[ks], KSa[tc]);
                     KMa[tc] = Tr::mma(a[tc], Mb[ks], KMa[tc]);
+                    QSa[tc] = Tr::mma(b[tc], Sb[ks], QSa[tc]);
+                    QMa[tc] = Tr::mma(b[tc], Mb[ks], QMa[tc]);
                 }
             }
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc) {
-                const floatx4 ca = crow(MDN_COEF_ABAR, tc), cb = crow(MDN_COEF_ABP, tc);
+                const floatx4 ca = crow(MDN_COEF_ABAR, tc), cp = crow(MDN_COEF_ABP, tc), cb = crow(MDN_COEF_B, tc);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float vv = Tr::to_f(Vl[(SL::perm(16 * tc + 4 * g) + e) * OW]);
-                    W[tc][e] = vv - ca[e] * KSa[tc][e] + cb[e] * KMa[tc][e];
+                    P[tc][e] = cp[e] * KMa[tc][e] - ca[e] * KSa[tc][e];
+                    R[tc][e] = ca[e] * QSa[tc][e] - cb[e] * QMa[tc][e];
                 }
             }
-            // vtilde = T W
-            frag Wb[KSC];
+        }
+        if constexpr (RS == 2) {
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) Wb[ks] = SL::from_acc(W, ks);
+            for (int tc = 0; tc < NCT; ++tc) xp[((ct * 2 + h) * NCT + tc) * 64 + lane] = P[tc];
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc)            // the partner's output row tiles
+                if (tc / NOT != h) xr[((ct * 2 + h) * NOT + tc % NOT) * 64 + lane] = R[tc];
+        }
+        // first half of the state updates, while the chunk-start M is at hand
+        {
+            const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
+            const float bC = cf[MDN_COEF_B * C + C - 1];
+            const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
+#pragma unroll
+            for (int t = 0; t < NDH; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    XS[t][e] = abarC * XS[t][e] - bC * XM[t][e];
+                    XM[t][e] = mubarC * XM[t][e];
+                }
+        }
+        lds_barrier();                                  // X: partial products visible
+
+        // -- phase 2 --
+        if constexpr (RS == 2) {
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc) {
+                const floatx4 o = xp[((ct * 2 + 1 - h) * NCT + tc) * 64 + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) P[tc][e] += o[e];
+            }
+        }
+        // W = V + P_0 + P_1;  vtilde = T W
+        const E* Vl = reinterpret_cast<const E*>(cur + LT::V0) + 16 * ct + nn;
+#pragma unroll
+        for (int tc = 0; tc < NCT; ++tc)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) P[tc][e] += Tr::to_f(Vl[(SL::perm(16 * tc + 4 * g) + e) * OW]);
+        frag Wb[KSC];
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) Wb[ks] = SL::from_acc(P, ks);
+        floatx4 Vx[NCT];
+        {
+            const char* Tl = cur + LT::T0;
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc) Vx[tc] = zero4();
 #pragma unroll
@@ -358,121 +408,79 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
                 for (int tc = 0; tc < NCT; ++tc) Vx[tc] = Tr::mma(a[tc], Wb[ks], Vx[tc]);
             }
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) {
-                xv[ct][tc][lane] = Vx[tc];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ov[(SL::perm(16 * tc + 4 * g) + e) * OW + 16 * ct + nn] = Tr::from_f(Vx[tc][e]);
-            }
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) { Sb[ks] = xs[ct][ks][lane]; Mb[ks] = SL::from_acc(X, ks); }
-            floatx4 QSa[NCT], QMa[NCT];
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) { QSa[tc] = zero4(); QMa[tc] = zero4(); }
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                frag a[NCT];
-#pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) a[tc] = LdsA<Tr, LT::PK>::load(Ql, SL::perm(16 * tc + nn), ks, g);
-#pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) {
-                    QSa[tc] = Tr::mma(a[tc], Sb[ks], QSa[tc]);
-                    QMa[tc] = Tr::mma(a[tc], Mb[ks], QMa[tc]);
-                }
-            }
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) {
-                const floatx4 ca = crow(MDN_COEF_ABAR, tc), cb = crow(MDN_COEF_B, tc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Op[tc][e] = ca[e] * QSa[tc][e] - cb[e] * QMa[tc][e];
-            }
         }
-        lds_barrier();                                  // B1: vtilde and the states of chunk n visible
-
-        if (swave) {
-            // S <- (abar_C S - b_C M) + K^T Diag(gS) vtilde
-            frag VS[KSC];
+        frag Vb[KSC];
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                float sc[NSL];
-#pragma unroll
-                for (int j = 0; j < NSL; ++j) sc[j] = cf[MDN_COEF_GS * C + SL::row(ks, g, j)];
-                VS[ks] = SL::from_acc_scaled(Vx, ks, sc);
-            }
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                frag a[NDT];
-#pragma unroll
-                for (int td = 0; td < NDT; ++td) a[td] = KtOperand<Tr, LT::PK>::load(Kl, td, ks, lane);
-#pragma unroll
-                for (int td = 0; td < NDT; ++td) X[td] = Tr::mma(a[td], VS[ks], X[td]);
-            }
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) xs[ct][ks][lane] = SL::from_acc(X, ks);
-        } else {
-            floatx4 Vv[NCT];
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) Vv[tc] = xv[ct][tc][lane];
-            frag VM[KSC], Vb[KSC];
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                float sc[NSL];
-#pragma unroll
-                for (int j = 0; j < NSL; ++j) sc[j] = -cf[MDN_COEF_GM * C + SL::row(ks, g, j)];
-                VM[ks] = SL::from_acc_scaled(Vv, ks, sc);
-                Vb[ks] = SL::from_acc(Vv, ks);
-            }
-            // M <- mubar_C M - K^T Diag(gM) vtilde
-            const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
-#pragma unroll
-            for (int td = 0; td < NDT; ++td)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) X[td][e] = mubarC * X[td][e];
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                frag a[NDT];
-#pragma unroll
-                for (int td = 0; td < NDT; ++td) a[td] = KtOperand<Tr, LT::PK>::load(Kl, td, ks, lane);
-#pragma unroll
-                for (int td = 0; td < NDT; ++td) X[td] = Tr::mma(a[td], VM[ks], X[td]);
-            }
-#pragma unroll
-            for (int td = 0; td < NDT; ++td) xm[ct][td][lane] = X[td];
-            // O = Op + Aqk vtilde
+        for (int ks = 0; ks < KSC; ++ks) Vb[ks] = SL::from_acc(Vx, ks);
+        // output rows of this wave: O = R_0 + R_1 + Aqk vtilde; and its vtilde rows
+        {
             const char* Al = cur + LT::A0;
 #pragma unroll
+            for (int tc = 0; tc < NCT; ++tc) {
+                if (tc / NOT != h) continue;            // uniform: another wave's rows
+                floatx4 o = R[tc];
+                if constexpr (RS == 2) {
+                    const floatx4 r = xr[((ct * 2 + 1 - h) * NOT + tc % NOT) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] += r[e];
+                }
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks)
+                    o = Tr::mma(LdsA<Tr, LT::PT>::load(Al, SL::perm(16 * tc + nn), ks, g), Vb[ks], o);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = SL::perm(16 * tc + 4 * g) + e;
+                    oo[row * OW + 16 * ct + nn] = Tr::from_f(o[e]);
+                    ov[row * OW + 16 * ct + nn] = Tr::from_f(Vx[tc][e]);
+                }
+            }
+        }
+        // S_h += K_h^T Diag(gS) vtilde;  M_h -= K_h^T Diag(gM) vtilde
+        {
+            frag VS[KSC], VM[KSC];
+#pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
-                frag a[NCT];
+                float ss[NSL], sm[NSL];
 #pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) a[tc] = LdsA<Tr, LT::PT>::load(Al, SL::perm(16 * tc + nn), ks, g);
-#pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) Op[tc] = Tr::mma(a[tc], Vb[ks], Op[tc]);
+                for (int j = 0; j < NSL; ++j) {
+                    ss[j] = cf[MDN_COEF_GS * C + SL::row(ks, g, j)];
+                    sm[j] = -cf[MDN_COEF_GM * C + SL::row(ks, g, j)];
+                }
+                VS[ks] = SL::from_acc_scaled(Vx, ks, ss);
+                VM[ks] = SL::from_acc_scaled(Vx, ks, sm);
             }
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc)
+            for (int ks = 0; ks < KSC; ++ks) {
+                frag a[NDH];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    oo[(SL::perm(16 * tc + 4 * g) + e) * OW + 16 * ct + nn] = Tr::from_f(Op[tc][e]);
+                for (int t = 0; t < NDH; ++t) a[t] = KtOperand<Tr, LT::PK>::load(Kl, td0 + t, ks, lane);
+#pragma unroll
+                for (int t = 0; t < NDH; ++t) {
+                    XS[t] = Tr::mma(a[t], VS[ks], XS[t]);
+                    XM[t] = Tr::mma(a[t], VM[ks], XM[t]);
+                }
+            }
         }
     };
 
     if constexpr (NBUF == 2) {
         for (int64_t n = 0; n < NT; n += 2) {
-            chunk(stA, n);
-            if (n + 1 < NT) chunk(stB, n + 1);
+            chunk(stA);
+            if (n + 1 < NT) chunk(stB);
         }
     } else {
-        for (int64_t n = 0; n < NT; ++n) chunk(stA, n);
+        for (int64_t n = 0; n < NT; ++n) chunk(stA);
     }
     lds_barrier();
 
-    float* Xo = swave ? ST : MT;
 #pragma unroll
-    for (int td = 0; td < NDT; ++td)
+    for (int t = 0; t < NDH; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Xo[sbase + (size_t)SL::perm(16 * td + 4 * g + e) * D + col] = X[td][e];
+        for (int e = 0; e < 4; ++e) {
+            const size_t off = sbase + (size_t)SL::perm(16 * (td0 + t) + 4 * g + e) * D + col;
+            ST[off] = XS[t][e];
+            MT[off] = XM[t][e];
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -483,10 +491,10 @@ static hipError_t launch_inter_nw(const ChunkArgs& a)
 {
     using E = typename Tr::elem;
     using P = InterPick<Tr, D, C>;
-    constexpr int NCOL = P::NCOL, NBUF = P::NBUF;
+    constexpr int NCOL = P::NCOL, RS = P::RS, NBUF = P::NBUF, NLD = 4;
     const int64_t grid = a.BH * (D / (16 * NCOL));
-    hipLaunchKernelGGL((mdn_inter_kernel<Tr, D, C, NCOL, NBUF>), dim3((unsigned)grid), dim3(64 * (2 * NCOL + 2)), 0,
-                       (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v,
+    hipLaunchKernelGGL((mdn_inter_kernel<Tr, D, C, NCOL, RS, NBUF, NLD>), dim3((unsigned)grid), dim3(64 * (NCOL * RS + NLD)),
+                       0, (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v,
                        (const E*)a.Tmat, (const E*)a.Aqk, a.coef, a.S0, a.M0,
                        (E*)a.O, a.ST, a.MT, (E*)a.Vt, a.T, a.NT, (int)a.BH);
     return hipGetLastError();
