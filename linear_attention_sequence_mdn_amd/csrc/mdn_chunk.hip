@@ -85,10 +85,11 @@ struct InterLayout {
     static constexpr int CF0 = A0 + C * PT * 16;
     static constexpr int V0 = CF0 + PC * 16;
     static constexpr int BUF = V0 + C * PV * 16;
-    // partial-product exchange (RS = 2): P for every row tile, R for the
-    // partner's output row tiles
+    // partial-product exchange (RS > 1): P for every row tile, R for the
+    // other waves' output row tiles; 4 fp32 values per lane and tile
     static constexpr int NCT = C / 16;
-    static constexpr int XCH = RS == 2 ? NCOL * 2 * (NCT + NCT / 2) * 64 * 16 : 0;
+    static constexpr int XB = 16;                     // bytes per lane and tile
+    static constexpr int XCH = RS > 1 ? NCOL * RS * (NCT + NCT - NCT / RS) * 64 * XB : 0;
     static constexpr int OUT = 2 * C * PV * 16;
     static constexpr int TOTAL = NBUF * BUF + XCH + OUT;
 };
@@ -96,9 +97,12 @@ struct InterLayout {
 template <typename Tr, int D, int C>
 struct InterPick {
     static constexpr int LIMIT = 160 * 1024 - 1024;
-    // a row half must hold whole contraction steps of the state products
-    // and each of the two waves some output row tiles
-    static constexpr int RS = ((std::is_same<Tr, TraitsBf16>::value ? D >= 64 : D >= 32) && C >= 32) ? 2 : 1;
+    // A row half must hold whole contraction steps of the state products and
+    // each of the two waves some output row tiles.  (Four parts, two compute
+    // waves per SIMD, measured slower: the barrier-synchronised waves sit in
+    // the same latency-bound phase at the same time.)
+    static constexpr bool BF = std::is_same<Tr, TraitsBf16>::value;
+    static constexpr int RS = ((BF ? D >= 64 : D >= 32) && C >= 32) ? 2 : 1;
     static constexpr int NCOL = (D >= 32 && InterLayout<Tr, D, C, 2, RS, 1>::TOTAL <= LIMIT) ? 2 : 1;
     static constexpr int NBUF = InterLayout<Tr, D, C, NCOL, RS, 2>::TOTAL <= LIMIT ? 2 : 1;
 };
@@ -223,8 +227,9 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     // prefetched from every buffer being read.
     __shared__ __attribute__((aligned(16))) char stA[LT::BUF];
     __shared__ __attribute__((aligned(16))) char stB[NBUF == 2 ? LT::BUF : 16];
-    __shared__ __attribute__((aligned(16))) floatx4 xp[RS == 2 ? NCOL * 2 * NCT * 64 : 1];   // P_h
-    __shared__ __attribute__((aligned(16))) floatx4 xr[RS == 2 ? NCOL * 2 * NOT * 64 : 1];   // R_h
+    constexpr int NOS = NCT - NOT;                    // other waves' output row tiles
+    __shared__ __attribute__((aligned(16))) floatx4 xp[RS > 1 ? NCOL * RS * NCT * 64 : 1];   // P_h
+    __shared__ __attribute__((aligned(16))) floatx4 xr[RS > 1 ? NCOL * RS * NOS * 64 : 1];   // R_h
     __shared__ __attribute__((aligned(16))) E ov[C * OW];                // vtilde out tile
     __shared__ __attribute__((aligned(16))) E oo[C * OW];                // O out tile
 
@@ -291,8 +296,13 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     }
 
     // ---- compute waves ----
+    // The row half is a template constant of the wave's code, so that the
+    // code of a chunk is straight-line (uniform branches on it would split
+    // the chunk into small blocks, each waiting for its own LDS reads).
     const int cw = __builtin_amdgcn_readfirstlane(wave);
-    const int ct = cw / RS, h = cw % RS;              // column tile, row half (wave-uniform)
+    const int ct = cw / RS;                           // column tile
+    auto compute = [&](auto hc) __attribute__((always_inline)) {
+    constexpr int h = decltype(hc)::value;            // row half
     const int col = col0 + 16 * ct + nn;
     const int td0 = h * NDH, ks0 = h * KSH;           // first state tile / contraction step owned
 
@@ -345,6 +355,19 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                     QMa[tc] = Tr::mma(b[tc], Mb[ks], QMa[tc]);
                 }
             }
+            // first half of the state updates, while the chunk-start M is at hand
+            {
+                const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
+                const float bC = cf[MDN_COEF_B * C + C - 1];
+                const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
+#pragma unroll
+                for (int t = 0; t < NDH; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        XS[t][e] = abarC * XS[t][e] - bC * XM[t][e];
+                        XM[t][e] = mubarC * XM[t][e];
+                    }
+            }
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc) {
                 const floatx4 ca = crow(MDN_COEF_ABAR, tc), cp = crow(MDN_COEF_ABP, tc), cb = crow(MDN_COEF_B, tc);
@@ -355,110 +378,107 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 }
             }
         }
-        if constexpr (RS == 2) {
+        if constexpr (RS > 1) {
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) xp[((ct * 2 + h) * NCT + tc) * 64 + lane] = P[tc];
+            for (int tc = 0; tc < NCT; ++tc) xp[((ct * RS + h) * NCT + tc) * 64 + lane] = P[tc];
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc)            // the partner's output row tiles
-                if (tc / NOT != h) xr[((ct * 2 + h) * NOT + tc % NOT) * 64 + lane] = R[tc];
-        }
-        // first half of the state updates, while the chunk-start M is at hand
-        {
-            const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
-            const float bC = cf[MDN_COEF_B * C + C - 1];
-            const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
-#pragma unroll
-            for (int t = 0; t < NDH; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    XS[t][e] = abarC * XS[t][e] - bC * XM[t][e];
-                    XM[t][e] = mubarC * XM[t][e];
-                }
+            for (int tc = 0; tc < NCT; ++tc)            // the other waves' output row tiles
+                if (tc / NOT != h)
+                    xr[((ct * RS + h) * NOS + (tc < h * NOT ? tc : tc - NOT)) * 64 + lane] = R[tc];
         }
         lds_barrier();                                  // X: partial products visible
 
-        // -- phase 2 --
-        if constexpr (RS == 2) {
+        // -- phase 2: every LDS read of the phase is issued first --
+        const char* Tl = cur + LT::T0;
+        const char* Al = cur + LT::A0;
+        frag tA[KSC][NCT];                              // T operands
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) {
-                const floatx4 o = xp[((ct * 2 + 1 - h) * NCT + tc) * 64 + lane];
+        for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) P[tc][e] += o[e];
+            for (int tc = 0; tc < NCT; ++tc) tA[ks][tc] = LdsA<Tr, LT::PT>::load(Tl, SL::perm(16 * tc + nn), ks, g);
+        {                                               // W = V + P_0 + P_1 (V slab values of the accumulator rows)
+            const E* Vl = reinterpret_cast<const E*>(cur + LT::V0) + 16 * ct + nn;
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) P[tc][e] += Tr::to_f(Vl[(SL::perm(16 * tc + 4 * g) + e) * OW]);
+        }
+        if constexpr (RS > 1) {
+#pragma unroll
+            for (int h2 = 0; h2 < RS; ++h2) {
+                if (h2 == h) continue;                  // uniform
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) {
+                    const floatx4 o = xp[((ct * RS + h2) * NCT + tc) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) P[tc][e] += o[e];
+                }
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) {
+                    if (tc / NOT != h) continue;        // uniform
+                    const floatx4 r = xr[((ct * RS + h2) * NOS + (tc < h2 * NOT ? tc : tc - NOT)) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) R[tc][e] += r[e];
+                }
             }
         }
-        // W = V + P_0 + P_1;  vtilde = T W
-        const E* Vl = reinterpret_cast<const E*>(cur + LT::V0) + 16 * ct + nn;
-#pragma unroll
-        for (int tc = 0; tc < NCT; ++tc)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) P[tc][e] += Tr::to_f(Vl[(SL::perm(16 * tc + 4 * g) + e) * OW]);
-        frag Wb[KSC];
-#pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) Wb[ks] = SL::from_acc(P, ks);
+        // vtilde = T W
         floatx4 Vx[NCT];
         {
-            const char* Tl = cur + LT::T0;
+            frag Wb[KSC];
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) Wb[ks] = SL::from_acc(P, ks);
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc) Vx[tc] = zero4();
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                frag a[NCT];
+            for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) a[tc] = LdsA<Tr, LT::PT>::load(Tl, SL::perm(16 * tc + nn), ks, g);
-#pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) Vx[tc] = Tr::mma(a[tc], Wb[ks], Vx[tc]);
-            }
+                for (int tc = 0; tc < NCT; ++tc) Vx[tc] = Tr::mma(tA[ks][tc], Wb[ks], Vx[tc]);
         }
-        frag Vb[KSC];
+        // read while T W runs: gS, gM of the contraction slots, K^T operands of the wave's rows
+        float gs[KSC][NSL], gm[KSC][NSL];
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) Vb[ks] = SL::from_acc(Vx, ks);
-        // output rows of this wave: O = R_0 + R_1 + Aqk vtilde; and its vtilde rows
-        {
-            const char* Al = cur + LT::A0;
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) {
-                if (tc / NOT != h) continue;            // uniform: another wave's rows
-                floatx4 o = R[tc];
-                if constexpr (RS == 2) {
-                    const floatx4 r = xr[((ct * 2 + 1 - h) * NOT + tc % NOT) * 64 + lane];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] += r[e];
-                }
-#pragma unroll
-                for (int ks = 0; ks < KSC; ++ks)
-                    o = Tr::mma(LdsA<Tr, LT::PT>::load(Al, SL::perm(16 * tc + nn), ks, g), Vb[ks], o);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = SL::perm(16 * tc + 4 * g) + e;
-                    oo[row * OW + 16 * ct + nn] = Tr::from_f(o[e]);
-                    ov[row * OW + 16 * ct + nn] = Tr::from_f(Vx[tc][e]);
-                }
-            }
+        for (int ks = 0; ks < KSC; ++ks) {
+            SL::load_row(cf + MDN_COEF_GS * C, ks, g, gs[ks]);
+            SL::load_row(cf + MDN_COEF_GM * C, ks, g, gm[ks]);
         }
+        frag kT[KSC][NDH];
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+            for (int t = 0; t < NDH; ++t) kT[ks][t] = KtOperand<Tr, LT::PK>::load(Kl, td0 + t, ks, lane);
         // S_h += K_h^T Diag(gS) vtilde;  M_h -= K_h^T Diag(gM) vtilde
+        frag Vb[KSC];
         {
             frag VS[KSC], VM[KSC];
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
-                float ss[NSL], sm[NSL];
 #pragma unroll
-                for (int j = 0; j < NSL; ++j) {
-                    ss[j] = cf[MDN_COEF_GS * C + SL::row(ks, g, j)];
-                    sm[j] = -cf[MDN_COEF_GM * C + SL::row(ks, g, j)];
-                }
-                VS[ks] = SL::from_acc_scaled(Vx, ks, ss);
-                VM[ks] = SL::from_acc_scaled(Vx, ks, sm);
+                for (int j = 0; j < NSL; ++j) gm[ks][j] = -gm[ks][j];
+                VS[ks] = SL::from_acc_scaled(Vx, ks, gs[ks]);
+                VM[ks] = SL::from_acc_scaled(Vx, ks, gm[ks]);
+                Vb[ks] = SL::from_acc(Vx, ks);
             }
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                frag a[NDH];
-#pragma unroll
-                for (int t = 0; t < NDH; ++t) a[t] = KtOperand<Tr, LT::PK>::load(Kl, td0 + t, ks, lane);
+            for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
                 for (int t = 0; t < NDH; ++t) {
-                    XS[t] = Tr::mma(a[t], VS[ks], XS[t]);
-                    XM[t] = Tr::mma(a[t], VM[ks], XM[t]);
+                    XS[t] = Tr::mma(kT[ks][t], VS[ks], XS[t]);
+                    XM[t] = Tr::mma(kT[ks][t], VM[ks], XM[t]);
                 }
+        }
+        // output rows of this wave: O = R_0 + R_1 + Aqk vtilde, and its vtilde rows
+#pragma unroll
+        for (int tc = 0; tc < NCT; ++tc) {
+            if (tc / NOT != h) continue;                // uniform: another wave's rows
+            floatx4 o = R[tc];
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) o = Tr::mma(LdsA<Tr, LT::PT>::load(Al, SL::perm(16 * tc + nn), ks, g), Vb[ks], o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = SL::perm(16 * tc + 4 * g) + e;
+                oo[row * OW + 16 * ct + nn] = Tr::from_f(o[e]);
+                ov[row * OW + 16 * ct + nn] = Tr::from_f(Vx[tc][e]);
             }
         }
     };
@@ -481,6 +501,13 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             ST[off] = XS[t][e];
             MT[off] = XM[t][e];
         }
+    };
+    if constexpr (RS == 1) {
+        compute(std::integral_constant<int, 0>{});
+    } else {
+        if (cw % RS == 0) compute(std::integral_constant<int, 0>{});
+        else compute(std::integral_constant<int, 1>{});
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -101,6 +101,14 @@ template <> struct Slots<TraitsBf16> {
         f.u = uint4{0u, 0u, 0u, 0u};
         return f.v;
     }
+    // the per-slot factors p[row(ks, g, j)], j = 0..7, of a row vector p
+    // (16-byte aligned): two 16-byte reads
+    static __device__ __forceinline__ void load_row(const float* p, int ks, int g, float (&out)[NSLOT]) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(p + 32 * ks + 8 * g);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(p + 32 * ks + 8 * g + 4);
+        out[0] = a[0]; out[1] = a[1]; out[2] = a[2]; out[3] = a[3];
+        out[4] = b[0]; out[5] = b[1]; out[6] = b[2]; out[7] = b[3];
+    }
 };
 
 template <> struct Slots<TraitsF32> {
@@ -117,6 +125,9 @@ template <> struct Slots<TraitsF32> {
         return acc[ks >> 2][ks & 3] * s[0];
     }
     static __device__ __forceinline__ float zero() { return 0.f; }
+    static __device__ __forceinline__ void load_row(const float* p, int ks, int g, float (&out)[NSLOT]) {
+        out[0] = p[row(ks, g, 0)];
+    }
 };
 
 // Operand with contiguous contraction index, natural order (both operands
