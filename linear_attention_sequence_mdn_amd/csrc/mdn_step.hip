@@ -20,16 +20,21 @@
 
 namespace mdn {
 
-template <typename Tr, int DK, int DV>
+#ifndef MDN_STEP_SPLIT
+#define MDN_STEP_SPLIT 2
+#endif
+
+template <typename Tr, int DK, int DV, int NSPLIT>
 struct StepCfg {
-    static constexpr int CG = DV / 4;                       // float4 column groups
+    static constexpr int DVW = DV / NSPLIT;                 // columns per workgroup
+    static constexpr int CG = DVW / 4;                      // float4 column groups
     static constexpr int RG = (256 / CG) < DK ? (256 / CG) : DK;  // row groups
     static constexpr int RPT = DK / RG;                     // rows per thread
     static constexpr int NTHR = CG * RG;
     static_assert(DK % RG == 0, "row groups must tile dk");
 };
 
-template <typename Tr, int DK, int DV>
+template <typename Tr, int DK, int DV, int NSPLIT>
 __global__ __launch_bounds__(256)
 void mdn_step_kernel(const typename Tr::elem* __restrict__ q,
                      const typename Tr::elem* __restrict__ k,
@@ -39,28 +44,32 @@ void mdn_step_kernel(const typename Tr::elem* __restrict__ q,
                      float* __restrict__ S, float* __restrict__ M,
                      typename Tr::elem* __restrict__ o)
 {
-    using Cfg = StepCfg<Tr, DK, DV>;
+    using Cfg = StepCfg<Tr, DK, DV, NSPLIT>;
     constexpr int CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT;
     __shared__ float4 red[RG][CG];
 
-    const int bh = blockIdx.x;
+    // workgroup = (head, block of DV / NSPLIT columns); columns are independent
+    const int bh = blockIdx.x / NSPLIT;
+    const int cb = (blockIdx.x % NSPLIT) * Cfg::DVW;
     const int t = threadIdx.x;
     const int cg = t % CG, rg = t / CG;
 
-    float* Sh = S + (size_t)bh * DK * DV;
-    float* Mh = M + (size_t)bh * DK * DV;
+    float* Sh = S + (size_t)bh * DK * DV + cb;
+    float* Mh = M + (size_t)bh * DK * DV + cb;
 
     // Issue the state loads first: they are the whole cost of the step.
-    float4 s[RPT], m[RPT];
+    // The state streams through once per step and is far larger than the
+    // caches, so loads and stores are non-temporal.
+    floatx4 s[RPT], m[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + RG * i;
-        s[i] = *reinterpret_cast<const float4*>(Sh + (size_t)row * DV + 4 * cg);
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sh + (size_t)row * DV + 4 * cg));
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + RG * i;
-        m[i] = *reinterpret_cast<const float4*>(Mh + (size_t)row * DV + 4 * cg);
+        m[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Mh + (size_t)row * DV + 4 * cg));
     }
     const float a = alpha[bh], mm = mu[bh], b = beta[bh], e = eta[bh];
     float kk[RPT], qq[RPT];
@@ -72,14 +81,14 @@ void mdn_step_kernel(const typename Tr::elem* __restrict__ q,
     }
     float vv[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vv[c] = Tr::to_f(v[(size_t)bh * DV + 4 * cg + c]);
+    for (int c = 0; c < 4; ++c) vv[c] = Tr::to_f(v[(size_t)bh * DV + cb + 4 * cg + c]);
 
     // u = S^T k over this thread's rows, then across row groups.
     float4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        u.x += s[i].x * kk[i]; u.y += s[i].y * kk[i];
-        u.z += s[i].z * kk[i]; u.w += s[i].w * kk[i];
+        u.x += s[i][0] * kk[i]; u.y += s[i][1] * kk[i];
+        u.z += s[i][2] * kk[i]; u.w += s[i][3] * kk[i];
     }
     red[rg][cg] = u;
     __syncthreads();
@@ -97,15 +106,15 @@ void mdn_step_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const float ek = e * kk[i];
-        float4 mn, sn;
-        mn.x = mm * m[i].x - ek * vt0; mn.y = mm * m[i].y - ek * vt1;
-        mn.z = mm * m[i].z - ek * vt2; mn.w = mm * m[i].w - ek * vt3;
-        sn.x = a * s[i].x - b * mn.x; sn.y = a * s[i].y - b * mn.y;
-        sn.z = a * s[i].z - b * mn.z; sn.w = a * s[i].w - b * mn.w;
+        floatx4 mn, sn;
+        mn[0] = mm * m[i][0] - ek * vt0; mn[1] = mm * m[i][1] - ek * vt1;
+        mn[2] = mm * m[i][2] - ek * vt2; mn[3] = mm * m[i][3] - ek * vt3;
+        sn[0] = a * s[i][0] - b * mn[0]; sn[1] = a * s[i][1] - b * mn[1];
+        sn[2] = a * s[i][2] - b * mn[2]; sn[3] = a * s[i][3] - b * mn[3];
         const int row = rg + RG * i;
-        *reinterpret_cast<float4*>(Mh + (size_t)row * DV + 4 * cg) = mn;
-        *reinterpret_cast<float4*>(Sh + (size_t)row * DV + 4 * cg) = sn;
-        w.x += sn.x * qq[i]; w.y += sn.y * qq[i]; w.z += sn.z * qq[i]; w.w += sn.w * qq[i];
+        __builtin_nontemporal_store(mn, reinterpret_cast<floatx4*>(Mh + (size_t)row * DV + 4 * cg));
+        __builtin_nontemporal_store(sn, reinterpret_cast<floatx4*>(Sh + (size_t)row * DV + 4 * cg));
+        w.x += sn[0] * qq[i]; w.y += sn[1] * qq[i]; w.z += sn[2] * qq[i]; w.w += sn[3] * qq[i];
     }
     __syncthreads();          // every thread has read red[] for u
     red[rg][cg] = w;
@@ -117,7 +126,7 @@ void mdn_step_kernel(const typename Tr::elem* __restrict__ q,
             const float4 p = red[r][cg];
             ot.x += p.x; ot.y += p.y; ot.z += p.z; ot.w += p.w;
         }
-        typename Tr::elem* op = o + (size_t)bh * DV + 4 * cg;
+        typename Tr::elem* op = o + (size_t)bh * DV + cb + 4 * cg;
         op[0] = Tr::from_f(ot.x); op[1] = Tr::from_f(ot.y);
         op[2] = Tr::from_f(ot.z); op[3] = Tr::from_f(ot.w);
     }
@@ -126,9 +135,10 @@ void mdn_step_kernel(const typename Tr::elem* __restrict__ q,
 template <typename Tr, int DK, int DV>
 static hipError_t launch_step_t(const StepArgs& a)
 {
-    using Cfg = StepCfg<Tr, DK, DV>;
+    constexpr int NSPLIT = DV >= 64 ? MDN_STEP_SPLIT : 1;
+    using Cfg = StepCfg<Tr, DK, DV, NSPLIT>;
     using E = typename Tr::elem;
-    hipLaunchKernelGGL((mdn_step_kernel<Tr, DK, DV>), dim3((unsigned)a.BH), dim3(Cfg::NTHR), 0,
+    hipLaunchKernelGGL((mdn_step_kernel<Tr, DK, DV, NSPLIT>), dim3((unsigned)(a.BH * NSPLIT)), dim3(Cfg::NTHR), 0,
                        (hipStream_t)a.stream,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v,
                        a.alpha, a.mu, a.beta, a.eta, a.S, a.M, (E*)a.o);
