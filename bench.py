@@ -56,6 +56,10 @@ def parse():
     p.add_argument("--calibration-copy", action="store_true",
                    help="run one 1 GiB device copy first (HBM counter calibration)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="threads of the CPU-baseline oracle (0 = all the host's OpenMP threads)")
+    p.add_argument("--workload", type=int, default=1, choices=(1, 2, 4),
+                   help="chunk workload: 1 = 400M layer (the headline line), 2 = 1.3B layer, 4 = long context")
     return p.parse_args()
 
 
@@ -82,15 +86,24 @@ def load_traffic(summary, sha):
     return d.get("traffic_bytes_per_launch")
 
 
+WORKLOAD_NAMES = {
+    1: "400M-layer chunk forward B8 H8 T4096 dk=dv=128 C64 bf16, zero initial state",
+    2: "1.3B-layer chunk forward B4 H16 T4096 dk=dv=128 C64 bf16, S0/M0 ~ N(0, 0.02^2)",
+    4: "long-context chunk forward B1 H16 T16384 dk=dv=128 C64 bf16, log mu ~ U[-2,-1.5]",
+}
+
+
 def chunk_bench(args, torch, mdn, inputs):
-    cfg = inputs.CONFIGS[1]
-    x = inputs.config_inputs(1)
+    cfg = inputs.CONFIGS[args.workload]
+    x = inputs.config_inputs(args.workload)
     B, H, T, d, C = x.B, x.H, x.T, x.dk, x.C
     to = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
                               if bf else torch.from_numpy(np.ascontiguousarray(a)).cuda())
     q, k, v = to(x.q, True), to(x.k, True), to(x.v, True)
     gates = [to(x.alpha), to(x.mu), to(x.beta), to(x.eta)]
-    call = mdn.ChunkCall(q, k, v, *gates, None, None, C)
+    S0 = None if x.S0 is None else to(x.S0)
+    M0 = None if x.M0 is None else to(x.M0)
+    call = mdn.ChunkCall(q, k, v, *gates, S0, M0, C)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -126,7 +139,8 @@ def chunk_bench(args, torch, mdn, inputs):
     # read and write (each input once, each output once) and its causal-triangle
     # matrix work
     intra_bytes = tok_head * (2 * 2 * d + 16 + 2 * C * es + 8 * 4)
-    inter_bytes = tok_head * (es * 3 * d + es * 2 * d + 2 * C * es + 8 * 4) + B * H * 2 * d * d * 4
+    nstate = 2 if x.S0 is None else 4                 # S_T, M_T written (and S0, M0 read when given)
+    inter_bytes = tok_head * (es * 3 * d + es * 2 * d + 2 * C * es + 8 * 4) + B * H * nstate * d * d * 4
     intra_flop = tok_head * (2 * C * d + (2 * C * C) // 3)
     inter_flop = tok_head * (12 * d * d + 2 * C * d)
     kernels = {
@@ -144,7 +158,8 @@ def chunk_bench(args, torch, mdn, inputs):
             "mdn_inter_kernel": ["mdn_chunk.hip", "mdn_lds.h", "mdn_device.h"]}
     for name, kd in kernels.items():
         kd["source_sha"] = kernel_sources_sha(srcs[name])
-        kd["traffic"] = load_traffic(f"traffic_{name}_400M_layer.md", kd["source_sha"])
+        kd["traffic"] = (load_traffic(f"traffic_{name}_400M_layer.md", kd["source_sha"])
+                         if args.workload == 1 else None)
     dom_name = max(kernels, key=lambda n: kernels[n]["ms"])
     dom = kernels[dom_name]
     sha, traffic = dom["source_sha"], dom["traffic"]
@@ -219,6 +234,8 @@ def cpu_baseline(args, x):
     when it takes less than ``--cpu-seconds`` (repeated to fill that time,
     median reported), else a prefix of the sequence on all heads."""
     import oracle
+    if args.cpu_threads > 0:
+        oracle.set_threads(args.cpu_threads)
 
     def run(Ts):
         sl = lambda a: np.ascontiguousarray(a[:, :, :Ts])
@@ -281,8 +298,7 @@ def main():
         ch = chunk_bench(args, torch, mdn, inputs)
         x = ch["x"]
         out.update({"value": ch["tokens_per_s"], "ms_per_step": ch["ms_step"],
-                    "config": {"workload": "400M-layer chunk forward B8 H8 T4096 dk=dv=128 C64 bf16, "
-                                           "zero initial state", "B": x.B, "H": x.H, "T": x.T,
+                    "config": {"workload": WORKLOAD_NAMES[args.workload], "B": x.B, "H": x.H, "T": x.T,
                                "dk": x.dk, "dv": x.dv, "C": x.C, "tokens_per_step": x.B * x.T},
                     "mfma_frac_of_bf16_peak": ch["mfma_frac"], "flop_per_token_head": F_TOKEN_HEAD,
                     "kernels": ch["kernels"], "roofline": ch["roofline"], "outputs_finite": ch["finite"]})

@@ -57,6 +57,8 @@ def _load():
         lib.mdn_oracle_step.restype = None
         lib.mdn_oracle_threads.argtypes = []
         lib.mdn_oracle_threads.restype = ctypes.c_int
+        lib.mdn_oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.mdn_oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -72,6 +74,11 @@ def _ptr(a):
 def threads() -> int:
     """OpenMP threads the C oracle uses."""
     return int(_load().mdn_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Use n OpenMP threads in the following oracle calls."""
+    _load().mdn_oracle_set_threads(int(n))
 
 
 def fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None):

@@ -103,6 +103,17 @@ void mdn_oracle_step(long BH, long dk, long dv,
     }
 }
 
+/* Set the number of OpenMP threads for the following calls (n >= 1). */
+void mdn_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of OpenMP threads the oracle will use (for reporting). */
 int mdn_oracle_threads(void)
 {
