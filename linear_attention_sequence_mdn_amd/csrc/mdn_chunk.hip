@@ -244,9 +244,10 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         // ---- loader waves: every global->LDS copy and every output store ----
         // The K and Q rows of chunk n+1 are issued right after the chunk
         // barrier, T, Aqk, the V slab and the coefficients after the
-        // mid-chunk barrier.  Loader 0 writes O and loader 1 vtilde: the out
-        // tiles of chunk n are written in phase 2 of chunk n and copied out
-        // between the next chunk's two barriers, before they are written again.
+        // mid-chunk barrier.  Loader 1 writes vtilde (its out tile is written
+        // in phase 2 of chunk n and copied out before the mid-chunk barrier
+        // of chunk n+1); loader 0 writes O (finished in phase 1 of chunk n+1
+        // and copied out after that barrier).
         const int lw = __builtin_amdgcn_readfirstlane(wave - NW);
         auto issue = [&](uint32_t buf, int64_t m, int half) __attribute__((always_inline)) {
             const size_t tile = (size_t)bh * NT + m;
@@ -255,10 +256,11 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             if (half == 0) stage_chunk<LT, E, D, C, NLD, 0>(lw, buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
             else stage_chunk<LT, E, D, C, NLD, 1>(lw, buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
         };
-        auto copy_prev = [&](int64_t m) __attribute__((always_inline)) {   // out tiles of chunk m
-            const size_t rb = (size_t)bh * T + m * C;
-            if (lw == 0) copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + rb * D, valid_of(m), col0, lane);
-            else if (lw == 1) copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + rb * D, valid_of(m), col0, lane);
+        auto copy_o = [&](int64_t m) __attribute__((always_inline)) {
+            copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + ((size_t)bh * T + m * C) * D, valid_of(m), col0, lane);
+        };
+        auto copy_vt = [&](int64_t m) __attribute__((always_inline)) {
+            copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + ((size_t)bh * T + m * C) * D, valid_of(m), col0, lane);
         };
         const uint32_t aA = lds_addr(stA), aB = lds_addr(stB);
         if (NBUF == 2 && NT > 0) {
@@ -278,9 +280,10 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 __builtin_amdgcn_s_waitcnt(0);
                 lds_barrier();                          // B0
             }
-            if (n > 0) copy_prev(n - 1);
+            if (n > 0 && lw == 1) copy_vt(n - 1);        // vtilde of chunk n-1 (its phase 2)
             lds_barrier();                              // X
             if (NBUF == 2 && more) issue(nxt, n + 1, 1);
+            if (n > 0 && lw == 0) copy_o(n - 1);         // O of chunk n-1 (finished in phase 1 of chunk n)
         };
         if constexpr (NBUF == 2) {
             for (int64_t n = 0; n < NT; n += 2) {
@@ -290,8 +293,10 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         } else {
             for (int64_t n = 0; n < NT; ++n) load(aA, aA, n);
         }
-        lds_barrier();
-        if (NT > 0) copy_prev(NT - 1);
+        lds_barrier();                                  // E1: vtilde and R of the last chunk written
+        if (NT > 0 && lw == 1) copy_vt(NT - 1);
+        lds_barrier();                                  // E2: O of the last chunk written
+        if (NT > 0 && lw == 0) copy_o(NT - 1);
         return;
     }
 
@@ -318,9 +323,34 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             XM[t][e] = M0 ? M0[off] : 0.f;
         }
 
+    // Output rows of this wave, carried over the chunk boundary: the partner's
+    // share of R arrives with the next chunk barrier.
+    floatx4 Op[NCT];
+    auto finish_output = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int tc = 0; tc < NCT; ++tc) {
+            if (tc / NOT != h) continue;                // uniform: another wave's rows
+            floatx4 o = Op[tc];
+            if constexpr (RS > 1) {
+#pragma unroll
+                for (int h2 = 0; h2 < RS; ++h2) {
+                    if (h2 == h) continue;
+                    const floatx4 r = xr[((ct * RS + h2) * NOS + (tc < h2 * NOT ? tc : tc - NOT)) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] += r[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oo[(SL::perm(16 * tc + 4 * g) + e) * OW + 16 * ct + nn] = Tr::from_f(o[e]);
+        }
+    };
+
+    int64_t nchunk = 0;
     auto chunk = [&](const char* cur) __attribute__((always_inline)) {
         if constexpr (NBUF == 1) lds_barrier();         // B0'
-        lds_barrier();                                  // B0: chunk n staged, exchange areas free
+        lds_barrier();                                  // B0: chunk n staged, R of chunk n-1 visible
+        if (nchunk > 0) finish_output();                // O of chunk n-1
+        ++nchunk;
 
         const char* Kl = cur + LT::K0;
         const char* Ql = cur + LT::Q0;
@@ -330,29 +360,24 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             return *reinterpret_cast<const floatx4*>(cf + which * C + SL::perm(16 * tc + 4 * g));
         };
 
-        // -- phase 1: partial products over the wave's state rows --
-        floatx4 P[NCT], R[NCT];
+        // -- phase 1: P_h = -Diag(abar) K S_h + Diag(alpha b_prev) K M_h over the wave's rows --
+        frag Sb[KSH], Mb[KSH];                          // chunk-start states, also used in phase 2
+#pragma unroll
+        for (int ks = 0; ks < KSH; ++ks) { Sb[ks] = SL::from_acc(XS, ks); Mb[ks] = SL::from_acc(XM, ks); }
+        floatx4 P[NCT];
         {
-            frag Sb[KSH], Mb[KSH];
+            floatx4 KSa[NCT], KMa[NCT];
 #pragma unroll
-            for (int ks = 0; ks < KSH; ++ks) { Sb[ks] = SL::from_acc(XS, ks); Mb[ks] = SL::from_acc(XM, ks); }
-            floatx4 KSa[NCT], KMa[NCT], QSa[NCT], QMa[NCT];
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) { KSa[tc] = zero4(); KMa[tc] = zero4(); QSa[tc] = zero4(); QMa[tc] = zero4(); }
+            for (int tc = 0; tc < NCT; ++tc) { KSa[tc] = zero4(); KMa[tc] = zero4(); }
 #pragma unroll
             for (int ks = 0; ks < KSH; ++ks) {
-                frag a[NCT], b[NCT];
+                frag a[NCT];
 #pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) {
-                    a[tc] = LdsA<Tr, LT::PK>::load(Kl, SL::perm(16 * tc + nn), ks0 + ks, g);
-                    b[tc] = LdsA<Tr, LT::PK>::load(Ql, SL::perm(16 * tc + nn), ks0 + ks, g);
-                }
+                for (int tc = 0; tc < NCT; ++tc) a[tc] = LdsA<Tr, LT::PK>::load(Kl, SL::perm(16 * tc + nn), ks0 + ks, g);
 #pragma unroll
                 for (int tc = 0; tc < NCT; ++tc) {
                     KSa[tc] = Tr::mma(a[tc], Sb[ks], KSa[tc]);
                     KMa[tc] = Tr::mma(a[tc], Mb[ks], KMa[tc]);
-                    QSa[tc] = Tr::mma(b[tc], Sb[ks], QSa[tc]);
-                    QMa[tc] = Tr::mma(b[tc], Mb[ks], QMa[tc]);
                 }
             }
             // first half of the state updates, while the chunk-start M is at hand
@@ -370,25 +395,18 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             }
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc) {
-                const floatx4 ca = crow(MDN_COEF_ABAR, tc), cp = crow(MDN_COEF_ABP, tc), cb = crow(MDN_COEF_B, tc);
+                const floatx4 ca = crow(MDN_COEF_ABAR, tc), cp = crow(MDN_COEF_ABP, tc);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    P[tc][e] = cp[e] * KMa[tc][e] - ca[e] * KSa[tc][e];
-                    R[tc][e] = ca[e] * QSa[tc][e] - cb[e] * QMa[tc][e];
-                }
+                for (int e = 0; e < 4; ++e) P[tc][e] = cp[e] * KMa[tc][e] - ca[e] * KSa[tc][e];
             }
         }
         if constexpr (RS > 1) {
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc) xp[((ct * RS + h) * NCT + tc) * 64 + lane] = P[tc];
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc)            // the other waves' output row tiles
-                if (tc / NOT != h)
-                    xr[((ct * RS + h) * NOS + (tc < h * NOT ? tc : tc - NOT)) * 64 + lane] = R[tc];
         }
         lds_barrier();                                  // X: partial products visible
 
-        // -- phase 2: every LDS read of the phase is issued first --
+        // -- phase 2 --
         const char* Tl = cur + LT::T0;
         const char* Al = cur + LT::A0;
         frag tA[KSC][NCT];                              // T operands
@@ -413,13 +431,6 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
                     for (int e = 0; e < 4; ++e) P[tc][e] += o[e];
                 }
-#pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) {
-                    if (tc / NOT != h) continue;        // uniform
-                    const floatx4 r = xr[((ct * RS + h2) * NOS + (tc < h2 * NOT ? tc : tc - NOT)) * 64 + lane];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) R[tc][e] += r[e];
-                }
             }
         }
         // vtilde = T W
@@ -435,7 +446,32 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
                 for (int tc = 0; tc < NCT; ++tc) Vx[tc] = Tr::mma(tA[ks][tc], Wb[ks], Vx[tc]);
         }
-        // read while T W runs: gS, gM of the contraction slots, K^T operands of the wave's rows
+        // independent of vtilde, run while T W is in flight:
+        // R_h = Diag(abar) Q S_h - Diag(b) Q M_h with the chunk-start states
+        floatx4 R[NCT];
+        {
+            floatx4 QSa[NCT], QMa[NCT];
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc) { QSa[tc] = zero4(); QMa[tc] = zero4(); }
+#pragma unroll
+            for (int ks = 0; ks < KSH; ++ks) {
+                frag b[NCT];
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) b[tc] = LdsA<Tr, LT::PK>::load(Ql, SL::perm(16 * tc + nn), ks0 + ks, g);
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) {
+                    QSa[tc] = Tr::mma(b[tc], Sb[ks], QSa[tc]);
+                    QMa[tc] = Tr::mma(b[tc], Mb[ks], QMa[tc]);
+                }
+            }
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc) {
+                const floatx4 ca = crow(MDN_COEF_ABAR, tc), cb = crow(MDN_COEF_B, tc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) R[tc][e] = ca[e] * QSa[tc][e] - cb[e] * QMa[tc][e];
+            }
+        }
+        // gS, gM of the contraction slots, K^T operands of the wave's rows
         float gs[KSC][NSL], gm[KSC][NSL];
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
@@ -467,19 +503,20 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                     XM[t] = Tr::mma(kT[ks][t], VM[ks], XM[t]);
                 }
         }
-        // output rows of this wave: O = R_0 + R_1 + Aqk vtilde, and its vtilde rows
+        // this wave's output rows: Op = R_h + Aqk vtilde (the partner's R follows);
+        // the other rows' R to the exchange; this wave's vtilde rows to the out tile
 #pragma unroll
         for (int tc = 0; tc < NCT; ++tc) {
-            if (tc / NOT != h) continue;                // uniform: another wave's rows
+            if (tc / NOT != h) {                        // uniform
+                if constexpr (RS > 1) xr[((ct * RS + h) * NOS + (tc < h * NOT ? tc : tc - NOT)) * 64 + lane] = R[tc];
+                continue;
+            }
             floatx4 o = R[tc];
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) o = Tr::mma(LdsA<Tr, LT::PT>::load(Al, SL::perm(16 * tc + nn), ks, g), Vb[ks], o);
+            Op[tc] = o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = SL::perm(16 * tc + 4 * g) + e;
-                oo[row * OW + 16 * ct + nn] = Tr::from_f(o[e]);
-                ov[row * OW + 16 * ct + nn] = Tr::from_f(Vx[tc][e]);
-            }
+            for (int e = 0; e < 4; ++e) ov[(SL::perm(16 * tc + 4 * g) + e) * OW + 16 * ct + nn] = Tr::from_f(Vx[tc][e]);
         }
     };
 
@@ -491,7 +528,9 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     } else {
         for (int64_t n = 0; n < NT; ++n) chunk(stA);
     }
-    lds_barrier();
+    lds_barrier();                                      // E1: R of the last chunk visible
+    if (NT > 0) finish_output();
+    lds_barrier();                                      // E2: O of the last chunk in the out tile
 
 #pragma unroll
     for (int t = 0; t < NDH; ++t)
