@@ -40,38 +40,47 @@ namespace mdn {
 // mdn_inter_kernel
 //
 // One workgroup owns a slab of 16*NCOL state columns of one head and runs
-// the chunks of that head in order.  State columns are independent.  For
-// every 16-column tile, RS compute waves split the dk state rows into RS
-// halves: wave (ct, h) holds rows [h*D/RS, (h+1)*D/RS) of both S and M for
-// column tile ct in fp32 registers.  Per chunk:
-//   phase 1: partial products over its own state rows,
+// the chunks of that head in order.  State columns are independent.
+//
+// Chain waves (NCOL*RS of them) carry the state.  For every 16-column tile,
+// RS chain waves split the dk state rows into RS parts: wave (ct, h) holds
+// rows [h*D/RS, (h+1)*D/RS) of both S and M for column tile ct in fp32
+// registers.  Per chunk:
+//   phase 1: vtilde starts as T V; the partial products over its own rows,
 //              P_h = -Diag(abar) K S_h + Diag(alpha b_prev) K M_h,
-//              R_h =  Diag(abar) Q S_h - Diag(b) Q M_h,
-//            exchanged with the partner wave (one barrier);
-//   phase 2: W = V + P_0 + P_1 and vtilde = T W (both waves, so that no
-//            second exchange is needed), the output rows the wave owns,
-//            O = R_0 + R_1 + Aqk vtilde, and the updates of its own rows
-//            S_h <- abar_C S_h - b_C M_h + K_h^T Diag(gS) vtilde,
-//            M_h <- mubar_C M_h - K_h^T Diag(gM) vtilde,
-//            which need nothing from the partner.
-// With RS = 1 one wave does all of it and nothing is exchanged.
+//            are exchanged with the partner wave (one barrier), and the
+//            first half of the state update (abar_C S_h - b_C M_h,
+//            mubar_C M_h) is done while the chunk-start M_h is at hand;
+//   phase 2: vtilde += T (P_0 + P_1) (both waves, so that no second
+//            exchange is needed), the vtilde operands go to LDS, and the
+//            wave's rows are updated, S_h += K_h^T Diag(gS) vtilde,
+//            M_h -= K_h^T Diag(gM) vtilde, which needs nothing from the
+//            partner; the new state's bf16 operands go to LDS.
+// With RS = 1 one wave per column tile does all of it and nothing is
+// exchanged.  The output is off the state chain: nothing of it is computed
+// by the chain waves.
 //
 // Four loader waves issue every global->LDS copy (K, Q, T, Aqk, the
 // coefficient rows and the V slab of the next chunk, 16 bytes per lane, into
-// one of two buffers) and every output store (O and vtilde through LDS out
-// tiles, 16-byte stores).  K, Q, T and Aqk rows are XOR-swizzled by 16-byte
-// piece so that the 16 rows an operand read touches fall in different LDS
-// banks.  K^T, the A operand of the state updates, is read from the
-// row-major K tile with the LDS transpose read (bf16).  Rows past the end of
-// a ragged last chunk are copies of the last valid row: they only ever meet
-// zero weights (T and Aqk are lower triangular, gS = gM = 0 there) and are
-// never stored.
+// one of two buffers) and every output store, and they compute the output:
+// after the barrier of chunk n each forms, for its token tile and column
+// tiles, R = Diag(abar) Q S - Diag(b) Q M from the chunk-start state
+// operands (all dk rows, so no partial sums are exchanged); after the next
+// chunk barrier it adds Aqk vtilde, and writes O and vtilde to LDS out tiles
+// that are copied out with 16-byte stores.  K, Q, T and Aqk rows are
+// XOR-swizzled by 16-byte piece so that the 16 rows an operand read touches
+// fall in different LDS banks.  K^T, the A operand of the state updates, and
+// V, the B operand of T V, are read with the LDS transpose read (bf16).  Rows
+// past the end of a ragged last chunk are copies of the last valid row: they
+// only ever meet zero weights (T and Aqk are lower triangular, gS = gM = 0
+// there) and are never stored.
 // ---------------------------------------------------------------------------
 template <typename Tr, int D, int C, int NCOL, int RS, int NBUF>
 struct InterLayout {
     using E = typename Tr::elem;
     using frag = typename Tr::frag;
     static constexpr int ES = sizeof(E);
+    static constexpr int FS = sizeof(frag);
     static constexpr int PK = D * ES / 16;            // 16-byte pieces per K/Q row
     static constexpr int PT = C * ES / 16;            // pieces per T/Aqk row
     static constexpr int PV = 16 * NCOL * ES / 16;    // pieces per V-slab / out row
@@ -85,26 +94,33 @@ struct InterLayout {
     static constexpr int CF0 = A0 + C * PT * 16;
     static constexpr int V0 = CF0 + PC * 16;
     static constexpr int BUF = V0 + C * PV * 16;
-    // partial-product exchange (RS > 1): P for every row tile, R for the
-    // other waves' output row tiles; 4 fp32 values per lane and tile
     static constexpr int NCT = C / 16;
-    static constexpr int XB = 16;                     // bytes per lane and tile
-    static constexpr int XCH = RS > 1 ? NCOL * RS * (NCT + NCT - NCT / RS) * 64 * XB : 0;
+    static constexpr int KSH = D / RS / Tr::KW;       // contraction steps of one row part
+    static constexpr int KSC = C / Tr::KW;
+    // partial-product exchange (RS > 1): 4 fp32 values per lane and row tile
+    static constexpr int XP = RS > 1 ? NCOL * RS * NCT * 64 * 16 : 0;
+    // chain -> output waves: chunk-start S, M operands and vtilde operands
+    static constexpr int SM = NCOL * RS * 2 * KSH * 64 * FS;
+    static constexpr int VB = NCOL * KSC * 64 * FS;
     static constexpr int OUT = 2 * C * PV * 16;
-    static constexpr int TOTAL = NBUF * BUF + XCH + OUT;
+    static constexpr int TOTAL = NBUF * BUF + XP + SM + VB + OUT;
 };
 
 template <typename Tr, int D, int C>
 struct InterPick {
     static constexpr int LIMIT = 160 * 1024 - 1024;
-    // A row half must hold whole contraction steps of the state products and
-    // each of the two waves some output row tiles.  (Four parts, two compute
-    // waves per SIMD, measured slower: the barrier-synchronised waves sit in
-    // the same latency-bound phase at the same time.)
+    // One chain wave per column tile holds all dk rows.  Splitting the rows
+    // over two waves (one per SIMD, with the partial products of K S and
+    // K M exchanged through LDS every chunk) measured slower once the output
+    // moved to the loader waves: the exchange puts a second workgroup
+    // barrier on the chain and four waves read every T operand.  fp32
+    // operands at dk >= 64 keep the split, which halves the registers a
+    // chain wave holds.
     static constexpr bool BF = std::is_same<Tr, TraitsBf16>::value;
-    static constexpr int RS = ((BF ? D >= 64 : D >= 32) && C >= 32) ? 2 : 1;
+    static constexpr int RS = (!BF && D >= 64 && C >= 32) ? 2 : 1;
     static constexpr int NCOL = (D >= 32 && InterLayout<Tr, D, C, 2, RS, 1>::TOTAL <= LIMIT) ? 2 : 1;
     static constexpr int NBUF = InterLayout<Tr, D, C, NCOL, RS, 2>::TOTAL <= LIMIT ? 2 : 1;
+    static_assert(InterLayout<Tr, D, C, NCOL, RS, NBUF>::TOTAL <= LIMIT, "LDS");
 };
 
 // K^T operand of the state update for d-tile td, contraction step ks.
@@ -133,6 +149,34 @@ template <int P> struct KtOperand<TraitsF32, P> {
         const int g = lane >> 4, m = lane & 15;
         const int r = 16 * (ks >> 2) + 4 * g + (ks & 3);
         return *reinterpret_cast<const float*>(Kt + swz<P>(r, 4 * (16 * td + m)));
+    }
+};
+
+// V slab (plain rows of OW elements) as the B operand of T V for column tile
+// ct, contraction step ks.
+template <typename Tr, int OW> struct VOperand;
+template <int OW> struct VOperand<TraitsBf16, OW> {
+    static __device__ __forceinline__ bf16x8 load(const char* Vs, int ct, int ks, int lane) {
+        // Transpose read: source lane s of group g points at row
+        // 32ks + 8g + s/4 (+4 for the second half) and columns
+        // 16ct + 4(s%4) .. +3, so lane i receives V[32ks + 8g + j][16ct + i]
+        // for j = 0..3 (4..7): the contraction slots of lane group g.
+        const int g = lane >> 4, s = lane & 15;
+        const int r0 = 32 * ks + 8 * g + (s >> 2);
+        const int b = 2 * (16 * ct + 4 * (s & 3));
+        union { shortx4 h[2]; bf16x8 v; } f;
+        f.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(Vs + r0 * OW * 2 + b));
+        f.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(Vs + (r0 + 4) * OW * 2 + b));
+        return f.v;
+    }
+};
+template <int OW> struct VOperand<TraitsF32, OW> {
+    static __device__ __forceinline__ float load(const char* Vs, int ct, int ks, int lane) {
+        const int g = lane >> 4, m = lane & 15;
+        const int r = 16 * (ks >> 2) + 4 * g + (ks & 3);
+        return *reinterpret_cast<const float*>(Vs + 4 * (r * OW + 16 * ct + m));
     }
 };
 
@@ -183,16 +227,25 @@ __device__ __forceinline__ void stage_chunk(int lw, uint32_t buf, const E* __res
 }
 
 // Copy an out tile (C rows x 16*NCOL elements in LDS) to rows [0, valid) of
-// a row-major [.., D] output, by one wave; `dst` points at the chunk's first row.
+// a row-major [.., D] output, by one wave; `dst` points at the chunk's first
+// row.  Every LDS read is issued before the first store.
 template <typename LT, typename E, int D, int C>
 __device__ __forceinline__ void copy_out(const char* tile, E* __restrict__ dst, int valid, int col0, int lane)
 {
     constexpr int EPS = 16 / LT::ES;
-    for (int s = lane; s < C * LT::PV; s += 64) {
+    constexpr int NP = C * LT::PV, NI = (NP + 63) / 64;
+    uint4 val[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int s = i * 64 + lane;
+        if (NP % 64 == 0 || s < NP) val[i] = *reinterpret_cast<const uint4*>(tile + s * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int s = i * 64 + lane;
         const int r = s / LT::PV, p = s % LT::PV;
-        if (r < valid)
-            *reinterpret_cast<uint4*>(dst + (size_t)r * D + col0 + p * EPS) =
-                *reinterpret_cast<const uint4*>(tile + s * 16);
+        if ((NP % 64 == 0 || s < NP) && r < valid)
+            *reinterpret_cast<uint4*>(dst + (size_t)r * D + col0 + p * EPS) = val[i];
     }
 }
 
@@ -215,21 +268,20 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     using LT = InterLayout<Tr, D, C, NCOL, RS, NBUF>;
     using frag = typename Tr::frag;
     constexpr int NSL = SL::NSLOT;
-    constexpr int NW = NCOL * RS;                     // compute waves; waves NW .. NW+NLD-1 load
-    constexpr int NCT = C / 16, KSC = C / Tr::KW;
-    constexpr int DH = D / RS;                        // state rows per compute wave
+    constexpr int NW = NCOL * RS;                     // chain waves; waves NW .. NW+NLD-1 load and output
+    constexpr int NCT = C / 16, KSC = C / Tr::KW, KSD = D / Tr::KW;
+    constexpr int DH = D / RS;                        // state rows per chain wave
     constexpr int NDH = DH / 16, KSH = DH / Tr::KW;   // its accumulator tiles / contraction steps
-    constexpr int NOT = NCT / RS;                     // output row tiles per compute wave
     constexpr int SLABS = D / (16 * NCOL);
     constexpr int OW = 16 * NCOL;                     // out-tile row length (elements)
-    static_assert(DH % 16 == 0 && DH % Tr::KW == 0 && NCT % RS == 0, "row split");
+    static_assert(DH % 16 == 0 && DH % Tr::KW == 0 && NLD == 4 && NLD % NCT == 0, "row split, output tasks");
     // Distinct LDS objects, so that the compiler can tell the buffer being
     // prefetched from every buffer being read.
     __shared__ __attribute__((aligned(16))) char stA[LT::BUF];
     __shared__ __attribute__((aligned(16))) char stB[NBUF == 2 ? LT::BUF : 16];
-    constexpr int NOS = NCT - NOT;                    // other waves' output row tiles
     __shared__ __attribute__((aligned(16))) floatx4 xp[RS > 1 ? NCOL * RS * NCT * 64 : 1];   // P_h
-    __shared__ __attribute__((aligned(16))) floatx4 xr[RS > 1 ? NCOL * RS * NOS * 64 : 1];   // R_h
+    __shared__ __attribute__((aligned(16))) frag sm[NCOL * RS * 2 * KSH * 64];             // S_h, M_h operands
+    __shared__ __attribute__((aligned(16))) frag vb[NCOL * KSC * 64];                       // vtilde operands
     __shared__ __attribute__((aligned(16))) E ov[C * OW];                // vtilde out tile
     __shared__ __attribute__((aligned(16))) E oo[C * OW];                // O out tile
 
@@ -239,16 +291,31 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     xcd_head_map(blockIdx.x, SLABS, BH, bh, slab);
     const int col0 = slab * OW;
     auto valid_of = [&](int64_t n) { return (int)((T - n * C) < C ? (T - n * C) : C); };
+    // coefficient of accumulator rows perm(16tc + 4g) + e, e = 0..3 (contiguous)
+    auto crow = [&](const float* cf, int which, int tc) __attribute__((always_inline)) {
+        return *reinterpret_cast<const floatx4*>(cf + which * C + SL::perm(16 * tc + 4 * g));
+    };
 
     if (wave >= NW) {
-        // ---- loader waves: every global->LDS copy and every output store ----
-        // The K and Q rows of chunk n+1 are issued right after the chunk
-        // barrier, T, Aqk, the V slab and the coefficients after the
-        // mid-chunk barrier.  Loader 1 writes vtilde (its out tile is written
-        // in phase 2 of chunk n and copied out before the mid-chunk barrier
-        // of chunk n+1); loader 0 writes O (finished in phase 1 of chunk n+1
-        // and copied out after that barrier).
-        const int lw = __builtin_amdgcn_readfirstlane(wave - NW);
+        // ---- loader / output waves ----
+        // Copies: the K and Q rows of chunk n+1 are issued right after the
+        // chunk barrier, T, Aqk, the V slab and the coefficients after the
+        // mid-chunk barrier.  Output: wave lw owns token tile tc = lw % NCT
+        // of the column tiles lw / NCT + i * (NLD / NCT).  Between the
+        // barrier of chunk n and its mid-chunk barrier it finishes O and
+        // vtilde of chunk n-1 into the out tiles (the vtilde operands of
+        // chunk n-1 were stored before the barrier, and its Aqk is still
+        // staged) and forms R of chunk n (its chunk-start state operands
+        // were stored before the barrier too).  The out tiles are copied
+        // out after the mid-chunk barrier, O by loader 2 and vtilde by
+        // loader 3 (loaders 0 and 1 issue the larger copies).
+        // The wave index is a template constant of the wave's code, so that
+        // the token tile and every choice of which copy to issue are too.
+        auto loader = [&](auto lwc) __attribute__((always_inline)) {
+        constexpr int lw = decltype(lwc)::value;
+        constexpr int OCS = NLD / NCT;                 // output waves per token tile
+        constexpr int NOC = (NCOL + OCS - 1) / OCS;    // column tiles per output wave
+        constexpr int tc = lw % NCT, oc0 = lw / NCT;
         auto issue = [&](uint32_t buf, int64_t m, int half) __attribute__((always_inline)) {
             const size_t tile = (size_t)bh * NT + m;
             const size_t rb = (size_t)bh * T + m * C;
@@ -256,58 +323,117 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             if (half == 0) stage_chunk<LT, E, D, C, NLD, 0>(lw, buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
             else stage_chunk<LT, E, D, C, NLD, 1>(lw, buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
         };
-        auto copy_o = [&](int64_t m) __attribute__((always_inline)) {
-            copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + ((size_t)bh * T + m * C) * D, valid_of(m), col0, lane);
+        auto copy_outs = [&](int64_t m) __attribute__((always_inline)) {
+            if (lw == 2)
+                copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + ((size_t)bh * T + m * C) * D, valid_of(m), col0, lane);
+            else if (lw == 3)
+                copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + ((size_t)bh * T + m * C) * D, valid_of(m), col0, lane);
         };
-        auto copy_vt = [&](int64_t m) __attribute__((always_inline)) {
-            copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + ((size_t)bh * T + m * C) * D, valid_of(m), col0, lane);
+        floatx4 R[NOC];
+        // R = Diag(abar) Q S - Diag(b) Q M of the chunk staged in `cur`, over all dk rows
+        auto out_r = [&](const char* cur) __attribute__((always_inline)) {
+            const char* Ql = cur + LT::Q0;
+            const float* cf = reinterpret_cast<const float*>(cur + LT::CF0);
+            frag qa[KSD];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) qa[ks] = LdsA<Tr, LT::PK>::load(Ql, SL::perm(16 * tc + nn), ks, g);
+            const floatx4 ca = crow(cf, MDN_COEF_ABAR, tc), cb = crow(cf, MDN_COEF_B, tc);
+#pragma unroll
+            for (int i = 0; i < NOC; ++i) {
+                const int oct = oc0 + i * OCS;
+                if (oct >= NCOL) continue;
+                floatx4 qs = zero4(), qm = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) {
+                    const int base = ((oct * RS + ks / KSH) * 2) * KSH * 64 + (ks % KSH) * 64 + lane;
+                    qs = Tr::mma(qa[ks], sm[base], qs);
+                    qm = Tr::mma(qa[ks], sm[base + KSH * 64], qm);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) R[i][e] = ca[e] * qs[e] - cb[e] * qm[e];
+            }
+        };
+        // O = R + Aqk vtilde and the vtilde rows of the chunk staged in `cur`, into the out tiles
+        auto out_o = [&](const char* cur) __attribute__((always_inline)) {
+            const char* Al = cur + LT::A0;
+            frag aa[KSC];
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) aa[ks] = LdsA<Tr, LT::PT>::load(Al, SL::perm(16 * tc + nn), ks, g);
+#pragma unroll
+            for (int i = 0; i < NOC; ++i) {
+                const int oct = oc0 + i * OCS;
+                if (oct >= NCOL) continue;
+                frag vf[KSC];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) vf[ks] = vb[(oct * KSC + ks) * 64 + lane];
+                floatx4 o = R[i];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) o = Tr::mma(aa[ks], vf[ks], o);
+                const int r0 = SL::perm(16 * tc + 4 * g), c = 16 * oct + nn;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    oo[(r0 + e) * OW + c] = Tr::from_f(o[e]);
+                    ov[(r0 + e) * OW + c] = SL::acc_elem(vf, tc, e);
+                }
+            }
         };
         const uint32_t aA = lds_addr(stA), aB = lds_addr(stB);
-        if (NBUF == 2 && NT > 0) {
-            issue(aA, 0, 0);
-            issue(aA, 0, 1);
-        }
-        auto load = [&](uint32_t cur, uint32_t nxt, int64_t n) __attribute__((always_inline)) {
-            const bool more = n + 1 < NT;
-            if constexpr (NBUF == 2) {
+        if constexpr (NBUF == 2) {
+            if (NT > 0) {
+                issue(aA, 0, 0);
+                issue(aA, 0, 1);
+            }
+            auto step = [&](uint32_t nxt, const char* cur, const char* prev, int64_t n) __attribute__((always_inline)) {
+                const bool more = n + 1 < NT;
                 __builtin_amdgcn_s_waitcnt(0);          // chunk n has landed (and earlier stores left)
                 lds_barrier();                          // B0
                 if (more) issue(nxt, n + 1, 0);
-            } else {
-                lds_barrier();                          // B0': the previous chunk's reads are done
-                issue(cur, n, 0);
-                issue(cur, n, 1);
-                __builtin_amdgcn_s_waitcnt(0);
-                lds_barrier();                          // B0
-            }
-            if (n > 0 && lw == 1) copy_vt(n - 1);        // vtilde of chunk n-1 (its phase 2)
-            lds_barrier();                              // X
-            if (NBUF == 2 && more) issue(nxt, n + 1, 1);
-            if (n > 0 && lw == 0) copy_o(n - 1);         // O of chunk n-1 (finished in phase 1 of chunk n)
-        };
-        if constexpr (NBUF == 2) {
+                if (n > 0) out_o(prev);                 // chunk n-1
+                out_r(cur);                             // chunk n
+                lds_barrier();                          // X
+                if (more) issue(nxt, n + 1, 1);
+                if (n > 0) copy_outs(n - 1);
+            };
             for (int64_t n = 0; n < NT; n += 2) {
-                load(aA, aB, n);
-                if (n + 1 < NT) load(aB, aA, n + 1);
+                step(aB, stA, stB, n);
+                if (n + 1 < NT) step(aA, stB, stA, n + 1);
             }
         } else {
-            for (int64_t n = 0; n < NT; ++n) load(aA, aA, n);
+            for (int64_t n = 0; n < NT; ++n) {
+                lds_barrier();                          // B0': the chain waves are done with chunk n-1
+                if (n > 0) out_o(stA);                  // chunk n-1, before its Aqk is overwritten
+                lds_barrier();                          // B0'': every read of chunk n-1 is done
+                issue(aA, n, 0);
+                issue(aA, n, 1);
+                if (n > 0) copy_outs(n - 1);
+                __builtin_amdgcn_s_waitcnt(0);
+                lds_barrier();                          // B0
+                out_r(stA);
+                lds_barrier();                          // X
+            }
         }
-        lds_barrier();                                  // E1: vtilde and R of the last chunk written
-        if (NT > 0 && lw == 1) copy_vt(NT - 1);
-        lds_barrier();                                  // E2: O of the last chunk written
-        if (NT > 0 && lw == 0) copy_o(NT - 1);
+        lds_barrier();                                  // E1: vtilde operands of the last chunk stored
+        if (NT > 0) out_o(NBUF == 2 && ((NT - 1) & 1) ? stB : stA);
+        lds_barrier();                                  // E2: out tiles of the last chunk written
+        if (NT > 0) copy_outs(NT - 1);
+        };
+        switch (__builtin_amdgcn_readfirstlane(wave - NW)) {
+        case 0: loader(std::integral_constant<int, 0>{}); break;
+        case 1: loader(std::integral_constant<int, 1>{}); break;
+        case 2: loader(std::integral_constant<int, 2>{}); break;
+        default: loader(std::integral_constant<int, 3>{}); break;
+        }
         return;
     }
 
-    // ---- compute waves ----
-    // The row half is a template constant of the wave's code, so that the
+    // ---- chain waves ----
+    // The row part is a template constant of the wave's code, so that the
     // code of a chunk is straight-line (uniform branches on it would split
     // the chunk into small blocks, each waiting for its own LDS reads).
     const int cw = __builtin_amdgcn_readfirstlane(wave);
     const int ct = cw / RS;                           // column tile
-    auto compute = [&](auto hc) __attribute__((always_inline)) {
-    constexpr int h = decltype(hc)::value;            // row half
+    auto chain = [&](auto hc) __attribute__((always_inline)) {
+    constexpr int h = decltype(hc)::value;            // row part
     const int col = col0 + 16 * ct + nn;
     const int td0 = h * NDH, ks0 = h * KSH;           // first state tile / contraction step owned
 
@@ -322,50 +448,46 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             XS[t][e] = S0 ? S0[off] : 0.f;
             XM[t][e] = M0 ? M0[off] : 0.f;
         }
-
-    // Output rows of this wave, carried over the chunk boundary: the partner's
-    // share of R arrives with the next chunk barrier.
-    floatx4 Op[NCT];
-    auto finish_output = [&]() __attribute__((always_inline)) {
+    frag* const smS = sm + ((ct * RS + h) * 2) * KSH * 64 + lane;
+    frag* const smM = smS + KSH * 64;
+    // chunk-start state operands, for P and for the output waves; stored
+    // before the chunk barrier, at the end of the previous chunk
+    frag Sb[KSH], Mb[KSH];
+    auto state_operands = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int tc = 0; tc < NCT; ++tc) {
-            if (tc / NOT != h) continue;                // uniform: another wave's rows
-            floatx4 o = Op[tc];
-            if constexpr (RS > 1) {
-#pragma unroll
-                for (int h2 = 0; h2 < RS; ++h2) {
-                    if (h2 == h) continue;
-                    const floatx4 r = xr[((ct * RS + h2) * NOS + (tc < h2 * NOT ? tc : tc - NOT)) * 64 + lane];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] += r[e];
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) oo[(SL::perm(16 * tc + 4 * g) + e) * OW + 16 * ct + nn] = Tr::from_f(o[e]);
+        for (int ks = 0; ks < KSH; ++ks) {
+            Sb[ks] = SL::from_acc(XS, ks);
+            Mb[ks] = SL::from_acc(XM, ks);
+            smS[ks * 64] = Sb[ks];
+            smM[ks * 64] = Mb[ks];
         }
     };
+    state_operands();
 
-    int64_t nchunk = 0;
     auto chunk = [&](const char* cur) __attribute__((always_inline)) {
-        if constexpr (NBUF == 1) lds_barrier();         // B0'
-        lds_barrier();                                  // B0: chunk n staged, R of chunk n-1 visible
-        if (nchunk > 0) finish_output();                // O of chunk n-1
-        ++nchunk;
-
+        if constexpr (NBUF == 1) {
+            lds_barrier();                              // B0'
+            lds_barrier();                              // B0''
+        }
+        lds_barrier();                                  // B0: chunk n staged
         const char* Kl = cur + LT::K0;
-        const char* Ql = cur + LT::Q0;
+        const char* Tl = cur + LT::T0;
+        const char* Vl = cur + LT::V0;
         const float* cf = reinterpret_cast<const float*>(cur + LT::CF0);
-        // coefficient of accumulator rows perm(16tc + 4g) + e, e = 0..3 (contiguous)
-        auto crow = [&](int which, int tc) __attribute__((always_inline)) {
-            return *reinterpret_cast<const floatx4*>(cf + which * C + SL::perm(16 * tc + 4 * g));
-        };
 
-        // -- phase 1: P_h = -Diag(abar) K S_h + Diag(alpha b_prev) K M_h over the wave's rows --
-        frag Sb[KSH], Mb[KSH];                          // chunk-start states, also used in phase 2
+        // -- phase 1 --
+        // T operands (for T V now and T W in phase 2); vtilde starts as T V
+        frag tA[KSC][NCT];
 #pragma unroll
-        for (int ks = 0; ks < KSH; ++ks) { Sb[ks] = SL::from_acc(XS, ks); Mb[ks] = SL::from_acc(XM, ks); }
+        for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+            for (int tc = 0; tc < NCT; ++tc) tA[ks][tc] = LdsA<Tr, LT::PT>::load(Tl, SL::perm(16 * tc + nn), ks, g);
+        floatx4 Vx[NCT];
+#pragma unroll
+        for (int tc = 0; tc < NCT; ++tc) Vx[tc] = zero4();
         floatx4 P[NCT];
         {
+            // P_h = -Diag(abar) K S_h + Diag(alpha b_prev) K M_h over the wave's rows
             floatx4 KSa[NCT], KMa[NCT];
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc) { KSa[tc] = zero4(); KMa[tc] = zero4(); }
@@ -379,6 +501,15 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                     KSa[tc] = Tr::mma(a[tc], Sb[ks], KSa[tc]);
                     KMa[tc] = Tr::mma(a[tc], Mb[ks], KMa[tc]);
                 }
+                if constexpr (KSH > 2) {                // bounds the K operands held at once
+                    if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                const frag vB = VOperand<Tr, OW>::load(Vl, ct, ks, lane);
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) Vx[tc] = Tr::mma(tA[ks][tc], vB, Vx[tc]);
             }
             // first half of the state updates, while the chunk-start M is at hand
             {
@@ -395,7 +526,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             }
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc) {
-                const floatx4 ca = crow(MDN_COEF_ABAR, tc), cp = crow(MDN_COEF_ABP, tc);
+                const floatx4 ca = crow(cf, MDN_COEF_ABAR, tc), cp = crow(cf, MDN_COEF_ABP, tc);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) P[tc][e] = cp[e] * KMa[tc][e] - ca[e] * KSa[tc][e];
             }
@@ -404,24 +535,25 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc) xp[((ct * RS + h) * NCT + tc) * 64 + lane] = P[tc];
         }
+        // gS, gM of the contraction slots, K^T operands of the wave's rows (for
+        // phase 2; read before the barrier where the registers allow)
+        float gs[KSC][NSL], gm[KSC][NSL];
+        frag kT[KSC][NDH];
+        auto read_update_operands = [&](int ks) __attribute__((always_inline)) {
+            SL::load_row(cf + MDN_COEF_GS * C, ks, g, gs[ks]);
+            SL::load_row(cf + MDN_COEF_GM * C, ks, g, gm[ks]);
+#pragma unroll
+            for (int t = 0; t < NDH; ++t) kT[ks][t] = KtOperand<Tr, LT::PK>::load(Kl, td0 + t, ks, lane);
+        };
+        constexpr bool EARLY = KSC * (NDH * sizeof(frag) / 4 + 2 * NSL) <= 64;
+        if constexpr (EARLY) {
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) read_update_operands(ks);
+        }
         lds_barrier();                                  // X: partial products visible
 
         // -- phase 2 --
-        const char* Tl = cur + LT::T0;
-        const char* Al = cur + LT::A0;
-        frag tA[KSC][NCT];                              // T operands
-#pragma unroll
-        for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) tA[ks][tc] = LdsA<Tr, LT::PT>::load(Tl, SL::perm(16 * tc + nn), ks, g);
-        {                                               // W = V + P_0 + P_1 (V slab values of the accumulator rows)
-            const E* Vl = reinterpret_cast<const E*>(cur + LT::V0) + 16 * ct + nn;
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) P[tc][e] += Tr::to_f(Vl[(SL::perm(16 * tc + 4 * g) + e) * OW]);
-        }
-        if constexpr (RS > 1) {
+        if constexpr (RS > 1) {                         // W - V = P_0 + P_1
 #pragma unroll
             for (int h2 = 0; h2 < RS; ++h2) {
                 if (h2 == h) continue;                  // uniform
@@ -433,91 +565,38 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 }
             }
         }
-        // vtilde = T W
-        floatx4 Vx[NCT];
+        // vtilde = T V + T (W - V)
         {
             frag Wb[KSC];
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) Wb[ks] = SL::from_acc(P, ks);
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) Vx[tc] = zero4();
-#pragma unroll
             for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
                 for (int tc = 0; tc < NCT; ++tc) Vx[tc] = Tr::mma(tA[ks][tc], Wb[ks], Vx[tc]);
         }
-        // independent of vtilde, run while T W is in flight:
-        // R_h = Diag(abar) Q S_h - Diag(b) Q M_h with the chunk-start states
-        floatx4 R[NCT];
-        {
-            floatx4 QSa[NCT], QMa[NCT];
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) { QSa[tc] = zero4(); QMa[tc] = zero4(); }
-#pragma unroll
-            for (int ks = 0; ks < KSH; ++ks) {
-                frag b[NCT];
-#pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) b[tc] = LdsA<Tr, LT::PK>::load(Ql, SL::perm(16 * tc + nn), ks0 + ks, g);
-#pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) {
-                    QSa[tc] = Tr::mma(b[tc], Sb[ks], QSa[tc]);
-                    QMa[tc] = Tr::mma(b[tc], Mb[ks], QMa[tc]);
-                }
-            }
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) {
-                const floatx4 ca = crow(MDN_COEF_ABAR, tc), cb = crow(MDN_COEF_B, tc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) R[tc][e] = ca[e] * QSa[tc][e] - cb[e] * QMa[tc][e];
-            }
-        }
-        // gS, gM of the contraction slots, K^T operands of the wave's rows
-        float gs[KSC][NSL], gm[KSC][NSL];
+        // S_h += K_h^T Diag(gS) vtilde;  M_h -= K_h^T Diag(gM) vtilde, one
+        // contraction step at a time (with the operands read just before
+        // where they were not read ahead)
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
-            SL::load_row(cf + MDN_COEF_GS * C, ks, g, gs[ks]);
-            SL::load_row(cf + MDN_COEF_GM * C, ks, g, gm[ks]);
+            if constexpr (!EARLY) read_update_operands(ks);
+#pragma unroll
+            for (int j = 0; j < NSL; ++j) gm[ks][j] = -gm[ks][j];
+            const frag VS = SL::from_acc_scaled(Vx, ks, gs[ks]);
+            const frag VM = SL::from_acc_scaled(Vx, ks, gm[ks]);
+#pragma unroll
+            for (int t = 0; t < NDH; ++t) {
+                XS[t] = Tr::mma(kT[ks][t], VS, XS[t]);
+                XM[t] = Tr::mma(kT[ks][t], VM, XM[t]);
+            }
+            if constexpr (!EARLY) __builtin_amdgcn_sched_barrier(0);
         }
-        frag kT[KSC][NDH];
+        // vtilde operands for the output waves (the row parts share the steps)
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-            for (int t = 0; t < NDH; ++t) kT[ks][t] = KtOperand<Tr, LT::PK>::load(Kl, td0 + t, ks, lane);
-        // S_h += K_h^T Diag(gS) vtilde;  M_h -= K_h^T Diag(gM) vtilde
-        frag Vb[KSC];
-        {
-            frag VS[KSC], VM[KSC];
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-#pragma unroll
-                for (int j = 0; j < NSL; ++j) gm[ks][j] = -gm[ks][j];
-                VS[ks] = SL::from_acc_scaled(Vx, ks, gs[ks]);
-                VM[ks] = SL::from_acc_scaled(Vx, ks, gm[ks]);
-                Vb[ks] = SL::from_acc(Vx, ks);
-            }
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-                for (int t = 0; t < NDH; ++t) {
-                    XS[t] = Tr::mma(kT[ks][t], VS[ks], XS[t]);
-                    XM[t] = Tr::mma(kT[ks][t], VM[ks], XM[t]);
-                }
-        }
-        // this wave's output rows: Op = R_h + Aqk vtilde (the partner's R follows);
-        // the other rows' R to the exchange; this wave's vtilde rows to the out tile
-#pragma unroll
-        for (int tc = 0; tc < NCT; ++tc) {
-            if (tc / NOT != h) {                        // uniform
-                if constexpr (RS > 1) xr[((ct * RS + h) * NOS + (tc < h * NOT ? tc : tc - NOT)) * 64 + lane] = R[tc];
-                continue;
-            }
-            floatx4 o = R[tc];
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) o = Tr::mma(LdsA<Tr, LT::PT>::load(Al, SL::perm(16 * tc + nn), ks, g), Vb[ks], o);
-            Op[tc] = o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ov[(SL::perm(16 * tc + 4 * g) + e) * OW + 16 * ct + nn] = Tr::from_f(Vx[tc][e]);
-        }
+            if (ks % RS == h) vb[(ct * KSC + ks) * 64 + lane] = SL::from_acc(Vx, ks);
+        state_operands();                               // of the next chunk
     };
 
     if constexpr (NBUF == 2) {
@@ -528,9 +607,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     } else {
         for (int64_t n = 0; n < NT; ++n) chunk(stA);
     }
-    lds_barrier();                                      // E1: R of the last chunk visible
-    if (NT > 0) finish_output();
-    lds_barrier();                                      // E2: O of the last chunk in the out tile
+    lds_barrier();                                      // E1
+    lds_barrier();                                      // E2
 
 #pragma unroll
     for (int t = 0; t < NDH; ++t)
@@ -542,10 +620,10 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         }
     };
     if constexpr (RS == 1) {
-        compute(std::integral_constant<int, 0>{});
+        chain(std::integral_constant<int, 0>{});
     } else {
-        if (cw % RS == 0) compute(std::integral_constant<int, 0>{});
-        else compute(std::integral_constant<int, 1>{});
+        if (cw % RS == 0) chain(std::integral_constant<int, 0>{});
+        else chain(std::integral_constant<int, 1>{});
     }
 }
 

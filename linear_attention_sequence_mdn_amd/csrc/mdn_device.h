@@ -101,6 +101,11 @@ template <> struct Slots<TraitsBf16> {
         f.u = uint4{0u, 0u, 0u, 0u};
         return f.v;
     }
+    // element e of accumulator tile t, read back from the B operands that
+    // from_acc built from the whole column
+    static __device__ __forceinline__ __bf16 acc_elem(const bf16x8* b, int t, int e) {
+        return b[t >> 1][4 * (t & 1) + e];
+    }
     // the per-slot factors p[row(ks, g, j)], j = 0..7, of a row vector p
     // (16-byte aligned): two 16-byte reads
     static __device__ __forceinline__ void load_row(const float* p, int ks, int g, float (&out)[NSLOT]) {
@@ -125,6 +130,7 @@ template <> struct Slots<TraitsF32> {
         return acc[ks >> 2][ks & 3] * s[0];
     }
     static __device__ __forceinline__ float zero() { return 0.f; }
+    static __device__ __forceinline__ float acc_elem(const float* b, int t, int e) { return b[4 * t + e]; }
     static __device__ __forceinline__ void load_row(const float* p, int ks, int g, float (&out)[NSLOT]) {
         out[0] = p[row(ks, g, 0)];
     }
