@@ -192,7 +192,7 @@ __device__ __forceinline__ void stage_chunk(int lw, uint32_t buf, const E* __res
                                             const E* __restrict__ Aqk, const float* __restrict__ coef,
                                             size_t rowbase, int valid, size_t tile, int col0, int lane)
 {
-    static_assert(NLD == 2 || NLD == 4, "two or four loader waves");
+    static_assert(NLD == 4, "four loader waves");
     constexpr unsigned RB = D * LT::ES;              // bytes per K/Q/V row
     const unsigned vlast = (unsigned)valid - 1;
     auto seq_row = [&](unsigned r) { return (r < vlast ? r : vlast) * RB; };
@@ -202,22 +202,15 @@ __device__ __forceinline__ void stage_chunk(int lw, uint32_t buf, const E* __res
         constexpr int NH = NLD / 2, RPL = C / NH;    // loaders per matrix, rows per loader
         const bool isq = lw >= NH;
         const int part = lw % NH;
-        dma_tile<RPL, LT::PK>(buf + (isq ? LT::Q0 : LT::K0), reinterpret_cast<const char*>((isq ? q : k) + rowbase * D),
-                              seq_row, lane, part * RPL);
-    } else if constexpr (NLD == 2) {
-        if (lw == 0) {
-            dma_tile<C, LT::PT>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
-            dma_plain<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
-                                 cf_row, lane);
-        } else {
-            dma_tile<C, LT::PT>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
-            dma_plain<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), seq_row, lane);
-        }
+        if (isq)      // Q is read only by the loader waves: swizzle key 1
+            dma_tile<RPL, LT::PK, 1>(buf + LT::Q0, reinterpret_cast<const char*>(q + rowbase * D), seq_row, lane, part * RPL);
+        else
+            dma_tile<RPL, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rowbase * D), seq_row, lane, part * RPL);
     } else {
         if (lw == 0)
             dma_tile<C, LT::PT>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
         else if (lw == 1)
-            dma_tile<C, LT::PT>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
+            dma_tile<C, LT::PT, 1>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
         else if (lw == 2)
             dma_plain<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), seq_row, lane);
         else
@@ -226,9 +219,15 @@ __device__ __forceinline__ void stage_chunk(int lw, uint32_t buf, const E* __res
     }
 }
 
-// Copy an out tile (C rows x 16*NCOL elements in LDS) to rows [0, valid) of
-// a row-major [.., D] output, by one wave; `dst` points at the chunk's first
-// row.  Every LDS read is issued before the first store.
+// Row r of an out tile is stored at row out_row(r): the accumulator rows a
+// lane group writes with one 2-byte store (rows 8 apart) then fall in
+// different LDS banks.  The map is its own inverse.
+__device__ __forceinline__ int out_row(int r) { return r ^ ((r >> 3) & 3); }
+
+// Copy an out tile (C rows x 16*NCOL elements in LDS, rows placed by
+// out_row) to rows [0, valid) of a row-major [.., D] output, by one wave;
+// `dst` points at the chunk's first row.  Every LDS read is issued before
+// the first store.
 template <typename LT, typename E, int D, int C>
 __device__ __forceinline__ void copy_out(const char* tile, E* __restrict__ dst, int valid, int col0, int lane)
 {
@@ -243,7 +242,7 @@ __device__ __forceinline__ void copy_out(const char* tile, E* __restrict__ dst, 
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int s = i * 64 + lane;
-        const int r = s / LT::PV, p = s % LT::PV;
+        const int r = out_row(s / LT::PV), p = s % LT::PV;
         if ((NP % 64 == 0 || s < NP) && r < valid)
             *reinterpret_cast<uint4*>(dst + (size_t)r * D + col0 + p * EPS) = val[i];
     }
@@ -336,7 +335,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             const float* cf = reinterpret_cast<const float*>(cur + LT::CF0);
             frag qa[KSD];
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) qa[ks] = LdsA<Tr, LT::PK>::load(Ql, SL::perm(16 * tc + nn), ks, g);
+            for (int ks = 0; ks < KSD; ++ks) qa[ks] = LdsA<Tr, LT::PK, 1>::load(Ql, SL::perm(16 * tc + nn), ks, g);
             const floatx4 ca = crow(cf, MDN_COEF_ABAR, tc), cb = crow(cf, MDN_COEF_B, tc);
 #pragma unroll
             for (int i = 0; i < NOC; ++i) {
@@ -358,7 +357,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             const char* Al = cur + LT::A0;
             frag aa[KSC];
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) aa[ks] = LdsA<Tr, LT::PT>::load(Al, SL::perm(16 * tc + nn), ks, g);
+            for (int ks = 0; ks < KSC; ++ks) aa[ks] = LdsA<Tr, LT::PT, 1>::load(Al, SL::perm(16 * tc + nn), ks, g);
 #pragma unroll
             for (int i = 0; i < NOC; ++i) {
                 const int oct = oc0 + i * OCS;
@@ -372,8 +371,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 const int r0 = SL::perm(16 * tc + 4 * g), c = 16 * oct + nn;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    oo[(r0 + e) * OW + c] = Tr::from_f(o[e]);
-                    ov[(r0 + e) * OW + c] = SL::acc_elem(vf, tc, e);
+                    oo[out_row(r0 + e) * OW + c] = Tr::from_f(o[e]);
+                    ov[out_row(r0 + e) * OW + c] = SL::acc_elem(vf, tc, e);
                 }
             }
         };

@@ -22,36 +22,44 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Swizzle key of row r for rows of P 16-byte pieces: the 16 rows an operand
-// read touches (perm of 16 consecutive accumulator rows, or the 4 x 4
-// row/column pattern of the transpose read) get distinct keys.
-template <int P>
+// Swizzle key of row r for rows of P 16-byte pieces.  Key 0 gives the 16
+// rows an operand read touches (perm of 16 consecutive accumulator rows, or
+// the 4 x 4 row/column pattern of the transpose read) distinct keys, and
+// does not depend on the bit of the row that tells even from odd row tiles,
+// so the reads of all row tiles share their lane addresses up to a constant.
+// Key 1 was chosen by measuring bank conflicts on gfx950: with it the
+// 16-byte operand reads of 16 rows perm(16t + i) are conflict-free, where
+// key 0 measures two-way conflicts; it costs address registers, so it is
+// used for the tiles that only waves with registers to spare read.
+template <int P, int KEY = 0>
 __device__ __forceinline__ int swz_key(int r) {
-    return ((r & 3) * (P / 4)) | ((r >> 3) & (P / 4 - 1));
+    static_assert(P >= 4 && (P & (P - 1)) == 0, "rows of 4, 8, 16, ... pieces");
+    if constexpr (KEY == 0) return ((r & 3) * (P / 4)) | ((r >> 3) & (P / 4 - 1));
+    else return ((r & 3) * (P / 4)) ^ ((r >> 2) & (P / 2 - 1));
 }
 
 // byte offset of (row r, byte b) in a row of P 16-byte pieces; piece p of
 // row r is stored at piece p ^ key(r)
-template <int P>
+template <int P, int KEY = 0>
 __device__ __forceinline__ int swz(int r, int b) {
-    return r * P * 16 + ((((b >> 4) ^ swz_key<P>(r))) << 4) + (b & 15);
+    return r * P * 16 + ((((b >> 4) ^ swz_key<P, KEY>(r))) << 4) + (b & 15);
 }
 
 // A operand of a product whose B operand comes from accumulators (slot map),
 // from a swizzled LDS tile whose rows hold the contraction index.
-template <typename Tr, int P> struct LdsA;
-template <int P> struct LdsA<TraitsBf16, P> {
+template <typename Tr, int P, int KEY = 0> struct LdsA;
+template <int P, int KEY> struct LdsA<TraitsBf16, P, KEY> {
     // slots of lane group g are the contiguous columns 32ks + 8g .. +7
     static __device__ __forceinline__ bf16x8 load(const char* tile, int row, int ks, int g) {
         union { uint4 u; bf16x8 v; } f;
-        f.u = *reinterpret_cast<const uint4*>(tile + swz<P>(row, 2 * (32 * ks + 8 * g)));
+        f.u = *reinterpret_cast<const uint4*>(tile + swz<P, KEY>(row, 2 * (32 * ks + 8 * g)));
         return f.v;
     }
 };
-template <int P> struct LdsA<TraitsF32, P> {
+template <int P, int KEY> struct LdsA<TraitsF32, P, KEY> {
     static __device__ __forceinline__ float load(const char* tile, int row, int ks, int g) {
         const int c = 16 * (ks >> 2) + 4 * g + (ks & 3);
-        return *reinterpret_cast<const float*>(tile + swz<P>(row, 4 * c));
+        return *reinterpret_cast<const float*>(tile + swz<P, KEY>(row, 4 * c));
     }
 };
 
@@ -62,7 +70,7 @@ template <int P> struct LdsA<TraitsF32, P> {
 // and physical piece l%P, so its source offset is a per-lane constant plus a
 // per-instruction constant.  `rowoff(r)` gives the byte offset of global row
 // r relative to `base`.
-template <int R, int P, typename RowOff>
+template <int R, int P, int KEY = 0, typename RowOff>
 __device__ __forceinline__ void dma_tile(uint32_t dst, const char* __restrict__ base, RowOff rowoff, int lane,
                                          int r0 = 0)
 {
@@ -75,7 +83,7 @@ __device__ __forceinline__ void dma_tile(uint32_t dst, const char* __restrict__ 
     for (int i = 0; i < NI; ++i) {
         const unsigned rl = i * RPI + lr;             // row within the copied range
         const unsigned r = (unsigned)r0 + rl;
-        const unsigned p = lp ^ (unsigned)swz_key<P>((int)r);
+        const unsigned p = lp ^ (unsigned)swz_key<P, KEY>((int)r);
         if (R * P % 64 == 0 || rl < (unsigned)R)
             __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(uintptr_t)(d0 + i * 1024), 16, 0, 0);
     }
