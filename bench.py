@@ -17,6 +17,8 @@ The same run also reports, each measured live with HIP events:
     of the dominant kernel;
   * the decode workload (B=256, H=16, d=128, 128 consecutive ``mdn_step``
     calls, median of 5 repetitions) as GB/s of algorithmic HBM traffic;
+  * the gate pre-operation with the query correction (``mdn_gates``) on the
+    400M-layer shape, as GB/s of algorithmic HBM traffic;
   * the fp64 CPU oracle on a bounded sample of the chunk workload.
 Prints ONE JSON line.
 """
@@ -50,6 +52,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-gates", action="store_true")
     p.add_argument("--no-chunk", action="store_true")
     p.add_argument("--decode-reps", type=int, default=5)
     p.add_argument("--decode-steps", type=int, default=128)
@@ -229,6 +232,38 @@ def decode_bench(args, torch, mdn, inputs):
                          "source_sha": sha}}
 
 
+def gates_bench(args, torch, mdn, inputs):
+    """Gate pre-operation with the query correction on the 400M-layer shape
+    (B8 H8 T4096, dk = 128, bf16): GB/s of algorithmic traffic."""
+    B, H, T, d = 8, 8, 4096, 128
+    g = inputs.make_gate_inputs(B, H, T, d, dtype="bf16", seed=1)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x, a, b, ml, dd = f(g.x), f(g.a), f(g.b), f(g.mu_log), f(g.d)
+    q, k = f(g.q).to(torch.bfloat16), f(g.k).to(torch.bfloat16)
+    outs = tuple(torch.empty((B, H, T), dtype=torch.float32, device="cuda") for _ in range(4))
+    qo = torch.empty_like(q)
+    run = lambda: mdn.gates(x, a, b, ml, q=q, k=k, d=dd, q_out=qo, out=outs)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    reps = 50
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    # per token-head: four fp32 inputs and four fp32 outputs, q and k read, q' written
+    bytes_call = B * H * T * (8 * 4 + 3 * d * 2)
+    gbs = bytes_call / (ms / 1e3) / 1e9
+    return {"metric": "gate pre-op GB/s", "value": gbs, "unit": "GB/s",
+            "workload": f"gates + query correction B{B} H{H} T{T} d{d} bf16", "ms_per_call": ms,
+            "alg_bytes_per_call": bytes_call,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "kernel": "mdn_gates_kernel"}}
+
+
 def cpu_baseline(args, x):
     """The fp64 oracle, untuned, on the chunk workload: the whole workload
     when it takes less than ``--cpu-seconds`` (repeated to fill that time,
@@ -304,6 +339,8 @@ def main():
                     "kernels": ch["kernels"], "roofline": ch["roofline"], "outputs_finite": ch["finite"]})
     if not args.no_decode:
         out["decode"] = decode_bench(args, torch, mdn, inputs)
+    if not args.no_gates:
+        out["gates"] = gates_bench(args, torch, mdn, inputs)
     if ch is not None and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, ch["x"])
     try:

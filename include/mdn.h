@@ -172,13 +172,42 @@ int mdn_chunk_coef(int64_t B, int64_t H, int64_t T, int C,
                    const float* alpha, const float* mu, const float* beta, const float* eta,
                    float* coef, float* gamma, void* stream);
 
+/* Gate pre-operation and query correction: the elementwise step between a
+ * layer's projections and the recurrence (summary, steps 6 and 7; article,
+ * sections 5 and 8).  For every (b, h, t):
+ *   eta   = tanh(x) + 1
+ *   theta = arctan(s * eta),  alpha_max = cos^2 theta,  beta_max = sin^2 theta
+ *   alpha = alpha_max * sigmoid(a),  beta = beta_max * sigmoid(b)
+ *           (so alpha + beta <= 1: the stable-gating constraint)
+ *   mu    = exp(clamp(mu_log, mu_log_min, 0))
+ * and, when q_out is not NULL, the output correction of the query
+ *   q_out[b][h][t][:] = q[b][h][t][:] - d[h] * k[b][h][t][:]
+ * in fp32, rounded to dtype (round to nearest even for bf16).
+ *   x, a, b, mu_log        [B][H][T] fp32 in (finite).
+ *   alpha, mu, beta, eta   [B][H][T] fp32 out; they must not overlap each
+ *                          other or any input.
+ *   s                      scale inside arctan: finite and > 0 (1 in the
+ *                          workloads here).
+ *   mu_log_min             lower clamp of log mu: finite and <= 0 (-2 on the
+ *                          pages).
+ *   q, k                   [B][H][T][dk] (dtype) in, d [H] fp32 in, q_out
+ *                          [B][H][T][dk] (dtype) out; either all four are
+ *                          NULL (no correction) or none.  q_out may be
+ *                          exactly q (in place); any other overlap is
+ *                          MDN_ERR_ALIAS.  dk in {16, 32, 64, 128}.
+ * A bad s or mu_log_min returns MDN_ERR_BAD_SHAPE. */
+int mdn_gates(int64_t B, int64_t H, int64_t T, int dk, int dtype, float s, float mu_log_min,
+              const float* x, const float* a, const float* b, const float* mu_log,
+              float* alpha, float* mu, float* beta, float* eta,
+              const void* q, const void* k, const float* d, void* q_out, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mdn_status_string(int status);
 
 /* ABI revision of this header (incremented on any signature change). */
 int mdn_abi_version(void);
 
-#define MDN_ABI_VERSION 2
+#define MDN_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
         -> (O, S_T, M_T, Vtilde)
     step(q, k, v, alpha, mu, beta, eta, S, M) -> o   (S, M updated in place)
     chunk_coef(alpha, mu, beta, eta, C) -> (coef, gamma)
+    gates(x, a, b, mu_log, s=1.0, mu_log_min=-2.0, q=None, k=None, d=None)
+        -> (alpha, mu, beta, eta) [+ q_out]
     chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype) -> int
 """
 from __future__ import annotations
@@ -58,6 +60,8 @@ def lib():
         L.mdn_step.restype = i32
         L.mdn_chunk_coef.argtypes = [i64, i64, i64, i32] + [vp] * 6 + [vp]
         L.mdn_chunk_coef.restype = i32
+        L.mdn_gates.argtypes = [i64, i64, i64, i32, i32, ctypes.c_float, ctypes.c_float] + [vp] * 12 + [vp]
+        L.mdn_gates.restype = i32
         L.mdn_status_string.argtypes = [i32]
         L.mdn_status_string.restype = ctypes.c_char_p
         L.mdn_abi_version.argtypes = []
@@ -227,3 +231,38 @@ def chunk_coef(alpha, mu, beta, eta, C, *, with_gamma=True, stream=None):
                               _ptr(coef), _ptr(gamma), _stream(stream))
     _check(st, "mdn_chunk_coef")
     return coef, gamma
+
+
+def gates(x, a, b, mu_log, *, s=1.0, mu_log_min=-2.0, q=None, k=None, d=None, q_out=None,
+          out=None, stream=None):
+    """Gate pre-operation: (alpha, mu, beta, eta) from the projection outputs
+    x, a, b, mu_log ([B,H,T] fp32).  With q, k ([B,H,T,dk], bf16 or fp32) and
+    d ([H] fp32) also the query correction q - d k, returned as a fifth
+    tensor (``q_out`` may be given, and may be ``q`` itself).  ``out`` may be
+    a tuple of four preallocated [B,H,T] fp32 tensors."""
+    torch = _torch()
+    B, H, T = x.shape
+    dev = x.device
+    for name, t in (("x", x), ("a", a), ("b", b), ("mu_log", mu_log)):
+        _need(t, name, torch.float32, (B, H, T), dev)
+    corr = q is not None or k is not None or d is not None
+    dk, dt = 16, MDN_F32
+    if corr:
+        if q is None or k is None or d is None:
+            raise ValueError("the query correction needs q, k and d")
+        dk = q.shape[-1]
+        dt = _dtype_code(q)
+        _need(q, "q", q.dtype, (B, H, T, dk), dev)
+        _need(k, "k", q.dtype, (B, H, T, dk), dev)
+        _need(d, "d", torch.float32, (H,), dev)
+        if q_out is None:
+            q_out = torch.empty_like(q)
+        _need(q_out, "q_out", q.dtype, (B, H, T, dk), dev)
+    if out is None:
+        out = tuple(torch.empty((B, H, T), dtype=torch.float32, device=dev) for _ in range(4))
+    for name, t in zip(("alpha", "mu", "beta", "eta"), out):
+        _need(t, name, torch.float32, (B, H, T), dev)
+    _check(lib().mdn_gates(B, H, T, dk, dt, float(s), float(mu_log_min),
+                           _ptr(x), _ptr(a), _ptr(b), _ptr(mu_log), *[_ptr(t) for t in out],
+                           _ptr(q), _ptr(k), _ptr(d), _ptr(q_out), _stream(stream)), "mdn_gates")
+    return (*out, q_out) if corr else tuple(out)

@@ -7,6 +7,7 @@
 // handed to the launchers in mdn_step.hip / mdn_chunk.hip.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -259,6 +260,48 @@ int mdn_step(int64_t B, int64_t H, int dk, int dv, int dtype,
     a.alpha = alpha; a.mu = mu; a.beta = beta; a.eta = eta;
     a.S = S; a.M = M; a.o = o; a.stream = stream;
     return hip_status(mdn::launch_step(a));
+}
+
+int mdn_gates(int64_t B, int64_t H, int64_t T, int dk, int dtype, float s, float mu_log_min,
+              const float* x, const float* a, const float* b, const float* mu_log,
+              float* alpha, float* mu, float* beta, float* eta,
+              const void* q, const void* k, const float* d, void* q_out, void* stream)
+{
+    int64_t BH, N;
+    if (B < 0 || H < 0 || T < 0 || !mul_ok(B, H, &BH) || !mul_ok(BH, T, &N)) return MDN_ERR_BAD_SHAPE;
+    if (!(s > 0.f) || !(s < INFINITY) || !(mu_log_min <= 0.f) || !(mu_log_min > -INFINITY)) return MDN_ERR_BAD_SHAPE;
+    if (dtype != MDN_F32 && dtype != MDN_BF16) return MDN_ERR_UNSUPPORTED;
+    const bool corr = q || k || d || q_out;
+    if (corr && (!q || !k || !d || !q_out)) return MDN_ERR_NULL_ARG;
+    if (corr && dk != 16 && dk != 32 && dk != 64 && dk != 128) return MDN_ERR_UNSUPPORTED;
+    if (N == 0) return MDN_OK;
+    if (!x || !a || !b || !mu_log || !alpha || !mu || !beta || !eta) return MDN_ERR_NULL_ARG;
+    const void* all[] = {x, a, b, mu_log, alpha, mu, beta, eta, q, k, d, q_out};
+    for (const void* p : all)
+        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
+    int64_t nq = 0;
+    if (corr && !mul_ok(N, (int64_t)dk, &nq)) return MDN_ERR_BAD_SHAPE;
+    const int64_t es = elem_size(dtype);
+    const Range ins[] = {range_of(x, N * 4), range_of(a, N * 4), range_of(b, N * 4), range_of(mu_log, N * 4),
+                         range_of(q, nq * es), range_of(k, nq * es), range_of(d, corr ? H * 4 : 0)};
+    const Range outs[] = {range_of(alpha, N * 4), range_of(mu, N * 4), range_of(beta, N * 4),
+                          range_of(eta, N * 4), range_of(q_out, nq * es)};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 7; ++j) {
+            if (!overlap(outs[i], ins[j])) continue;
+            if (i == 4 && j == 4 && q_out == q) continue;      // in-place correction
+            return MDN_ERR_ALIAS;
+        }
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(outs[i], outs[j])) return MDN_ERR_ALIAS;
+    }
+    mdn::GateArgs g;
+    memset(&g, 0, sizeof(g));
+    g.N = N; g.T = T; g.H = H; g.dk = dk; g.dtype = dtype; g.s = s; g.mu_log_min = mu_log_min;
+    g.x = x; g.a = a; g.b = b; g.mu_log = mu_log;
+    g.alpha = alpha; g.mu = mu; g.beta = beta; g.eta = eta;
+    g.q = q; g.k = k; g.d = d; g.qo = q_out; g.stream = stream;
+    return hip_status(mdn::launch_gates(g));
 }
 
 int mdn_chunk_coef(int64_t B, int64_t H, int64_t T, int C,

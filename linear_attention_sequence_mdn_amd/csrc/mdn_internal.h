@@ -36,7 +36,21 @@ struct ChunkArgs {
     void* stream;
 };
 
+struct GateArgs {
+    int64_t N, T, H;          // N = B*H*T tokens
+    int dk, dtype;
+    float s, mu_log_min;
+    const float *x, *a, *b, *mu_log;
+    float *alpha, *mu, *beta, *eta;
+    const void *q, *k;        // all NULL when the query correction is skipped
+    const float* d;
+    void* qo;
+    void* stream;
+};
+
 hipError_t launch_step(const StepArgs& a);
+// gate pre-operation and query correction
+hipError_t launch_gates(const GateArgs& g);
 // coefficient + intra-chunk stage (T, (QK^T) o Gamma, coefficients)
 hipError_t launch_chunk_intra(const ChunkArgs& a);
 // coefficient stage alone (diagnostic entry point)

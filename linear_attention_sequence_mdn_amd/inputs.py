@@ -164,3 +164,35 @@ def config_inputs(index: int) -> ChunkInputs:
     c = dict(CONFIGS[index])
     assert c.pop("kind") == "chunk"
     return make_chunk_inputs(**c)
+
+
+@dataclass
+class GateInputs:
+    """Raw projection outputs for the gate pre-operation: x, a, b, mu_log
+    ``[B, H, T]`` fp32, q, k ``[B, H, T, dk]`` (values exact in ``dtype``)
+    and one correction scalar d per head."""
+    x: np.ndarray
+    a: np.ndarray
+    b: np.ndarray
+    mu_log: np.ndarray
+    q: np.ndarray
+    k: np.ndarray
+    d: np.ndarray
+    dtype: str
+
+
+def make_gate_inputs(B, H, T, dk, dtype="bf16", seed=0, mu_range=(-3.0, 0.5)) -> GateInputs:
+    """Draw order: x, a, b ~ N(0, 1); mu_log ~ U[mu_range) (wide enough to
+    exercise both ends of the clamp); q, k ~ N(0, 1); d ~ U[0, 1) per head."""
+    rng = np.random.default_rng(seed)
+    f32 = lambda t: np.asarray(t, dtype=np.float32)
+    x = f32(rng.standard_normal((B, H, T)))
+    a = f32(rng.standard_normal((B, H, T)))
+    b = f32(rng.standard_normal((B, H, T)))
+    mu_log = f32(rng.uniform(mu_range[0], mu_range[1], (B, H, T)))
+    q = rng.standard_normal((B, H, T, dk))
+    k = rng.standard_normal((B, H, T, dk))
+    if dtype == "bf16":
+        q, k = round_to_bf16(q), round_to_bf16(k)
+    d = f32(rng.uniform(0.0, 1.0, H))
+    return GateInputs(x, a, b, mu_log, f32(q), f32(k), d, dtype)

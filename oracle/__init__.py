@@ -15,6 +15,8 @@ Contents
 * ``chunk_ref``: a NumPy fp64 restatement of the chunkwise algorithm (same
   summary, steps 2-5), used to pin the oracle and to give the per-chunk
   intermediates (coefficients, Gamma, T) a definition of their own.
+* ``gates_ref``: the gate pre-operation and query correction (same summary,
+  steps 6-7; article, sections 5 and 8) in NumPy fp64.
 
 Every function cites the passage it follows; the pins that tie the oracle to
 the pages live in ``tests/test_oracle_pins.py``.

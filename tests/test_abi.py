@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("mdn_chunk_fwd", "mdn_step", "mdn_chunk_fwd_workspace_bytes", "mdn_chunk_intra",
-              "mdn_chunk_inter", "mdn_chunk_coef", "mdn_status_string", "mdn_abi_version"):
+              "mdn_chunk_inter", "mdn_chunk_coef", "mdn_gates", "mdn_status_string", "mdn_abi_version"):
         assert n in names
 
 
@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.mdn_abi_version() == 2
+    assert L.mdn_abi_version() == 3
 
 
 def test_status_strings(L):
@@ -208,3 +208,28 @@ def test_stage_entry_points_validate(L):
                              ws, need, None) == NULL_ARG
     assert L.mdn_chunk_inter(1, 1, 64, 16, 16, 16, 0, q, k, v, a, m, b, e, s0, m0, O, ST, MT, O,
                              ws, need, None) == ALIAS
+
+
+def test_gates_validation(L):
+    p = addrs(12)
+    x, a, b, ml, al, mu, be, et, q, k, d, qo = p
+    f = ctypes.c_float
+    args = lambda **kw: [kw.get(n, v) for n, v in zip(
+        ("x", "a", "b", "ml", "al", "mu", "be", "et", "q", "k", "d", "qo"), p)]
+    call = lambda B=1, H=2, T=64, dk=16, dt=1, s=1.0, lo=-2.0, **kw: L.mdn_gates(
+        B, H, T, dk, dt, f(s), f(lo), *args(**kw), None)
+    assert call(T=-1) == BAD_SHAPE
+    assert call(s=0.0) == BAD_SHAPE and call(s=float("inf")) == BAD_SHAPE
+    assert call(lo=0.5) == BAD_SHAPE and call(lo=float("nan")) == BAD_SHAPE
+    assert call(dt=7) == UNSUPPORTED
+    assert call(dk=48) == UNSUPPORTED
+    assert call(d=None) == NULL_ARG                      # correction half given
+    assert call(T=0) == OK                               # nothing to do
+    assert call(x=None) == NULL_ARG
+    assert call(al=ctypes.c_void_p(al.value + 4)) == ALIGN
+    assert call(al=x) == ALIAS                           # output on an input
+    assert call(mu=al) == ALIAS                          # two outputs on each other
+    assert call(qo=k) == ALIAS
+    # no correction at all: q, k, d, q_out all NULL and dk is not checked
+    assert L.mdn_gates(1, 2, 0, 48, 1, f(1.0), f(-2.0), x, a, b, ml, al, mu, be, et,
+                       None, None, None, None, None) == OK
