@@ -257,11 +257,13 @@ def gates_bench(args, torch, mdn, inputs):
     # per token-head: four fp32 inputs and four fp32 outputs, q and k read, q' written
     bytes_call = B * H * T * (8 * 4 + 3 * d * 2)
     gbs = bytes_call / (ms / 1e3) / 1e9
+    sha = kernel_sources_sha(["mdn_gates.hip"])
+    traffic = load_traffic("traffic_mdn_gates_kernel_gates_400M_layer.md", sha)
     return {"metric": "gate pre-op GB/s", "value": gbs, "unit": "GB/s",
             "workload": f"gates + query correction B{B} H{H} T{T} d{d} bf16", "ms_per_call": ms,
-            "alg_bytes_per_call": bytes_call,
+            "alg_bytes_per_call": bytes_call, "source_sha": sha,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "kernel": "mdn_gates_kernel"}}
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "kernel": "mdn_gates_kernel"}}
 
 
 def cpu_baseline(args, x):
