@@ -19,6 +19,8 @@ The same run also reports, each measured live with HIP events:
     calls, median of 5 repetitions) as GB/s of algorithmic HBM traffic;
   * the gate pre-operation with the query correction (``mdn_gates``) on the
     400M-layer shape, as GB/s of algorithmic HBM traffic;
+  * a packed prefill batch (``mdn_chunk_fwd_varlen``): 32768 tokens of 8
+    heads in sequences of lengths ~U{1..4096}, as tokens/s;
   * the fp64 CPU oracle on a bounded sample of the chunk workload.
 Prints ONE JSON line.
 """
@@ -53,6 +55,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-gates", action="store_true")
+    p.add_argument("--no-varlen", action="store_true")
     p.add_argument("--no-chunk", action="store_true")
     p.add_argument("--decode-reps", type=int, default=5)
     p.add_argument("--decode-steps", type=int, default=128)
@@ -232,6 +235,34 @@ def decode_bench(args, torch, mdn, inputs):
                          "source_sha": sha}}
 
 
+def varlen_bench(args, torch, mdn, inputs):
+    """Packed prefill batch (``mdn_chunk_fwd_varlen``): 8 heads, d = 128,
+    C = 64, bf16, sequences with lengths ~ U{1..4096} packed to 32768 tokens
+    (the token count of the 400M-layer step), zero initial states.  Tokens/s
+    of the whole call (slot table, intra and inter kernels)."""
+    H, d, C, total = 8, 128, 64, 32768
+    lengths = inputs.serving_lengths(total, 1, 4096, seed=11)
+    x = inputs.make_varlen_inputs(H, lengths, d, C=C, dtype="bf16", seed=11)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, k, v = to(x.q).to(torch.bfloat16), to(x.k).to(torch.bfloat16), to(x.v).to(torch.bfloat16)
+    call = mdn.VarlenCall(q, k, v, to(x.alpha), to(x.mu), to(x.beta), to(x.eta), to(x.cu), None, None, C)
+    for _ in range(args.warmup):
+        call.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call.run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"metric": "packed prefill tokens/s", "value": total / (ms / 1e3), "unit": "tokens/s",
+            "ms_per_call": ms, "workload": f"packed prefill H{H} d{d} C{C} bf16, {len(lengths)} sequences "
+            f"with lengths ~U{{1..4096}} (seed 11) packed to {total} tokens, zero initial states",
+            "nseq": int(len(lengths)), "max_len": int(lengths.max()),
+            "fixed_layout_equivalent": "400M-layer step: the same token count in 8 sequences of 4096"}
+
+
 def gates_bench(args, torch, mdn, inputs):
     """Gate pre-operation with the query correction on the 400M-layer shape
     (B8 H8 T4096, dk = 128, bf16): GB/s of algorithmic traffic."""
@@ -343,6 +374,8 @@ def main():
         out["decode"] = decode_bench(args, torch, mdn, inputs)
     if not args.no_gates:
         out["gates"] = gates_bench(args, torch, mdn, inputs)
+    if not args.no_varlen:
+        out["varlen"] = varlen_bench(args, torch, mdn, inputs)
     if ch is not None and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, ch["x"])
     try:

@@ -149,6 +149,49 @@ int mdn_chunk_inter(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int 
                     void* O, float* S_T, float* M_T, void* Vtilde,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Packed variable-length batch: nseq independent sequences of any lengths,
+ * laid end to end along the token axis of every head, each starting from
+ * its own state.  Each sequence computes exactly what mdn_chunk_fwd computes
+ * for it alone (the recurrence of the summary, step 1, restarted at every
+ * sequence start; chunked as in steps 2-5, with chunks that begin at the
+ * sequence start and a short last chunk per sequence).  The packing is the
+ * usual serving layout and is not itself on the pages.
+ *   H, T        heads and packed length (sum of the sequence lengths);
+ *               T <= INT32_MAX.
+ *   nseq        number of sequences (0 is valid: nothing is written).
+ *   cu_seqlens  [nseq + 1] int32, DEVICE memory, 4-byte aligned: sequence i
+ *               is tokens [cu_seqlens[i], cu_seqlens[i+1]) of every head.
+ *               Required: cu_seqlens[0] == 0, nondecreasing, cu_seqlens[nseq]
+ *               == T.  This is not checked (the bounds live on the device);
+ *               the kernels clamp every bound into [0, T], so a table that
+ *               breaks it gives unspecified values but no access outside the
+ *               arguments.  Empty sequences are allowed: their S_T, M_T are
+ *               copies of S0, M0 (or zero).
+ *   dk, dv, C, dtype   as for mdn_chunk_fwd.
+ *   q, k        [H][T][dk] (dtype);  v, O, Vtilde  [H][T][dv] (dtype)
+ *   alpha, mu, beta, eta   [H][T] fp32
+ *   S0, M0      [nseq][H][dk][dv] fp32, or NULL for zero
+ *   S_T, M_T    [nseq][H][dk][dv] fp32 out (exact aliases of S0, M0 allowed)
+ *   workspace   at least mdn_chunk_fwd_varlen_workspace_bytes(); its layout
+ *               is that of mdn_chunk_fwd with NT = T / C + nseq tile slots per
+ *               head (sequence i owns slots from cu_seqlens[i] / C + i on),
+ *               followed by a [NT][2] int32 slot table and the [nseq] int32
+ *               dispatch order (sequences by length, longest first: their
+ *               inter-chunk carries start first), each on a 256-byte
+ *               boundary.
+ * Errors as for mdn_chunk_fwd; a NULL cu_seqlens with nseq > 0 is
+ * MDN_ERR_NULL_ARG, a misaligned one MDN_ERR_ALIGN. */
+size_t mdn_chunk_fwd_varlen_workspace_bytes(int64_t H, int64_t T, int64_t nseq,
+                                            int dk, int dv, int C, int dtype);
+
+int mdn_chunk_fwd_varlen(int64_t H, int64_t T, int64_t nseq, const int32_t* cu_seqlens,
+                         int dk, int dv, int C, int dtype,
+                         const void* q, const void* k, const void* v,
+                         const float* alpha, const float* mu, const float* beta, const float* eta,
+                         const float* S0, const float* M0,
+                         void* O, float* S_T, float* M_T, void* Vtilde,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* One recurrent decode step for every (batch, head), states updated in place
  * (article, section 6: generation runs the recurrence token by token).
  *   q, k        [B][H][dk] (dtype);  v [B][H][dv] (dtype)
@@ -207,7 +250,7 @@ const char* mdn_status_string(int status);
 /* ABI revision of this header (incremented on any signature change). */
 int mdn_abi_version(void);
 
-#define MDN_ABI_VERSION 3
+#define MDN_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

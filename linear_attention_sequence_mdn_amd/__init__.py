@@ -9,11 +9,14 @@ PyTorch fallback: if the library is missing, every call raises.
 Entry points (same names as the C ABI):
     chunk_fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64)
         -> (O, S_T, M_T, Vtilde)
+    chunk_fwd_varlen(q, k, v, alpha, mu, beta, eta, cu_seqlens, S0=None, M0=None, C=64)
+        -> (O, S_T, M_T, Vtilde)   packed variable-length batch
     step(q, k, v, alpha, mu, beta, eta, S, M) -> o   (S, M updated in place)
     chunk_coef(alpha, mu, beta, eta, C) -> (coef, gamma)
     gates(x, a, b, mu_log, s=1.0, mu_log_min=-2.0, q=None, k=None, d=None)
         -> (alpha, mu, beta, eta) [+ q_out]
     chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype) -> int
+    chunk_fwd_varlen_workspace_bytes(H, T, nseq, dk, dv, C, dtype) -> int
 """
 from __future__ import annotations
 
@@ -52,6 +55,10 @@ def lib():
         L.mdn_chunk_fwd_workspace_bytes.restype = sz
         L.mdn_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
         L.mdn_chunk_fwd.restype = i32
+        L.mdn_chunk_fwd_varlen_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32]
+        L.mdn_chunk_fwd_varlen_workspace_bytes.restype = sz
+        L.mdn_chunk_fwd_varlen.argtypes = [i64, i64, i64, vp, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
+        L.mdn_chunk_fwd_varlen.restype = i32
         L.mdn_chunk_intra.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 6 + [vp, sz, vp]
         L.mdn_chunk_intra.restype = i32
         L.mdn_chunk_inter.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
@@ -189,6 +196,79 @@ def chunk_fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, *,
     """
     call = ChunkCall(q, k, v, alpha, mu, beta, eta, S0, M0, C, out=out, S_T=S_T, M_T=M_T,
                      workspace=workspace)
+    return call.run(stream)
+
+
+def chunk_fwd_varlen_workspace_bytes(H, T, nseq, dk, dv, C, dtype) -> int:
+    n = lib().mdn_chunk_fwd_varlen_workspace_bytes(H, T, nseq, dk, dv, C, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise MdnError(3, "mdn_chunk_fwd_varlen_workspace_bytes")
+    return int(n)
+
+
+class VarlenCall:
+    """Validated, preallocated arguments of one packed variable-length
+    forward (``mdn_chunk_fwd_varlen``); ``run()`` allocates nothing."""
+
+    def __init__(self, q, k, v, alpha, mu, beta, eta, cu_seqlens, S0=None, M0=None, C=64, *,
+                 out=None, S_T=None, M_T=None, workspace=None):
+        torch = _torch()
+        H, T, dk = q.shape
+        dv = v.shape[-1]
+        self.dt = _dtype_code(q)
+        dev = q.device
+        nseq = cu_seqlens.numel() - 1
+        if cu_seqlens.dim() != 1 or nseq < 0:
+            raise ValueError("cu_seqlens must be a 1-D tensor of nseq + 1 sequence starts")
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,), dev)
+        _need(q, "q", q.dtype, (H, T, dk), dev)
+        _need(k, "k", q.dtype, (H, T, dk), dev)
+        _need(v, "v", q.dtype, (H, T, dv), dev)
+        for name, g in (("alpha", alpha), ("mu", mu), ("beta", beta), ("eta", eta)):
+            _need(g, name, torch.float32, (H, T), dev)
+        for name, s in (("S0", S0), ("M0", M0)):
+            if s is not None:
+                _need(s, name, torch.float32, (nseq, H, dk, dv), dev)
+        if out is None:
+            O = torch.empty((H, T, dv), dtype=q.dtype, device=dev)
+            Vt = torch.empty((H, T, dv), dtype=q.dtype, device=dev)
+        else:
+            O, Vt = out
+        if S_T is None:
+            S_T = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
+        if M_T is None:
+            M_T = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
+        nws = chunk_fwd_varlen_workspace_bytes(H, T, nseq, dk, dv, C, self.dt)
+        if workspace is None and nws > 0:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+        self.sizes = (H, T, nseq)
+        self.dims = (dk, dv, C, self.dt)
+        self.cu = cu_seqlens
+        self.tensors = (q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vt)
+        self.workspace = workspace
+        self.outputs = (O, S_T, M_T, Vt)
+        self._ptrs = [_ptr(t) for t in self.tensors]
+        self._ws = (_ptr(workspace) if workspace is not None else None,
+                    workspace.numel() if workspace is not None else 0)
+
+    def run(self, stream=None):
+        _check(lib().mdn_chunk_fwd_varlen(*self.sizes, _ptr(self.cu), *self.dims, *self._ptrs, *self._ws,
+                                          _stream(stream)), "mdn_chunk_fwd_varlen")
+        return self.outputs
+
+
+def chunk_fwd_varlen(q, k, v, alpha, mu, beta, eta, cu_seqlens, S0=None, M0=None, C=64, *,
+                     out=None, S_T=None, M_T=None, workspace=None, stream=None):
+    """Packed variable-length forward: returns (O, S_T, M_T, Vtilde).
+
+    q, k: [H,T,dk]; v: [H,T,dv] (bf16 or fp32); gates [H,T] fp32, where T is
+    the packed length; cu_seqlens: int32 [nseq+1] on the GPU, sequence i being
+    tokens [cu_seqlens[i], cu_seqlens[i+1]) (cu_seqlens[0] = 0, nondecreasing,
+    cu_seqlens[-1] = T); S0, M0 [nseq,H,dk,dv] fp32 or None.  O, Vtilde are
+    [H,T,dv]; S_T, M_T [nseq,H,dk,dv].
+    """
+    call = VarlenCall(q, k, v, alpha, mu, beta, eta, cu_seqlens, S0, M0, C, out=out, S_T=S_T,
+                      M_T=M_T, workspace=workspace)
     return call.run(stream)
 
 

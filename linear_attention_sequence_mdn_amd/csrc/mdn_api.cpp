@@ -62,6 +62,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct ChunkSizes {
     int64_t BH, NT, tok;         // tok = BH * T
     int64_t qk_elems, v_elems, g_elems, st_elems, tiles;
+    int64_t nseq;                // packed batch: number of sequences; -1 for the [B,H,T,.] layout
 };
 
 int chunk_sizes(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, ChunkSizes* s) {
@@ -76,7 +77,37 @@ int chunk_sizes(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, ChunkSiz
     if (!mul_ok(s->BH, s->NT, &s->tiles) || !mul_ok(s->tiles, (int64_t)C * C, &cc)) return MDN_ERR_BAD_SHAPE;
     // one workgroup per chunk tile / per column slab: keep the grids in range
     if (s->tiles > INT32_MAX || s->BH > INT32_MAX / 8) return MDN_ERR_BAD_SHAPE;
+    s->nseq = -1;
     return MDN_OK;
+}
+
+// Packed variable-length batch: H heads of T packed tokens, nseq sequences;
+// NT = T / C + nseq tile slots per head, states [nseq, H, dk, dv].
+int varlen_sizes(int64_t H, int64_t T, int64_t nseq, int dk, int dv, int C, ChunkSizes* s) {
+    if (H < 0 || T < 0 || nseq < 0 || dk <= 0 || dv <= 0 || C <= 0) return MDN_ERR_BAD_SHAPE;
+    if (T > INT32_MAX || nseq > INT32_MAX - 1) return MDN_ERR_BAD_SHAPE;   // int32 sequence bounds
+    s->BH = H;
+    if (!mul_ok(H, T, &s->tok)) return MDN_ERR_BAD_SHAPE;
+    s->NT = T / C + nseq;
+    if (!mul_ok(s->tok, dk, &s->qk_elems) || !mul_ok(s->tok, dv, &s->v_elems)) return MDN_ERR_BAD_SHAPE;
+    s->g_elems = s->tok;
+    int64_t dd, units, cc;
+    if (!mul_ok(nseq, H, &units) || !mul_ok((int64_t)dk, (int64_t)dv, &dd) || !mul_ok(units, dd, &s->st_elems))
+        return MDN_ERR_BAD_SHAPE;
+    if (!mul_ok(H, s->NT, &s->tiles) || !mul_ok(s->tiles, (int64_t)C * C, &cc)) return MDN_ERR_BAD_SHAPE;
+    if (s->tiles > INT32_MAX || units > INT32_MAX / 8) return MDN_ERR_BAD_SHAPE;
+    s->nseq = nseq;
+    return MDN_OK;
+}
+
+// workspace: T and Aqk per tile slot, the coefficients, and for a packed
+// batch the slot table and the dispatch order
+size_t workspace_of(const ChunkSizes& s, int C, int dtype) {
+    const size_t mat = align256((size_t)s.tiles * C * C * elem_size(dtype));
+    const size_t cf = align256((size_t)s.tiles * MDN_COEF_ROWS * C * sizeof(float));
+    const size_t tab = s.nseq >= 0 ? align256((size_t)s.NT * 2 * sizeof(int32_t)) : 0;
+    const size_t perm = s.nseq >= 0 ? align256((size_t)s.nseq * sizeof(int32_t)) : 0;
+    return 2 * mat + cf + tab + perm;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MDN_OK : MDN_ERR_HIP; }
@@ -107,15 +138,23 @@ size_t mdn_chunk_fwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int dk, in
     ChunkSizes s;
     if (chunk_sizes(B, H, T, dk, dv, C, &s) != MDN_OK) return (size_t)-1;
     if (!dims_supported_chunk(dtype, dk, dv, C)) return (size_t)-1;
-    const size_t mat = align256((size_t)s.tiles * C * C * elem_size(dtype));
-    const size_t cf = align256((size_t)s.tiles * MDN_COEF_ROWS * C * sizeof(float));
-    return 2 * mat + cf;
+    return workspace_of(s, C, dtype);
 }
 
-// Validation shared by mdn_chunk_fwd and its two stages.  `stage` is
-// 3 (both), 1 (intra only) or 2 (inter only); only the pointers a stage
-// reads or writes are required.
-static int chunk_prepare(int stage, int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+size_t mdn_chunk_fwd_varlen_workspace_bytes(int64_t H, int64_t T, int64_t nseq, int dk, int dv, int C, int dtype)
+{
+    ChunkSizes s;
+    if (varlen_sizes(H, T, nseq, dk, dv, C, &s) != MDN_OK) return (size_t)-1;
+    if (!dims_supported_chunk(dtype, dk, dv, C)) return (size_t)-1;
+    return workspace_of(s, C, dtype);
+}
+
+// Validation shared by mdn_chunk_fwd, its two stages and the packed-batch
+// forward (s.nseq >= 0, sequence bounds cu).  `stage` is 3 (both), 1 (intra
+// only) or 2 (inter only); only the pointers a stage reads or writes are
+// required.
+static int chunk_prepare(int stage, const ChunkSizes& s, int64_t T, int dk, int dv, int C, int dtype,
+                         const int32_t* cu,
                          const void* q, const void* k, const void* v,
                          const float* alpha, const float* mu, const float* beta, const float* eta,
                          const float* S0, const float* M0,
@@ -123,12 +162,12 @@ static int chunk_prepare(int stage, int64_t B, int64_t H, int64_t T, int dk, int
                          void* workspace, size_t workspace_bytes, void* stream,
                          mdn::ChunkArgs* a, bool* empty)
 {
-    ChunkSizes s;
-    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
-    if (st != MDN_OK) return st;
     if (!dims_supported_chunk(dtype, dk, dv, C)) return MDN_ERR_UNSUPPORTED;
-    *empty = s.BH == 0;
+    const bool packed = s.nseq >= 0;
+    *empty = s.BH == 0 || s.nseq == 0;
     if (*empty) return MDN_OK;
+    if (packed && !cu) return MDN_ERR_NULL_ARG;
+    if (packed && ((uintptr_t)cu & 3u) != 0) return MDN_ERR_ALIGN;
 
     const int64_t es = elem_size(dtype);
     const bool seq = s.tok > 0;
@@ -136,7 +175,7 @@ static int chunk_prepare(int stage, int64_t B, int64_t H, int64_t T, int dk, int
     if (inter && (!S_T || !M_T)) return MDN_ERR_NULL_ARG;
     if (seq && (!q || !k || !alpha || !mu || !beta || !eta)) return MDN_ERR_NULL_ARG;
     if (seq && inter && (!v || !O || !Vtilde)) return MDN_ERR_NULL_ARG;
-    const size_t need = mdn_chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype);
+    const size_t need = workspace_of(s, C, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return MDN_ERR_WORKSPACE;
 
     const void* all[] = {q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde, workspace};
@@ -151,10 +190,11 @@ static int chunk_prepare(int stage, int64_t B, int64_t H, int64_t T, int dk, int
     const Range rO = range_of(O, O ? s.v_elems * es : 0), rVt = range_of(Vtilde, Vtilde ? s.v_elems * es : 0);
     const Range rST = range_of(S_T, S_T ? s.st_elems * 4 : 0), rMT = range_of(M_T, M_T ? s.st_elems * 4 : 0);
     const Range rW = range_of(workspace, (int64_t)need);
-    const Range ins[] = {rq, rk, rv, ra, rm, rb, re, rs0, rm0};
+    const Range rcu = range_of(cu, packed ? (s.nseq + 1) * 4 : 0);
+    const Range ins[] = {rq, rk, rv, ra, rm, rb, re, rs0, rm0, rcu};
     const Range outs[] = {rO, rVt, rST, rMT, rW};
     for (int i = 0; i < 5; ++i) {
-        for (int j = 0; j < 9; ++j) {
+        for (int j = 0; j < 10; ++j) {
             if (!overlap(outs[i], ins[j])) continue;
             // the states may be updated in place, as exact aliases only
             if (i == 2 && j == 7 && (const void*)S_T == (const void*)S0) continue;
@@ -167,6 +207,8 @@ static int chunk_prepare(int stage, int64_t B, int64_t H, int64_t T, int dk, int
 
     memset(a, 0, sizeof(*a));
     a->BH = s.BH; a->T = T; a->NT = s.NT;
+    a->cu = packed ? cu : nullptr;
+    a->nseq = packed ? s.nseq : 0;
     a->dk = dk; a->dv = dv; a->C = C; a->dtype = dtype;
     a->q = q; a->k = k; a->v = v;
     a->alpha = alpha; a->mu = mu; a->beta = beta; a->eta = eta;
@@ -176,6 +218,10 @@ static int chunk_prepare(int stage, int64_t B, int64_t H, int64_t T, int dk, int
     a->Tmat = workspace;
     a->Aqk = workspace ? (char*)workspace + mat : nullptr;
     a->coef = workspace ? (float*)((char*)workspace + 2 * mat) : nullptr;
+    const size_t cfb = align256((size_t)s.tiles * MDN_COEF_ROWS * C * sizeof(float));
+    a->tab = packed ? (int32_t*)((char*)workspace + 2 * mat + cfb) : nullptr;
+    a->perm = packed ? (int32_t*)((char*)workspace + 2 * mat + cfb + align256((size_t)s.NT * 2 * sizeof(int32_t)))
+                     : nullptr;
     a->gamma = nullptr;
     a->stream = stream;
     return MDN_OK;
@@ -190,8 +236,11 @@ int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dt
 {
     mdn::ChunkArgs a;
     bool empty = false;
-    int st = chunk_prepare(3, B, H, T, dk, dv, C, dtype, q, k, v, alpha, mu, beta, eta, S0, M0,
-                           O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
+    ChunkSizes s;
+    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
+    if (st != MDN_OK) return st;
+    st = chunk_prepare(3, s, T, dk, dv, C, dtype, nullptr, q, k, v, alpha, mu, beta, eta, S0, M0,
+                       O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
     if (st != MDN_OK || empty) return st;
     if (T > 0) {
         st = hip_status(mdn::launch_chunk_intra(a));
@@ -207,9 +256,12 @@ int mdn_chunk_intra(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int 
 {
     mdn::ChunkArgs a;
     bool empty = false;
-    int st = chunk_prepare(1, B, H, T, dk, dv, C, dtype, q, k, nullptr, alpha, mu, beta, eta,
-                           nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                           workspace, workspace_bytes, stream, &a, &empty);
+    ChunkSizes s;
+    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
+    if (st != MDN_OK) return st;
+    st = chunk_prepare(1, s, T, dk, dv, C, dtype, nullptr, q, k, nullptr, alpha, mu, beta, eta,
+                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       workspace, workspace_bytes, stream, &a, &empty);
     if (st != MDN_OK || empty || T == 0) return st;
     return hip_status(mdn::launch_chunk_intra(a));
 }
@@ -223,9 +275,37 @@ int mdn_chunk_inter(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int 
 {
     mdn::ChunkArgs a;
     bool empty = false;
-    int st = chunk_prepare(2, B, H, T, dk, dv, C, dtype, q, k, v, alpha, mu, beta, eta, S0, M0,
-                           O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
+    ChunkSizes s;
+    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
+    if (st != MDN_OK) return st;
+    st = chunk_prepare(2, s, T, dk, dv, C, dtype, nullptr, q, k, v, alpha, mu, beta, eta, S0, M0,
+                       O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
     if (st != MDN_OK || empty) return st;
+    return hip_status(mdn::launch_chunk_inter(a));
+}
+
+int mdn_chunk_fwd_varlen(int64_t H, int64_t T, int64_t nseq, const int32_t* cu_seqlens,
+                         int dk, int dv, int C, int dtype,
+                         const void* q, const void* k, const void* v,
+                         const float* alpha, const float* mu, const float* beta, const float* eta,
+                         const float* S0, const float* M0,
+                         void* O, float* S_T, float* M_T, void* Vtilde,
+                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    mdn::ChunkArgs a;
+    bool empty = false;
+    ChunkSizes s;
+    int st = varlen_sizes(H, T, nseq, dk, dv, C, &s);
+    if (st != MDN_OK) return st;
+    st = chunk_prepare(3, s, T, dk, dv, C, dtype, cu_seqlens, q, k, v, alpha, mu, beta, eta, S0, M0,
+                       O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
+    if (st != MDN_OK || empty) return st;
+    st = hip_status(mdn::launch_varlen_prep(a));
+    if (st != MDN_OK) return st;
+    if (T > 0) {
+        st = hip_status(mdn::launch_chunk_intra(a));
+        if (st != MDN_OK) return st;
+    }
     return hip_status(mdn::launch_chunk_inter(a));
 }
 

@@ -260,7 +260,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                       typename Tr::elem* __restrict__ O,
                       float* __restrict__ ST, float* __restrict__ MT,
                       typename Tr::elem* __restrict__ Vt,
-                      int64_t T, int64_t NT, int BH)
+                      int64_t T, int64_t NT, int BH, const int32_t* __restrict__ cu,
+                      const int32_t* __restrict__ perm, int H)
 {
     using E = typename Tr::elem;
     using SL = Slots<Tr>;
@@ -286,10 +287,46 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, nn = lane & 15;
+    // the sequence this workgroup carries: its state index bh, column slab,
+    // first row, first tile slot and length
     int bh, slab;
-    xcd_head_map(blockIdx.x, SLABS, BH, bh, slab);
+    int64_t row0, tile0, len;
+    if (!cu) {
+        xcd_head_map(blockIdx.x, SLABS, BH, bh, slab);
+        row0 = (int64_t)bh * T;
+        tile0 = (int64_t)bh * NT;
+        len = T;
+    } else {
+        // Packed batch of BH = nseq * H units (sequence, head); states are
+        // [nseq, H, D, D].  Units are taken longest sequence first (perm):
+        // unit rank r = (sequence rank) * H + head.  Workgroups go to the
+        // XCDs round robin in launch order, so rank r runs on XCD r % 8, all
+        // its slabs there, and each XCD meets its units longest first.
+        int r;
+        if ((BH & 7) == 0) {
+            const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
+            r = (l / SLABS) * 8 + x;
+            slab = l % SLABS;
+        } else {
+            r = blockIdx.x / SLABS;
+            slab = blockIdx.x % SLABS;
+        }
+        const int64_t nseq = BH / H, h = r % H;
+        int64_t i = perm[r / H];
+        i = i < 0 ? 0 : (i >= nseq ? nseq - 1 : i);
+        bh = (int)(i * H + h);
+        // The bounds are clamped into [0, T] and ordered, which keeps every
+        // row and tile slot in range whatever the table holds.
+        int64_t c0 = cu[i], c1 = cu[i + 1];
+        c0 = c0 < 0 ? 0 : (c0 > T ? T : c0);
+        c1 = c1 < c0 ? c0 : (c1 > T ? T : c1);
+        row0 = h * T + c0;
+        tile0 = h * NT + c0 / C + i;
+        len = c1 - c0;
+    }
     const int col0 = slab * OW;
-    auto valid_of = [&](int64_t n) { return (int)((T - n * C) < C ? (T - n * C) : C); };
+    const int64_t NTu = (len + C - 1) / C;
+    auto valid_of = [&](int64_t n) { return (int)((len - n * C) < C ? (len - n * C) : C); };
     // coefficient of accumulator rows perm(16tc + 4g) + e, e = 0..3 (contiguous)
     auto crow = [&](const float* cf, int which, int tc) __attribute__((always_inline)) {
         return *reinterpret_cast<const floatx4*>(cf + which * C + SL::perm(16 * tc + 4 * g));
@@ -316,17 +353,17 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         constexpr int NOC = (NCOL + OCS - 1) / OCS;    // column tiles per output wave
         constexpr int tc = lw % NCT, oc0 = lw / NCT;
         auto issue = [&](uint32_t buf, int64_t m, int half) __attribute__((always_inline)) {
-            const size_t tile = (size_t)bh * NT + m;
-            const size_t rb = (size_t)bh * T + m * C;
+            const size_t tile = (size_t)(tile0 + m);
+            const size_t rb = (size_t)(row0 + m * C);
             const int vm = valid_of(m);
             if (half == 0) stage_chunk<LT, E, D, C, NLD, 0>(lw, buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
             else stage_chunk<LT, E, D, C, NLD, 1>(lw, buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
         };
         auto copy_outs = [&](int64_t m) __attribute__((always_inline)) {
             if (lw == 2)
-                copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + ((size_t)bh * T + m * C) * D, valid_of(m), col0, lane);
+                copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + (size_t)(row0 + m * C) * D, valid_of(m), col0, lane);
             else if (lw == 3)
-                copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + ((size_t)bh * T + m * C) * D, valid_of(m), col0, lane);
+                copy_out<LT, E, D, C>(reinterpret_cast<const char*>(ov), Vt + (size_t)(row0 + m * C) * D, valid_of(m), col0, lane);
         };
         floatx4 R[NOC];
         // R = Diag(abar) Q S - Diag(b) Q M of the chunk staged in `cur`, over all dk rows
@@ -378,12 +415,12 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         };
         const uint32_t aA = lds_addr(stA), aB = lds_addr(stB);
         if constexpr (NBUF == 2) {
-            if (NT > 0) {
+            if (NTu > 0) {
                 issue(aA, 0, 0);
                 issue(aA, 0, 1);
             }
             auto step = [&](uint32_t nxt, const char* cur, const char* prev, int64_t n) __attribute__((always_inline)) {
-                const bool more = n + 1 < NT;
+                const bool more = n + 1 < NTu;
                 __builtin_amdgcn_s_waitcnt(0);          // chunk n has landed (and earlier stores left)
                 lds_barrier();                          // B0
                 if (more) issue(nxt, n + 1, 0);
@@ -393,12 +430,12 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 if (more) issue(nxt, n + 1, 1);
                 if (n > 0) copy_outs(n - 1);
             };
-            for (int64_t n = 0; n < NT; n += 2) {
+            for (int64_t n = 0; n < NTu; n += 2) {
                 step(aB, stA, stB, n);
-                if (n + 1 < NT) step(aA, stB, stA, n + 1);
+                if (n + 1 < NTu) step(aA, stB, stA, n + 1);
             }
         } else {
-            for (int64_t n = 0; n < NT; ++n) {
+            for (int64_t n = 0; n < NTu; ++n) {
                 lds_barrier();                          // B0': the chain waves are done with chunk n-1
                 if (n > 0) out_o(stA);                  // chunk n-1, before its Aqk is overwritten
                 lds_barrier();                          // B0'': every read of chunk n-1 is done
@@ -412,9 +449,9 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             }
         }
         lds_barrier();                                  // E1: vtilde operands of the last chunk stored
-        if (NT > 0) out_o(NBUF == 2 && ((NT - 1) & 1) ? stB : stA);
+        if (NTu > 0) out_o(NBUF == 2 && ((NTu - 1) & 1) ? stB : stA);
         lds_barrier();                                  // E2: out tiles of the last chunk written
-        if (NT > 0) copy_outs(NT - 1);
+        if (NTu > 0) copy_outs(NTu - 1);
         };
         switch (__builtin_amdgcn_readfirstlane(wave - NW)) {
         case 0: loader(std::integral_constant<int, 0>{}); break;
@@ -599,12 +636,12 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     };
 
     if constexpr (NBUF == 2) {
-        for (int64_t n = 0; n < NT; n += 2) {
+        for (int64_t n = 0; n < NTu; n += 2) {
             chunk(stA);
-            if (n + 1 < NT) chunk(stB);
+            if (n + 1 < NTu) chunk(stB);
         }
     } else {
-        for (int64_t n = 0; n < NT; ++n) chunk(stA);
+        for (int64_t n = 0; n < NTu; ++n) chunk(stA);
     }
     lds_barrier();                                      // E1
     lds_barrier();                                      // E2
@@ -635,11 +672,12 @@ static hipError_t launch_inter_nw(const ChunkArgs& a)
     using E = typename Tr::elem;
     using P = InterPick<Tr, D, C>;
     constexpr int NCOL = P::NCOL, RS = P::RS, NBUF = P::NBUF, NLD = 4;
-    const int64_t grid = a.BH * (D / (16 * NCOL));
+    const int64_t units = a.cu ? a.BH * a.nseq : a.BH;   // (sequence, head) pairs of a packed batch
+    const int64_t grid = units * (D / (16 * NCOL));
     hipLaunchKernelGGL((mdn_inter_kernel<Tr, D, C, NCOL, RS, NBUF, NLD>), dim3((unsigned)grid), dim3(64 * (NCOL * RS + NLD)),
                        0, (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v,
                        (const E*)a.Tmat, (const E*)a.Aqk, a.coef, a.S0, a.M0,
-                       (E*)a.O, a.ST, a.MT, (E*)a.Vt, a.T, a.NT, (int)a.BH);
+                       (E*)a.O, a.ST, a.MT, (E*)a.Vt, a.T, a.NT, (int)units, a.cu, a.perm, (int)a.BH);
     return hipGetLastError();
 }
 
@@ -677,7 +715,7 @@ static hipError_t inter_dispatch(const ChunkArgs& a)
 
 hipError_t launch_chunk_inter(const ChunkArgs& a)
 {
-    if (a.BH == 0) return hipSuccess;
+    if (a.BH == 0 || (a.cu && a.nseq == 0)) return hipSuccess;
     return a.dtype == MDN_BF16 ? inter_dispatch<TraitsBf16>(a) : inter_dispatch<TraitsF32>(a);
 }
 

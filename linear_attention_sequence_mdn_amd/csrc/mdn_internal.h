@@ -33,6 +33,15 @@ struct ChunkArgs {
     void* Aqk;       // [BH*NT][C][C] elem
     float* coef;     // [BH*NT][8][C]
     float* gamma;    // [BH*NT][C][C] or nullptr (diagnostic only)
+    // Packed variable-length batch: nullptr for the [B,H,T,.] layout.  With
+    // cu set, BH is the head count H of the [H,T,.] packed layout, T the
+    // packed length, nseq the number of sequences, and NT = T / C + nseq the
+    // tile slots per head; tab holds (first row, rows) per slot and perm
+    // the sequences in dispatch order (longest first).
+    const int32_t* cu;   // [nseq + 1] sequence starts (device)
+    int64_t nseq;
+    int32_t* tab;        // [NT][2] (workspace)
+    int32_t* perm;       // [nseq] (workspace)
     void* stream;
 };
 
@@ -57,5 +66,7 @@ hipError_t launch_chunk_intra(const ChunkArgs& a);
 hipError_t launch_chunk_coef(const ChunkArgs& a);
 // sequential inter-chunk stage (vtilde, O, state carry)
 hipError_t launch_chunk_inter(const ChunkArgs& a);
+// slot table and dispatch order of a packed variable-length batch (a.cu set)
+hipError_t launch_varlen_prep(const ChunkArgs& a);
 
 }  // namespace mdn

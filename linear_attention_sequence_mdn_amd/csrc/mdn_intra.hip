@@ -169,7 +169,7 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
                       const typename Tr::elem* __restrict__ k,
                       const float* __restrict__ alpha, const float* __restrict__ mu,
                       const float* __restrict__ beta, const float* __restrict__ eta,
-                      int64_t T, int64_t NT,
+                      int64_t T, int64_t NT, const int2* __restrict__ tab,
                       typename Tr::elem* __restrict__ Tout,
                       typename Tr::elem* __restrict__ Aqk,
                       float* __restrict__ coef,
@@ -191,8 +191,23 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
 
     const int64_t tile = blockIdx.x;
     const int64_t bh = tile / NT, n = tile % NT;
-    const size_t rowbase = (size_t)(bh * T + n * C);
-    const int valid = (int)((T - n * C) < C ? (T - n * C) : C);
+    size_t rowbase;
+    int valid;
+    if (tab) {
+        // packed batch: slot n of head bh covers rows [first, first + rows)
+        // of the head's packed sequence; empty slots have no work.  Clamped,
+        // so that a malformed table can only give wrong values, never an
+        // access outside the head's rows.
+        const int2 e = tab[n];
+        const int64_t vmax = T < C ? T : C;
+        valid = (int)(e.y < 0 ? 0 : (e.y > vmax ? vmax : e.y));
+        if (valid == 0) return;
+        const int64_t f = e.x < 0 ? 0 : (e.x > T - valid ? T - valid : e.x);
+        rowbase = (size_t)(bh * T + f);
+    } else {
+        rowbase = (size_t)(bh * T + n * C);
+        valid = (int)((T - n * C) < C ? (T - n * C) : C);
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, nn = lane & 15;
@@ -476,7 +491,7 @@ static hipError_t launch_intra_t(const ChunkArgs& a)
     const int64_t tiles = a.BH * a.NT;
     hipLaunchKernelGGL((mdn_intra_kernel<Tr, DK, C, COEF_ONLY>), dim3((unsigned)tiles), dim3(256), 0,
                        (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k,
-                       a.alpha, a.mu, a.beta, a.eta, a.T, a.NT,
+                       a.alpha, a.mu, a.beta, a.eta, a.T, a.NT, reinterpret_cast<const int2*>(a.tab),
                        (E*)a.Tmat, (E*)a.Aqk, a.coef, a.gamma);
     return hipGetLastError();
 }
@@ -517,6 +532,84 @@ hipError_t launch_chunk_intra(const ChunkArgs& a)
 {
     if (a.BH * a.NT == 0) return hipSuccess;
     return a.dtype == MDN_BF16 ? intra_dispatch<TraitsBf16>(a) : intra_dispatch<TraitsF32>(a);
+}
+
+// Preparation of a packed variable-length batch, one thread per sequence.
+//
+// Slot table.  Sequence i (tokens [cu[i], cu[i+1]) of every head) owns the
+// slots [cu[i] / C + i, cu[i+1] / C + i + 1) of each head's NT = T / C + nseq
+// tile slots: its chunks first, then at most one empty slot.  For ordered
+// bounds these ranges tile [0, NT) and hold every chunk.  Thread i writes
+// sequence i's range, thread 0 also any slots before sequence 0's.  Entries
+// are (first row, rows), (0, 0) if empty.
+//
+// Dispatch order.  perm[r] is the sequence of rank r, lengths descending
+// (ties by index): the inter-chunk workgroups of long sequences start first,
+// so that the short ones fill in behind them.  Each thread ranks its
+// sequence against all others, reading the lengths through LDS in tiles.
+//
+// Every bound is clamped into [0, T] and ordered first, as the inter kernel
+// does, so a malformed cu gives wrong values, never an access out of range.
+__device__ __forceinline__ void seq_bounds(const int32_t* __restrict__ cu, int64_t i, int64_t T,
+                                           int64_t& c0, int64_t& c1)
+{
+    c0 = cu[i];
+    c1 = cu[i + 1];
+    c0 = c0 < 0 ? 0 : (c0 > T ? T : c0);
+    c1 = c1 < c0 ? c0 : (c1 > T ? T : c1);
+}
+
+__global__ __launch_bounds__(256)
+void mdn_varlen_prep_kernel(const int32_t* __restrict__ cu, int64_t nseq, int64_t T, int C, int64_t NT,
+                            int2* __restrict__ tab, int32_t* __restrict__ perm)
+{
+    constexpr int TILE = 2048;
+    __shared__ int lens[TILE];
+    const int tid = threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+    int li = 0;
+    if (i < nseq) {
+        int64_t c0, c1;
+        seq_bounds(cu, i, T, c0, c1);
+        li = (int)(c1 - c0);
+        int64_t cn = cu[i + 1];
+        cn = cn < 0 ? 0 : (cn > T ? T : cn);
+        const int64_t next = i + 1 < nseq ? cn / C + i + 1 : NT;
+        const int64_t base = c0 / C + i, nt = (c1 - c0 + C - 1) / C;
+        if (i == 0)
+            for (int64_t j = 0; j < base && j < NT; ++j) tab[j] = make_int2(0, 0);
+        for (int64_t j = base; j < next && j < NT; ++j) {
+            const int64_t n = j - base;
+            tab[j] = n < nt ? make_int2((int)(c0 + n * C), (int)((c1 - c0 - n * C) < C ? (c1 - c0 - n * C) : C))
+                            : make_int2(0, 0);
+        }
+    }
+    int64_t rank = 0;
+    for (int64_t t0 = 0; t0 < nseq; t0 += TILE) {
+        const int n = (int)(nseq - t0 < TILE ? nseq - t0 : TILE);
+        __syncthreads();
+        for (int j = tid; j < n; j += 256) {
+            int64_t c0, c1;
+            seq_bounds(cu, t0 + j, T, c0, c1);
+            lens[j] = (int)(c1 - c0);
+        }
+        __syncthreads();
+        if (i < nseq)
+            for (int j = 0; j < n; ++j) {
+                const int lj = lens[j];
+                rank += (lj > li) || (lj == li && t0 + j < i);
+            }
+    }
+    if (i < nseq) perm[rank] = (int32_t)i;
+}
+
+hipError_t launch_varlen_prep(const ChunkArgs& a)
+{
+    if (a.nseq == 0) return hipSuccess;
+    const int64_t blocks = (a.nseq + 255) / 256;
+    hipLaunchKernelGGL(mdn_varlen_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)a.stream,
+                       a.cu, a.nseq, a.T, a.C, a.NT, reinterpret_cast<int2*>(a.tab), a.perm);
+    return hipGetLastError();
 }
 
 hipError_t launch_chunk_coef(const ChunkArgs& a)

@@ -167,6 +167,61 @@ def config_inputs(index: int) -> ChunkInputs:
 
 
 @dataclass
+class VarlenInputs:
+    """A packed variable-length batch: sequence i is tokens [cu[i], cu[i+1])
+    of every head; per-sequence states are [nseq, H, dk, dv]."""
+    H: int
+    T: int                       # packed length = sum of lengths
+    dk: int
+    dv: int
+    C: int
+    dtype: str
+    lengths: np.ndarray          # int64 [nseq]
+    cu: np.ndarray               # int32 [nseq + 1]
+    q: np.ndarray                # float32 [H,T,dk]
+    k: np.ndarray
+    v: np.ndarray                # float32 [H,T,dv]
+    alpha: np.ndarray            # float32 [H,T]
+    mu: np.ndarray
+    beta: np.ndarray
+    eta: np.ndarray
+    S0: Optional[np.ndarray] = None   # float32 [nseq,H,dk,dv] or None (zero)
+    M0: Optional[np.ndarray] = None
+
+
+def serving_lengths(total, lo, hi, seed=0) -> np.ndarray:
+    """Sequence lengths ~ U{lo..hi} drawn until they sum to ``total`` (the
+    last one cut to fit): the length mix of a packed prefill batch."""
+    rng = np.random.default_rng(seed)
+    out, acc = [], 0
+    while acc < total:
+        n = int(min(rng.integers(lo, hi + 1), total - acc))
+        out.append(n)
+        acc += n
+    return np.asarray(out, dtype=np.int64)
+
+
+def make_varlen_inputs(H, lengths, dk, dv=None, C=64, dtype="bf16", seed=0,
+                       mu_range=(-1.0, 0.0), state_std=None) -> VarlenInputs:
+    """Packed batch with the chunk recipe above: q, k, v and gates drawn as
+    for one ``[1, H, sum(lengths)]`` workload, then the per-sequence initial
+    states (if ``state_std``) as ``[nseq, H, dk, dv]``."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    T = int(lengths.sum())
+    x = make_chunk_inputs(1, H, T, dk, dv, C=C, dtype=dtype, seed=seed, mu_range=mu_range)
+    dv = x.dv
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    S0 = M0 = None
+    if state_std is not None:
+        rng = np.random.default_rng(seed + 7919)
+        S0 = (rng.standard_normal((len(lengths), H, dk, dv)) * state_std).astype(np.float32)
+        M0 = (rng.standard_normal((len(lengths), H, dk, dv)) * state_std).astype(np.float32)
+    return VarlenInputs(H, T, dk, dv, C, dtype, lengths, cu, x.q[0], x.k[0], x.v[0],
+                        x.alpha[0], x.mu[0], x.beta[0], x.eta[0], S0, M0)
+
+
+@dataclass
 class GateInputs:
     """Raw projection outputs for the gate pre-operation: x, a, b, mu_log
     ``[B, H, T]`` fp32, q, k ``[B, H, T, dk]`` (values exact in ``dtype``)

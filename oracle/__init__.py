@@ -9,7 +9,8 @@ none of the method's arithmetic.
 Contents
 --------
 * ``fwd`` / ``step``: the token-by-token recurrence, in C (``mdn_oracle.c``),
-  fp64, OpenMP over heads.  This is the plain definition of what the chunkwise
+  fp64, OpenMP over heads.  ``fwd_varlen`` runs ``fwd`` per sequence of a
+  packed batch.  This is the plain definition of what the chunkwise
   forward and the decode step compute (MDN paper summary at paper.rainbus.top,
   method walk-through step 1; ijyty.com article on MDN, sections 3 and 6).
 * ``chunk_ref``: a NumPy fp64 restatement of the chunkwise algorithm (same
@@ -119,6 +120,44 @@ def fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None):
         m0p = M0.ctypes.data
     lib.mdn_oracle_fwd(BH, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu),
                        _ptr(beta), _ptr(eta), s0p, m0p, _ptr(O), _ptr(ST), _ptr(MT), _ptr(Vt))
+    return O, ST, MT, Vt
+
+
+def fwd_varlen(q, k, v, alpha, mu, beta, eta, cu, S0=None, M0=None):
+    """Packed variable-length forward in fp64: each sequence runs the
+    recurrence of :func:`fwd` on its own tokens from its own initial state.
+
+    q, k ``[H, T, dk]``; v ``[H, T, dv]``; gates ``[H, T]``; ``cu`` the
+    ``nseq + 1`` sequence starts (sequence i is tokens ``cu[i]:cu[i+1]`` of
+    every head); S0, M0 ``[nseq, H, dk, dv]`` or None (zero).  Returns
+    ``(O [H,T,dv], S_T [nseq,H,dk,dv], M_T, Vtilde [H,T,dv])``.
+
+    The recurrence is the MDN summary's (paper.rainbus.top, method
+    walk-through step 1); a sequence start resets the state to that
+    sequence's initial state, so no token of one sequence reaches another.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    alpha, mu, beta, eta = _f64(alpha), _f64(mu), _f64(beta), _f64(eta)
+    cu = np.asarray(cu, dtype=np.int64)
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    nseq = len(cu) - 1
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    O = np.zeros((H, T, dv))
+    Vt = np.zeros((H, T, dv))
+    ST = np.zeros((nseq, H, dk, dv))
+    MT = np.zeros((nseq, H, dk, dv))
+    for i in range(nseq):
+        a, b = int(cu[i]), int(cu[i + 1])
+        s0 = None if S0 is None else S0[i]
+        m0 = None if M0 is None else M0[i]
+        if a == b:
+            ST[i] = 0.0 if s0 is None else s0
+            MT[i] = 0.0 if m0 is None else m0
+            continue
+        o, st, mt, vt = fwd(q[:, a:b], k[:, a:b], v[:, a:b], alpha[:, a:b], mu[:, a:b],
+                            beta[:, a:b], eta[:, a:b], s0, m0)
+        O[:, a:b], Vt[:, a:b], ST[i], MT[i] = o, vt, st, mt
     return O, ST, MT, Vt
 
 

@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("mdn_chunk_fwd", "mdn_step", "mdn_chunk_fwd_workspace_bytes", "mdn_chunk_intra",
-              "mdn_chunk_inter", "mdn_chunk_coef", "mdn_gates", "mdn_status_string", "mdn_abi_version"):
+              "mdn_chunk_inter", "mdn_chunk_coef", "mdn_gates", "mdn_chunk_fwd_varlen",
+              "mdn_chunk_fwd_varlen_workspace_bytes", "mdn_status_string", "mdn_abi_version"):
         assert n in names
 
 
@@ -47,7 +48,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.mdn_abi_version() == 3
+    assert L.mdn_abi_version() == 4
 
 
 def test_status_strings(L):
@@ -233,3 +234,44 @@ def test_gates_validation(L):
     # no correction at all: q, k, d, q_out all NULL and dk is not checked
     assert L.mdn_gates(1, 2, 0, 48, 1, f(1.0), f(-2.0), x, a, b, ml, al, mu, be, et,
                        None, None, None, None, None) == OK
+
+
+def varlen_call(L, H=2, T=100, nseq=3, d=32, C=32, dt=1, cu=None, ptrs=None, ws_bytes=None):
+    p = addrs(14) if ptrs is None else ptrs
+    cu = ctypes.c_void_p(BASE - (1 << 20)) if cu is None else cu
+    n = L.mdn_chunk_fwd_varlen_workspace_bytes(H, T, nseq, d, d, C, dt) if ws_bytes is None else ws_bytes
+    return L.mdn_chunk_fwd_varlen(H, T, nseq, cu, d, d, C, dt, *p[:13], p[13], n, None)
+
+
+def test_varlen_workspace_bytes(L):
+    # tile slots T // C + nseq per head; T, Aqk (bf16), coefficients, the slot table, the order
+    H, T, nseq, d, C = 8, 32768, 19, 128, 64
+    slots = H * (T // C + nseq)
+    a256 = lambda x: (x + 255) // 256 * 256
+    expect = (2 * a256(slots * C * C * 2) + a256(slots * 8 * C * 4) + a256((T // C + nseq) * 8)
+              + a256(nseq * 4))
+    assert mdn.chunk_fwd_varlen_workspace_bytes(H, T, nseq, d, d, C, mdn.MDN_BF16) == expect
+    bad = ctypes.c_size_t(-1).value
+    assert L.mdn_chunk_fwd_varlen_workspace_bytes(1, 1 << 31, 1, 32, 32, 32, 1) == bad   # beyond int32
+    assert L.mdn_chunk_fwd_varlen_workspace_bytes(1, 64, -1, 32, 32, 32, 1) == bad
+    assert L.mdn_chunk_fwd_varlen_workspace_bytes(1, 64, 2, 48, 48, 32, 1) == bad
+
+
+def test_varlen_validation(L):
+    assert varlen_call(L, nseq=-1) == BAD_SHAPE
+    assert varlen_call(L, T=1 << 31) == BAD_SHAPE
+    assert varlen_call(L, d=48) == UNSUPPORTED
+    assert varlen_call(L, nseq=0, ptrs=[None] * 14, cu=ctypes.c_void_p(0)) == OK   # nothing to do
+    assert varlen_call(L, H=0, ptrs=[None] * 14) == OK
+    assert varlen_call(L, cu=ctypes.c_void_p(0)) == NULL_ARG
+    assert varlen_call(L, cu=ctypes.c_void_p(BASE - (1 << 20) + 2)) == ALIGN
+    p = addrs(14)
+    for i in (0, 1, 2, 3, 9, 10, 11, 12):
+        q = list(p)
+        q[i] = None
+        assert varlen_call(L, ptrs=q) == NULL_ARG, i
+    assert varlen_call(L, ws_bytes=1) == WORKSPACE
+    q = list(p)
+    q[9] = q[0]                                          # O on top of q
+    assert varlen_call(L, ptrs=q) == ALIAS
+    assert varlen_call(L, cu=p[13]) == ALIAS             # sequence bounds inside the workspace
