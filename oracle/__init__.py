@@ -10,7 +10,8 @@ Contents
 --------
 * ``fwd`` / ``step``: the token-by-token recurrence, in C (``mdn_oracle.c``),
   fp64, OpenMP over heads.  ``fwd_varlen`` runs ``fwd`` per sequence of a
-  packed batch.  This is the plain definition of what the chunkwise
+  packed batch.  ``bwd``: reverse mode of the same recurrence (C), the
+  gradients of every input for given output gradients.  This is the plain definition of what the chunkwise
   forward and the decode step compute (MDN paper summary at paper.rainbus.top,
   method walk-through step 1; ijyty.com article on MDN, sections 3 and 6).
 * ``chunk_ref``: a NumPy fp64 restatement of the chunkwise algorithm (same
@@ -58,6 +59,9 @@ def _load():
         lib.mdn_oracle_fwd.restype = None
         lib.mdn_oracle_step.argtypes = [L, L, L] + [d] * 7 + [d] * 4
         lib.mdn_oracle_step.restype = None
+        lib.mdn_oracle_bwd.argtypes = ([L, L, L, L] + [d] * 7 + [ctypes.c_void_p] * 2 + [d]
+                                       + [ctypes.c_void_p] * 2 + [d] * 9)
+        lib.mdn_oracle_bwd.restype = None
         lib.mdn_oracle_threads.argtypes = []
         lib.mdn_oracle_threads.restype = ctypes.c_int
         lib.mdn_oracle_set_threads.argtypes = [ctypes.c_int]
@@ -121,6 +125,45 @@ def fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None):
     lib.mdn_oracle_fwd(BH, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu),
                        _ptr(beta), _ptr(eta), s0p, m0p, _ptr(O), _ptr(ST), _ptr(MT), _ptr(Vt))
     return O, ST, MT, Vt
+
+
+def bwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, dO=None, dST=None, dMT=None):
+    """Gradients of L = sum(dO*O) + sum(dST*S_T) + sum(dMT*M_T) in fp64.
+
+    Same shapes as :func:`fwd`; dO like O, dST/dMT like S_T (None = zero).
+    Returns a dict with dq, dk, dv, dalpha, dmu, dbeta, deta, dS0, dM0 (the
+    gradient with respect to the initial states, zero or not).
+
+    Reverse mode of the recurrence of the MDN summary (paper.rainbus.top,
+    method walk-through step 1), one token at a time, last token first: the
+    chain rule applied to the four update equations (the C source lists each
+    term).  The states are replayed from checkpoints every 64 tokens.
+    """
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    alpha, mu, beta, eta = _f64(alpha), _f64(mu), _f64(beta), _f64(eta)
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    dO = np.zeros(lead + (T, dv)) if dO is None else _f64(np.broadcast_to(dO, lead + (T, dv)))
+    keep = []
+
+    def opt(x):
+        if x is None:
+            return None
+        a = _f64(np.broadcast_to(x, lead + (dk, dv)))
+        keep.append(a)
+        return a.ctypes.data
+
+    out = dict(dq=np.zeros(lead + (T, dk)), dk=np.zeros(lead + (T, dk)), dv=np.zeros(lead + (T, dv)),
+               dalpha=np.zeros(lead + (T,)), dmu=np.zeros(lead + (T,)), dbeta=np.zeros(lead + (T,)),
+               deta=np.zeros(lead + (T,)), dS0=np.zeros(lead + (dk, dv)), dM0=np.zeros(lead + (dk, dv)))
+    lib.mdn_oracle_bwd(BH, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu), _ptr(beta),
+                       _ptr(eta), opt(S0), opt(M0), _ptr(dO), opt(dST), opt(dMT),
+                       *(_ptr(out[n]) for n in ("dq", "dk", "dv", "dalpha", "dmu", "dbeta", "deta",
+                                                "dS0", "dM0")))
+    return out
 
 
 def fwd_varlen(q, k, v, alpha, mu, beta, eta, cu, S0=None, M0=None):
