@@ -186,3 +186,130 @@ def chunk_fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64):
     MT = np.stack([o[2] for o in outs]).reshape(lead + (dk, dv))
     Vt = np.stack([o[3] for o in outs]).reshape(lead + (T_len, dv))
     return O, ST, MT, Vt
+
+
+def chunk_bwd_head(q, k, v, alpha, mu, beta, eta, S0, M0, dO, dST, dMT, C):
+    """Chunkwise reverse mode of one head, fp64 (the gradients of
+    L = sum(dO*O) + sum(dST*S_T) + sum(dMT*M_T), like ``oracle.bwd``).
+
+    The pages give no backward; this is the chain rule applied to the chunk
+    equations of :func:`chunk_fwd_head` in the form
+    W = V - Diag(abar) K S + Diag(alpha b_prev) K M, Vtilde = T W (the same
+    numbers as U - Y S + Z M).  Three parts:
+
+    1. chunk-start states S[n], M[n] replayed forward from Vtilde (only the
+       state update, no T);
+    2. a reverse pass that carries dS, dM (adjoints of the chunk-end states)
+       to the chunk start:
+         dVt = Aqk^T dO + Diag(gS) K dS' - Diag(gM) K dM',   dW = T^T dVt,
+         dS  = abar_L dS' + Q^T Diag(abar) dO - K^T Diag(abar) dW,
+         dM  = mubar_L dM' - b_L dS' - Q^T Diag(b) dO + K^T Diag(alpha b_prev) dW;
+    3. per chunk, the gradients of Q, K, V and of the coefficients, then of
+       the gates through the coefficient definitions.  With
+       E[r,j] = abar_r/abar_j, F[j,i] = mubar_j/mubar_i, Psi = E Diag(beta) F
+       (so Gamma = Psi Diag(eta)) and b = E (beta mubar), the adjoints of
+       Gamma and b give
+         dbeta_j = Z_j = sum_{r>=j, i<=j} E[r,j] DPsi[r,i] F[j,i] + sum_{r>=j} E[r,j] Db_r mubar_j,
+         d Lambda_alpha_m += rowsum(DPsi o Psi)_m + Db_m b_m - beta_m Z_m,
+         d Lambda_mu_m    += beta_m Z_m - colsum(DPsi o Psi)_m,
+       and dalpha_s = sum_{r>=s} d Lambda_alpha_r / alpha_s (likewise mu),
+       where Lambda are the inclusive cumulative logs of the chunk.
+    Gates must be positive (the logs).  The last chunk may be shorter than C.
+    Returns the same dict as ``oracle.bwd``.
+    """
+    q, k, v, dO = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dO))
+    alpha, mu, beta, eta = (np.asarray(x, dtype=np.float64) for x in (alpha, mu, beta, eta))
+    T_len, dk = k.shape
+    dv = v.shape[1]
+    starts = list(range(0, T_len, C))
+    # 1. forward replay of the chunk-start states, keeping each chunk's matrices
+    S = np.array(S0, dtype=np.float64).reshape(dk, dv)
+    M = np.array(M0, dtype=np.float64).reshape(dk, dv)
+    saved = []
+    for s in starts:
+        sl = slice(s, min(s + C, T_len))
+        Kc, Qc, Vc = k[sl], q[sl], v[sl]
+        a, m, bt, et = alpha[sl], mu[sl], beta[sl], eta[sl]
+        n = a.shape[0]
+        la, lm = np.cumsum(np.log(a)), np.cumsum(np.log(m))
+        E = np.tril(np.exp(np.minimum(la[:, None] - la[None, :], 0.0)))
+        F = np.tril(np.exp(np.minimum(lm[:, None] - lm[None, :], 0.0)))
+        abar, mubar = np.exp(la), np.exp(lm)
+        Psi = E @ np.diag(bt) @ F
+        Gam = Psi * et[None, :]
+        b = E @ (bt * mubar)
+        bprev = np.concatenate([[0.0], b[:-1]])
+        ab = a * bprev
+        Gm = np.zeros((n, n))
+        Gm[1:, :] = Gam[:-1, :]
+        Gm = np.tril(Gm, -1)
+        P = a[:, None] * Kc
+        PK = P @ Kc.T
+        A = PK * Gm
+        Tm = np.linalg.inv(np.eye(n) + A)
+        QK = Qc @ Kc.T
+        Aqk = QK * Gam
+        W = Vc - abar[:, None] * (Kc @ S) + ab[:, None] * (Kc @ M)
+        Vt = Tm @ W
+        gS, gM = Gam[-1, :].copy(), et * F[-1, :]
+        saved.append(dict(sl=sl, S=S, M=M, E=E, F=F, abar=abar, mubar=mubar, Psi=Psi, Gam=Gam, b=b,
+                          bprev=bprev, ab=ab, Gm=Gm, P=P, PK=PK, Tm=Tm, QK=QK, Aqk=Aqk, Vt=Vt, gS=gS, gM=gM))
+        S = abar[-1] * S - b[-1] * M + Kc.T @ (gS[:, None] * Vt)
+        M = mubar[-1] * M - Kc.T @ (gM[:, None] * Vt)
+    out = dict(dq=np.zeros((T_len, dk)), dk=np.zeros((T_len, dk)), dv=np.zeros((T_len, dv)),
+               dalpha=np.zeros(T_len), dmu=np.zeros(T_len), dbeta=np.zeros(T_len), deta=np.zeros(T_len))
+    dS = np.zeros((dk, dv)) if dST is None else np.array(dST, dtype=np.float64).reshape(dk, dv)
+    dM = np.zeros((dk, dv)) if dMT is None else np.array(dMT, dtype=np.float64).reshape(dk, dv)
+    # 2 + 3. reverse over chunks
+    for c in reversed(saved):
+        sl = c["sl"]
+        Kc, Qc = k[sl], q[sl]
+        a, m, bt, et = alpha[sl], mu[sl], beta[sl], eta[sl]
+        dOc = dO[sl]
+        S, M, Vt = c["S"], c["M"], c["Vt"]
+        dVt = c["Aqk"].T @ dOc + c["gS"][:, None] * (Kc @ dS) - c["gM"][:, None] * (Kc @ dM)
+        dW = c["Tm"].T @ dVt
+        dAqk = np.tril(dOc @ Vt.T)
+        dA = -np.tril(dW @ Vt.T, -1)
+        dOS, dOM, dWS, dWM = dOc @ S.T, dOc @ M.T, dW @ S.T, dW @ M.T
+        # Q, K, V
+        X1 = dAqk * c["Gam"]
+        X2 = dA * c["Gm"]
+        dP = X2 @ Kc
+        out["dq"][sl] = c["abar"][:, None] * dOS - c["b"][:, None] * dOM + X1 @ Kc
+        out["dk"][sl] = (X1.T @ Qc + X2.T @ c["P"] + a[:, None] * dP - c["abar"][:, None] * dWS
+                         + c["ab"][:, None] * dWM + c["gS"][:, None] * (Vt @ dS.T) - c["gM"][:, None] * (Vt @ dM.T))
+        out["dv"][sl] = dW
+        # coefficient adjoints
+        L = a.shape[0] - 1
+        Dabar = (Qc * dOS).sum(1) - (Kc * dWS).sum(1)
+        Dabar[L] += (S * dS).sum()
+        Dab = (Kc * dWM).sum(1)
+        Db = -(Qc * dOM).sum(1)
+        Db[L] -= (M * dS).sum()
+        Db[:-1] += Dab[1:] * a[1:]
+        dalpha_direct = (Kc * dP).sum(1) + Dab * c["bprev"]
+        DGam = dAqk * c["QK"]
+        DGam[:-1, :] += np.tril(dA * c["PK"], -1)[1:, :]
+        DgS = ((Vt @ dS.T) * Kc).sum(1)
+        DgM = -((Vt @ dM.T) * Kc).sum(1)
+        DGam[L, :] += DgS
+        Dmubar_L = (M * dM).sum()
+        # gates through the coefficient definitions
+        E, F, Psi, b, mubar, abar = c["E"], c["F"], c["Psi"], c["b"], c["mubar"], c["abar"]
+        DPsi = np.tril(DGam) * et[None, :]
+        deta = (np.tril(DGam) * Psi).sum(0) + DgM * F[L, :]
+        Z = ((E.T @ DPsi) * F).sum(1) + (E.T @ Db) * mubar
+        dla = (DPsi * Psi).sum(1) + Db * b - bt * Z + Dabar * abar
+        dlm = bt * Z - (DPsi * Psi).sum(0) - DgM * c["gM"]
+        dlm[L] += (DgM * c["gM"]).sum() + Dmubar_L * mubar[L]
+        rev = lambda x: np.cumsum(x[::-1])[::-1]
+        out["dalpha"][sl] = rev(dla) / a + dalpha_direct
+        out["dmu"][sl] = rev(dlm) / m
+        out["dbeta"][sl] = Z
+        out["deta"][sl] = deta
+        # chunk-start adjoints
+        dS, dM = (abar[L] * dS + Qc.T @ (abar[:, None] * dOc) - Kc.T @ (abar[:, None] * dW),
+                  mubar[L] * dM - b[L] * dS + (-Qc.T @ (b[:, None] * dOc)) + Kc.T @ (c["ab"][:, None] * dW))
+    out["dS0"], out["dM0"] = dS, dM
+    return out

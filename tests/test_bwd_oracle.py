@@ -156,3 +156,17 @@ def mutant_bwd(name, tmpdir):
 def test_mutant_is_caught(name):
     with tempfile.TemporaryDirectory() as tmp:
         assert check_fd(bwd=mutant_bwd(name, tmp)) > 1e-3, name
+
+
+@pytest.mark.parametrize("seed,T,dk,dv,C,mu_range", [(1, 9, 3, 2, 4, (-1.0, 0.0)), (2, 40, 4, 3, 16, (-3.0, -2.0)),
+                                                     (3, 70, 5, 4, 64, (-1.0, 0.0)), (4, 33, 3, 3, 8, (-0.3, 0.0)),
+                                                     (5, 16, 2, 2, 1, (-1.0, 0.0))])
+def test_chunk_restatement_of_the_backward(seed, T, dk, dv, C, mu_range):
+    # the chunkwise reverse mode (states replayed from Vtilde, reverse carry of
+    # dS/dM, coefficient adjoints to the gates) equals the token reverse mode
+    from oracle import chunk_ref
+    p = pins.rng_problem(seed, T=T, dk=dk, dv=dv, mu_range=mu_range)
+    dO, dST, dMT = loss_terms(seed, T, dk, dv)
+    ref = oracle.bwd(*(p[n] for n in NAMES), p["S0"], p["M0"], dO=dO, dST=dST, dMT=dMT)
+    got = chunk_ref.chunk_bwd_head(*(p[n] for n in NAMES), p["S0"], p["M0"], dO, dST, dMT, C)
+    assert max_rel(got, ref) < 1e-12
