@@ -149,6 +149,41 @@ int mdn_chunk_inter(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int 
                     void* O, float* S_T, float* M_T, void* Vtilde,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward of mdn_chunk_fwd: the gradients of a scalar loss L with respect
+ * to every input, given dL/dO, dL/dS_T and dL/dM_T.  The pages print only
+ * the forward; this is the chain rule applied to its chunk equations (the
+ * summary, steps 2-5, in the form W = V - Diag(abar) K S + Diag(alpha_r
+ * b_{r-1}) K M, vtilde = T W).  The chunk-start states are rebuilt from the
+ * forward's materialised vtilde (the reason the forward stores it: summary,
+ * step 7; article, section 6 and the Q&A), so v itself is not needed.
+ *   B, H, T, dk, dv, C, dtype   as for mdn_chunk_fwd; supported: dk == dv
+ *               in {16, 32, 64} with C in {16, 32} for MDN_F32, dk in
+ *               {32, 64, 128} with C in {32, 64} for MDN_BF16.
+ *   q, k, alpha, mu, beta, eta, S0, M0   the forward's inputs (S0/M0 NULL
+ *               for zero).
+ *   Vtilde      [B][H][T][dv] (dtype): the forward's vtilde for these inputs.
+ *   dO          [B][H][T][dv] (dtype): dL/dO.
+ *   dS_T, dM_T  [B][H][dk][dv] fp32: dL/dS_T, dL/dM_T, or NULL for zero.
+ *   dq, dk_out  [B][H][T][dk] (dtype) out;  dv_out [B][H][T][dv] (dtype) out.
+ *   dalpha, dmu, dbeta, deta   [B][H][T] fp32 out.
+ *   dS0, dM0    [B][H][dk][dv] fp32 out: dL/dS0, dL/dM0 (written whether or
+ *               not S0, M0 were given).
+ *   workspace   at least mdn_chunk_bwd_workspace_bytes(); no output may
+ *               overlap an input or another output.
+ * Gates must be positive and finite (the coefficients use their logs).
+ * Errors as for mdn_chunk_fwd. */
+size_t mdn_chunk_bwd_workspace_bytes(int64_t B, int64_t H, int64_t T,
+                                     int dk, int dv, int C, int dtype);
+
+int mdn_chunk_bwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                  const void* q, const void* k,
+                  const float* alpha, const float* mu, const float* beta, const float* eta,
+                  const float* S0, const float* M0, const void* Vtilde,
+                  const void* dO, const float* dS_T, const float* dM_T,
+                  void* dq, void* dk_out, void* dv_out,
+                  float* dalpha, float* dmu, float* dbeta, float* deta, float* dS0, float* dM0,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Packed variable-length batch: nseq independent sequences of any lengths,
  * laid end to end along the token axis of every head, each starting from
  * its own state.  Each sequence computes exactly what mdn_chunk_fwd computes
@@ -250,7 +285,7 @@ const char* mdn_status_string(int status);
 /* ABI revision of this header (incremented on any signature change). */
 int mdn_abi_version(void);
 
-#define MDN_ABI_VERSION 4
+#define MDN_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

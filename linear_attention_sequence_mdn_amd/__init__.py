@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
     chunk_coef(alpha, mu, beta, eta, C) -> (coef, gamma)
     gates(x, a, b, mu_log, s=1.0, mu_log_min=-2.0, q=None, k=None, d=None)
         -> (alpha, mu, beta, eta) [+ q_out]
+    chunk_bwd(q, k, alpha, mu, beta, eta, Vtilde, dO, S0=None, M0=None, dS_T=None, dM_T=None, C=64)
+        -> dict of dq, dk, dv, dalpha, dmu, dbeta, deta, dS0, dM0
     chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype) -> int
     chunk_fwd_varlen_workspace_bytes(H, T, nseq, dk, dv, C, dtype) -> int
 """
@@ -55,6 +57,10 @@ def lib():
         L.mdn_chunk_fwd_workspace_bytes.restype = sz
         L.mdn_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
         L.mdn_chunk_fwd.restype = i32
+        L.mdn_chunk_bwd_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32]
+        L.mdn_chunk_bwd_workspace_bytes.restype = sz
+        L.mdn_chunk_bwd.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 21 + [vp, sz, vp]
+        L.mdn_chunk_bwd.restype = i32
         L.mdn_chunk_fwd_varlen_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32]
         L.mdn_chunk_fwd_varlen_workspace_bytes.restype = sz
         L.mdn_chunk_fwd_varlen.argtypes = [i64, i64, i64, vp, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
@@ -197,6 +203,69 @@ def chunk_fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, *,
     call = ChunkCall(q, k, v, alpha, mu, beta, eta, S0, M0, C, out=out, S_T=S_T, M_T=M_T,
                      workspace=workspace)
     return call.run(stream)
+
+
+def chunk_bwd_workspace_bytes(B, H, T, dk, dv, C, dtype) -> int:
+    n = lib().mdn_chunk_bwd_workspace_bytes(B, H, T, dk, dv, C, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise MdnError(3, "mdn_chunk_bwd_workspace_bytes")
+    return int(n)
+
+
+BWD_NAMES = ("dq", "dk", "dv", "dalpha", "dmu", "dbeta", "deta", "dS0", "dM0")
+
+
+class BwdCall:
+    """Validated, preallocated arguments of one ``mdn_chunk_bwd``; ``run()``
+    allocates nothing and returns the dict of gradient tensors."""
+
+    def __init__(self, q, k, alpha, mu, beta, eta, Vtilde, dO, S0=None, M0=None, dS_T=None, dM_T=None,
+                 C=64, *, workspace=None):
+        torch = _torch()
+        B, H, T, dk = q.shape
+        dv = Vtilde.shape[-1]
+        self.dt = _dtype_code(q)
+        dev = q.device
+        _need(k, "k", q.dtype, (B, H, T, dk), dev)
+        _need(Vtilde, "Vtilde", q.dtype, (B, H, T, dv), dev)
+        _need(dO, "dO", q.dtype, (B, H, T, dv), dev)
+        for name, g in (("alpha", alpha), ("mu", mu), ("beta", beta), ("eta", eta)):
+            _need(g, name, torch.float32, (B, H, T), dev)
+        for name, s in (("S0", S0), ("M0", M0), ("dS_T", dS_T), ("dM_T", dM_T)):
+            if s is not None:
+                _need(s, name, torch.float32, (B, H, dk, dv), dev)
+        self.grads = dict(
+            dq=torch.empty((B, H, T, dk), dtype=q.dtype, device=dev),
+            dk=torch.empty((B, H, T, dk), dtype=q.dtype, device=dev),
+            dv=torch.empty((B, H, T, dv), dtype=q.dtype, device=dev),
+            dalpha=torch.empty((B, H, T), dtype=torch.float32, device=dev),
+            dmu=torch.empty((B, H, T), dtype=torch.float32, device=dev),
+            dbeta=torch.empty((B, H, T), dtype=torch.float32, device=dev),
+            deta=torch.empty((B, H, T), dtype=torch.float32, device=dev),
+            dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev),
+            dM0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
+        nws = chunk_bwd_workspace_bytes(B, H, T, dk, dv, C, self.dt)
+        if workspace is None:
+            workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        self.sizes = (B, H, T, dk, dv, C, self.dt)
+        self.inputs = (q, k, alpha, mu, beta, eta, S0, M0, Vtilde, dO, dS_T, dM_T)
+        self._ptrs = [_ptr(t) for t in self.inputs] + [_ptr(self.grads[n]) for n in BWD_NAMES]
+        self._ws = (_ptr(workspace), workspace.numel())
+
+    def run(self, stream=None):
+        _check(lib().mdn_chunk_bwd(*self.sizes, *self._ptrs, *self._ws, _stream(stream)), "mdn_chunk_bwd")
+        return self.grads
+
+
+def chunk_bwd(q, k, alpha, mu, beta, eta, Vtilde, dO, S0=None, M0=None, dS_T=None, dM_T=None, C=64, *,
+              workspace=None, stream=None):
+    """Backward of :func:`chunk_fwd`: gradients of a loss given dL/dO (and
+    optionally dL/dS_T, dL/dM_T) for the forward's inputs.  ``Vtilde`` is the
+    forward's output for the same inputs.  Returns a dict with dq, dk, dv
+    ([B,H,T,d], input dtype), dalpha, dmu, dbeta, deta ([B,H,T] fp32) and
+    dS0, dM0 ([B,H,dk,dv] fp32)."""
+    return BwdCall(q, k, alpha, mu, beta, eta, Vtilde, dO, S0, M0, dS_T, dM_T, C, workspace=workspace).run(stream)
 
 
 def chunk_fwd_varlen_workspace_bytes(H, T, nseq, dk, dv, C, dtype) -> int:

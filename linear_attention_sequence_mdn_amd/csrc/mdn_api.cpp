@@ -52,6 +52,13 @@ bool dims_supported_chunk(int dtype, int dk, int dv, int C) {
     return false;
 }
 
+bool dims_supported_bwd(int dtype, int dk, int dv, int C) {
+    if (dk != dv) return false;
+    if (dtype == MDN_F32) return (dk == 16 || dk == 32 || dk == 64) && (C == 16 || C == 32);
+    if (dtype == MDN_BF16) return (dk == 32 || dk == 64 || dk == 128) && (C == 32 || C == 64);
+    return false;
+}
+
 bool dims_supported_step(int dtype, int dk, int dv) {
     if (dtype != MDN_F32 && dtype != MDN_BF16) return false;
     return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
@@ -147,6 +154,26 @@ size_t mdn_chunk_fwd_varlen_workspace_bytes(int64_t H, int64_t T, int64_t nseq, 
     if (varlen_sizes(H, T, nseq, dk, dv, C, &s) != MDN_OK) return (size_t)-1;
     if (!dims_supported_chunk(dtype, dk, dv, C)) return (size_t)-1;
     return workspace_of(s, C, dtype);
+}
+
+// Backward workspace: the forward's sections (T^T and Aqk^T in place of T and
+// Aqk, the coefficients), then per tile the chunk-start states S, M and the
+// chunk-end adjoints dS, dM (element type), the state-product parts of dq
+// and dk (fp32) and the coefficient adjoints (fp32).
+struct BwdSections {
+    size_t mat, cf, st, part, vec, total;
+};
+
+BwdSections bwd_sections(const ChunkSizes& s, int dk, int C, int dtype) {
+    BwdSections b;
+    const size_t es = (size_t)elem_size(dtype);
+    b.mat = align256((size_t)s.tiles * C * C * es);
+    b.cf = align256((size_t)s.tiles * MDN_COEF_ROWS * C * sizeof(float));
+    b.st = align256((size_t)s.tiles * dk * dk * es);
+    b.part = align256((size_t)s.tiles * C * dk * sizeof(float));
+    b.vec = align256((size_t)s.tiles * mdn::MDN_BWD_VEC_ROWS * C * sizeof(float));
+    b.total = 2 * b.mat + b.cf + 4 * b.st + 2 * b.part + b.vec;
+    return b;
 }
 
 // Validation shared by mdn_chunk_fwd, its two stages and the packed-batch
@@ -282,6 +309,89 @@ int mdn_chunk_inter(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int 
                        O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
     if (st != MDN_OK || empty) return st;
     return hip_status(mdn::launch_chunk_inter(a));
+}
+
+size_t mdn_chunk_bwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype)
+{
+    ChunkSizes s;
+    if (chunk_sizes(B, H, T, dk, dv, C, &s) != MDN_OK) return (size_t)-1;
+    if (!dims_supported_bwd(dtype, dk, dv, C)) return (size_t)-1;
+    int64_t x;
+    if (!mul_ok(s.tiles, (int64_t)dk * dk, &x)) return (size_t)-1;
+    return bwd_sections(s, dk, C, dtype).total;
+}
+
+int mdn_chunk_bwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                  const void* q, const void* k,
+                  const float* alpha, const float* mu, const float* beta, const float* eta,
+                  const float* S0, const float* M0, const void* Vtilde,
+                  const void* dO, const float* dS_T, const float* dM_T,
+                  void* dq, void* dk_out, void* dv_out,
+                  float* dalpha, float* dmu, float* dbeta, float* deta, float* dS0, float* dM0,
+                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    ChunkSizes s;
+    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
+    if (st != MDN_OK) return st;
+    if (!dims_supported_bwd(dtype, dk, dv, C)) return MDN_ERR_UNSUPPORTED;
+    int64_t x;
+    if (!mul_ok(s.tiles, (int64_t)dk * dk, &x)) return MDN_ERR_BAD_SHAPE;
+    if (s.BH == 0) return MDN_OK;
+    const bool seq = s.tok > 0;
+    if (!dS0 || !dM0) return MDN_ERR_NULL_ARG;
+    if (seq && (!q || !k || !alpha || !mu || !beta || !eta || !Vtilde || !dO || !dq || !dk_out || !dv_out ||
+                !dalpha || !dmu || !dbeta || !deta))
+        return MDN_ERR_NULL_ARG;
+    const BwdSections sec = bwd_sections(s, dk, C, dtype);
+    if (!workspace || workspace_bytes < sec.total) return MDN_ERR_WORKSPACE;
+    const void* all[] = {q, k, alpha, mu, beta, eta, S0, M0, Vtilde, dO, dS_T, dM_T,
+                         dq, dk_out, dv_out, dalpha, dmu, dbeta, deta, dS0, dM0, workspace};
+    for (const void* p : all)
+        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
+    const int64_t es = elem_size(dtype);
+    const Range ins[] = {range_of(q, s.qk_elems * es), range_of(k, s.qk_elems * es),
+                         range_of(alpha, s.g_elems * 4), range_of(mu, s.g_elems * 4),
+                         range_of(beta, s.g_elems * 4), range_of(eta, s.g_elems * 4),
+                         range_of(S0, S0 ? s.st_elems * 4 : 0), range_of(M0, M0 ? s.st_elems * 4 : 0),
+                         range_of(Vtilde, s.v_elems * es), range_of(dO, s.v_elems * es),
+                         range_of(dS_T, dS_T ? s.st_elems * 4 : 0), range_of(dM_T, dM_T ? s.st_elems * 4 : 0)};
+    const Range outs[] = {range_of(dq, s.qk_elems * es), range_of(dk_out, s.qk_elems * es),
+                          range_of(dv_out, s.v_elems * es), range_of(dalpha, s.g_elems * 4),
+                          range_of(dmu, s.g_elems * 4), range_of(dbeta, s.g_elems * 4),
+                          range_of(deta, s.g_elems * 4), range_of(dS0, s.st_elems * 4),
+                          range_of(dM0, s.st_elems * 4), range_of(workspace, (int64_t)sec.total)};
+    constexpr int NI = sizeof(ins) / sizeof(ins[0]), NO = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < NO; ++i) {
+        for (int j = 0; j < NI; ++j)
+            if (overlap(outs[i], ins[j])) return MDN_ERR_ALIAS;
+        for (int j = i + 1; j < NO; ++j)
+            if (overlap(outs[i], outs[j])) return MDN_ERR_ALIAS;
+    }
+
+    mdn::BwdArgs a;
+    memset(&a, 0, sizeof(a));
+    mdn::ChunkArgs& f = a.f;
+    f.BH = s.BH; f.T = T; f.NT = s.NT;
+    f.dk = dk; f.dv = dv; f.C = C; f.dtype = dtype;
+    f.q = q; f.k = k;
+    f.alpha = alpha; f.mu = mu; f.beta = beta; f.eta = eta;
+    f.S0 = S0; f.M0 = M0;
+    char* w = (char*)workspace;
+    f.Tmat = w;
+    f.Aqk = w + sec.mat;
+    f.coef = (float*)(w + 2 * sec.mat);
+    f.trans = true;
+    f.stream = stream;
+    char* st0 = w + 2 * sec.mat + sec.cf;
+    a.Sst = st0; a.Mst = st0 + sec.st; a.dSst = st0 + 2 * sec.st; a.dMst = st0 + 3 * sec.st;
+    a.dqp = (float*)(st0 + 4 * sec.st);
+    a.dkp = (float*)(st0 + 4 * sec.st + sec.part);
+    a.vec = (float*)(st0 + 4 * sec.st + 2 * sec.part);
+    a.Vt = Vtilde; a.dO = dO; a.dST = dS_T; a.dMT = dM_T;
+    a.dq = dq; a.dk = dk_out; a.dv = dv_out;
+    a.dalpha = dalpha; a.dmu = dmu; a.dbeta = dbeta; a.deta = deta;
+    a.dS0 = dS0; a.dM0 = dM0;
+    return hip_status(mdn::launch_bwd(a));
 }
 
 int mdn_chunk_fwd_varlen(int64_t H, int64_t T, int64_t nseq, const int32_t* cu_seqlens,

@@ -42,8 +42,27 @@ struct ChunkArgs {
     int64_t nseq;
     int32_t* tab;        // [NT][2] (workspace)
     int32_t* perm;       // [nseq] (workspace)
+    bool trans;          // intra stage writes T^T and Aqk^T (for the backward)
     void* stream;
 };
+
+// Backward of the chunk forward: the forward's arguments, its vtilde, the
+// output gradients and the gradient outputs; workspace sections as listed
+// in mdn_api.cpp.
+struct BwdArgs {
+    ChunkArgs f;          // q, k, gates, S0, M0, sizes; Tmat/Aqk hold T^T, Aqk^T
+    const void* Vt;       // [BH][T][D] elem (the forward's vtilde)
+    const void* dO;       // [BH][T][D] elem
+    const float *dST, *dMT;   // [BH][D][D] or NULL
+    void *dq, *dk, *dv;   // [BH][T][D] elem
+    float *dalpha, *dmu, *dbeta, *deta;   // [BH][T]
+    float *dS0, *dM0;     // [BH][D][D]
+    void *Sst, *Mst, *dSst, *dMst;        // [BH*NT][D][D] elem: chunk-start states, chunk-end adjoints
+    float *dqp, *dkp;     // [BH*NT][C][D] fp32: state-product parts of dq, dk
+    float* vec;           // [BH*NT][MDN_BWD_VEC_ROWS][C] fp32: coefficient adjoints from the state products
+};
+constexpr int MDN_BWD_VEC_ROWS = 8;   // Dabar, Db, Dab, DgS, DgM, then <S,dS'>, <M,dS'>, <M,dM'> in row 5
+hipError_t launch_bwd(const BwdArgs& a);
 
 struct GateArgs {
     int64_t N, T, H;          // N = B*H*T tokens

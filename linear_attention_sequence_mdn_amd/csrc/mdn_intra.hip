@@ -30,7 +30,8 @@
 //      forward substitution (one wave each), then column block b of T by
 //      block forward substitution, T_ab = -T_aa sum_{c=b..a-1} A_ac T_cb, on
 //      the fp32 matrix cores, one wave per column block;
-//   5. T and Aqk leave through LDS tiles as full 16-byte stores.
+//   5. T and Aqk leave through LDS tiles as full 16-byte stores (or, for the
+//      backward, T^T and Aqk^T).
 #include "mdn_device.h"
 #include "mdn_internal.h"
 #include "mdn_lds.h"
@@ -163,7 +164,7 @@ struct IntraProducts {
     }
 };
 
-template <typename Tr, int DK, int C, bool COEF_ONLY>
+template <typename Tr, int DK, int C, bool COEF_ONLY, bool TRANS = false>
 __global__ __launch_bounds__(256)
 void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
                       const typename Tr::elem* __restrict__ k,
@@ -475,9 +476,26 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
     constexpr int NP = L::OUT / 16;
     uint4* gT = reinterpret_cast<uint4*>(Tout + tile * C * C);
     uint4* gA = reinterpret_cast<uint4*>(Aqk + tile * C * C);
-    for (int p = tid; p < NP; p += 256) {
-        gT[p] = reinterpret_cast<const uint4*>(oT)[p];
-        gA[p] = reinterpret_cast<const uint4*>(oAq)[p];
+    if constexpr (!TRANS) {
+        for (int p = tid; p < NP; p += 256) {
+            gT[p] = reinterpret_cast<const uint4*>(oT)[p];
+            gA[p] = reinterpret_cast<const uint4*>(oAq)[p];
+        }
+    } else {
+        // T^T and Aqk^T (the backward's A operands): piece p holds row c of
+        // the transpose, columns r0 .. r0 + EPS - 1
+        constexpr int EPS = 16 / L::ES;
+        for (int p = tid; p < NP; p += 256) {
+            const int c = p / (C / EPS), r0 = (p % (C / EPS)) * EPS;
+            union { uint4 u; E e[EPS]; } t, a;
+#pragma unroll
+            for (int j = 0; j < EPS; ++j) {
+                t.e[j] = oT[(r0 + j) * C + c];
+                a.e[j] = oAq[(r0 + j) * C + c];
+            }
+            gT[p] = t.u;
+            gA[p] = a.u;
+        }
     }
 }
 
@@ -489,10 +507,16 @@ static hipError_t launch_intra_t(const ChunkArgs& a)
 {
     using E = typename Tr::elem;
     const int64_t tiles = a.BH * a.NT;
-    hipLaunchKernelGGL((mdn_intra_kernel<Tr, DK, C, COEF_ONLY>), dim3((unsigned)tiles), dim3(256), 0,
-                       (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k,
-                       a.alpha, a.mu, a.beta, a.eta, a.T, a.NT, reinterpret_cast<const int2*>(a.tab),
-                       (E*)a.Tmat, (E*)a.Aqk, a.coef, a.gamma);
+    if (!COEF_ONLY && a.trans)
+        hipLaunchKernelGGL((mdn_intra_kernel<Tr, DK, C, false, true>), dim3((unsigned)tiles), dim3(256), 0,
+                           (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k,
+                           a.alpha, a.mu, a.beta, a.eta, a.T, a.NT, reinterpret_cast<const int2*>(a.tab),
+                           (E*)a.Tmat, (E*)a.Aqk, a.coef, a.gamma);
+    else
+        hipLaunchKernelGGL((mdn_intra_kernel<Tr, DK, C, COEF_ONLY>), dim3((unsigned)tiles), dim3(256), 0,
+                           (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k,
+                           a.alpha, a.mu, a.beta, a.eta, a.T, a.NT, reinterpret_cast<const int2*>(a.tab),
+                           (E*)a.Tmat, (E*)a.Aqk, a.coef, a.gamma);
     return hipGetLastError();
 }
 

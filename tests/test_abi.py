@@ -33,7 +33,8 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("mdn_chunk_fwd", "mdn_step", "mdn_chunk_fwd_workspace_bytes", "mdn_chunk_intra",
               "mdn_chunk_inter", "mdn_chunk_coef", "mdn_gates", "mdn_chunk_fwd_varlen",
-              "mdn_chunk_fwd_varlen_workspace_bytes", "mdn_status_string", "mdn_abi_version"):
+              "mdn_chunk_fwd_varlen_workspace_bytes", "mdn_chunk_bwd", "mdn_chunk_bwd_workspace_bytes",
+              "mdn_status_string", "mdn_abi_version"):
         assert n in names
 
 
@@ -48,7 +49,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.mdn_abi_version() == 4
+    assert L.mdn_abi_version() == 5
 
 
 def test_status_strings(L):

@@ -1,0 +1,80 @@
+"""GPU parity of the chunkwise backward (mdn_chunk_bwd) against the fp64
+reverse-mode oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_sequence_mdn_amd import inputs
+from tests.gpu_util import TOL, dev, host, note, rel_err, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dalpha", "dmu", "dbeta", "deta", "dS0", "dM0")
+
+
+def upstream(x, seed, with_states=True):
+    rng = np.random.default_rng(900 + seed)
+    B, H, T = x.B, x.H, x.T
+    cast = inputs.round_to_bf16 if x.dtype == "bf16" else (lambda a: a.astype(np.float32))
+    dO = cast(rng.standard_normal((B, H, T, x.dv)))
+    dST = rng.standard_normal((B, H, x.dk, x.dv)).astype(np.float32) if with_states else None
+    dMT = rng.standard_normal((B, H, x.dk, x.dv)).astype(np.float32) if with_states else None
+    return dO, dST, dMT
+
+
+def run_bwd(x, dO, dST, dMT, C=None):
+    """GPU forward (for vtilde), then the GPU backward; host fp64 dict."""
+    import linear_attention_sequence_mdn_amd as mdn
+    torch = torch_mod()
+    C = x.C if C is None else C
+    dq, dk, dv = dev(x.q, x.dtype), dev(x.k, x.dtype), dev(x.v, x.dtype)
+    gates = [dev(x.alpha), dev(x.mu), dev(x.beta), dev(x.eta)]
+    S0 = None if x.S0 is None else dev(x.S0)
+    M0 = None if x.M0 is None else dev(x.M0)
+    _, _, _, Vt = mdn.chunk_fwd(dq, dk, dv, *gates, S0, M0, C=C)
+    g = mdn.chunk_bwd(dq, dk, *gates, Vt, dev(dO, x.dtype), S0, M0,
+                      None if dST is None else dev(dST), None if dMT is None else dev(dMT), C=C)
+    torch.cuda.synchronize()
+    return {n: host(t) for n, t in g.items()}
+
+
+def ref_bwd(x, dO, dST, dMT):
+    return oracle.bwd(x.q, x.k, x.v, x.alpha, x.mu, x.beta, x.eta, x.S0, x.M0, dO=dO, dST=dST, dMT=dMT)
+
+
+def check(got, ref, tol, label):
+    errs = {n: rel_err(got[n], ref[n]) for n in GRADS}
+    note(f"  {label}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= tol, (label, n, e)
+
+
+@pytest.mark.parametrize("d,C,T", [(16, 16, 50), (32, 32, 70), (64, 16, 40), (64, 32, 64), (16, 32, 33)])
+def test_bwd_fp32_small(d, C, T):
+    x = inputs.make_chunk_inputs(1, 2, T, d, C=C, dtype="f32", seed=d + C + T, state_std=0.3)
+    dO, dST, dMT = upstream(x, d + T)
+    note(f"bwd fp32 d={d} C={C} T={T}")
+    check(run_bwd(x, dO, dST, dMT), ref_bwd(x, dO, dST, dMT), TOL["f32"], f"bwd f32 d{d} C{C} T{T}")
+
+
+@pytest.mark.parametrize("d,C,T", [(64, 32, 100), (128, 64, 200), (32, 64, 130), (128, 32, 96), (64, 64, 64)])
+def test_bwd_bf16_small(d, C, T):
+    x = inputs.make_chunk_inputs(2, 2, T, d, C=C, dtype="bf16", seed=3 * d + C + T, state_std=0.02)
+    dO, dST, dMT = upstream(x, d + T)
+    note(f"bwd bf16 d={d} C={C} T={T}")
+    check(run_bwd(x, dO, dST, dMT), ref_bwd(x, dO, dST, dMT), TOL["bf16"], f"bwd bf16 d{d} C{C} T{T}")
+
+
+def test_bwd_zero_state_no_state_gradients():
+    x = inputs.make_chunk_inputs(1, 2, 150, 128, C=64, dtype="bf16", seed=40)
+    dO, _, _ = upstream(x, 40, with_states=False)
+    note("bwd bf16 d128 C64 T150, S0 = M0 = NULL, dS_T = dM_T = NULL")
+    check(run_bwd(x, dO, None, None), ref_bwd(x, dO, None, None), TOL["bf16"], "bwd zero state")
+
+
+def test_bwd_strong_momentum():
+    x = inputs.make_chunk_inputs(1, 2, 256, 128, C=64, dtype="bf16", seed=41,
+                                 mu_range=(-2.0, -1.5), a_range=(5.0, 10.0))
+    dO, dST, dMT = upstream(x, 41)
+    note("bwd bf16 long-context gates T=256")
+    check(run_bwd(x, dO, dST, dMT), ref_bwd(x, dO, dST, dMT), TOL["bf16"], "bwd strong momentum")
