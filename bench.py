@@ -21,6 +21,7 @@ The same run also reports, each measured live with HIP events:
     400M-layer shape, as GB/s of algorithmic HBM traffic;
   * a packed prefill batch (``mdn_chunk_fwd_varlen``): 32768 tokens of 8
     heads in sequences of lengths ~U{1..4096}, as tokens/s;
+  * the backward (``mdn_chunk_bwd``) on the 400M-layer workload, as tokens/s;
   * the fp64 CPU oracle on a bounded sample of the chunk workload.
 Prints ONE JSON line.
 """
@@ -56,6 +57,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-gates", action="store_true")
     p.add_argument("--no-varlen", action="store_true")
+    p.add_argument("--no-bwd", action="store_true")
     p.add_argument("--no-chunk", action="store_true")
     p.add_argument("--decode-reps", type=int, default=5)
     p.add_argument("--decode-steps", type=int, default=128)
@@ -181,7 +183,7 @@ def chunk_bench(args, torch, mdn, inputs):
     tps = tokens / (ms_step / 1e3)
     mfma_frac = tps * H * F_TOKEN_HEAD / (PEAK_BF16_TFLOPS * 1e12)
     return dict(ms_step=ms_step, tokens_per_s=tps, mfma_frac=mfma_frac, kernels=kernels,
-                roofline=roof, finite=finite, x=x, cfg=cfg)
+                roofline=roof, finite=finite, x=x, cfg=cfg, call=call)
 
 
 def decode_bench(args, torch, mdn, inputs):
@@ -233,6 +235,45 @@ def decode_bench(args, torch, mdn, inputs):
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "kernel": "mdn_step_kernel",
                          "source_sha": sha}}
+
+
+# algorithmic FLOP per token-head of the backward at d = 128, C = 64: the
+# state products of the reverse carry (12 d^2) and of the per-chunk state
+# gradients (12 d^2), the replay's state update (4 d^2), the in-chunk
+# products (about 12 C d over the causal halves) and the recomputed intra
+# stage (2 C d + 2 C^2 / 3)
+def bwd_flop_per_token_head(d, C):
+    return 28 * d * d + 12 * C * d + 2 * C * d + (2 * C * C) // 3
+
+
+def bwd_bench(args, torch, mdn, inputs, ch):
+    """The backward (``mdn_chunk_bwd``) on the 400M-layer workload, from the
+    forward's vtilde with a seeded bf16 dL/dO: tokens/s of whole calls."""
+    x = ch["x"]
+    call = ch["call"]
+    q, k, v, alpha, mu, beta, eta, S0, M0 = call.tensors[:9]
+    O, ST, MT, Vt = call.run()
+    rng = np.random.default_rng(901)
+    dO = torch.from_numpy(rng.standard_normal(O.shape).astype(np.float32)).cuda().to(torch.bfloat16)
+    bc = mdn.BwdCall(q, k, alpha, mu, beta, eta, Vt, dO, S0, M0, None, None, x.C)
+    for _ in range(args.warmup):
+        bc.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        bc.run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens = x.B * x.T
+    f = bwd_flop_per_token_head(x.dk, x.C)
+    tflops = tokens * x.H * f / (ms / 1e3) / 1e12
+    finite = all(bool(torch.isfinite(t.float()).all()) for t in bc.grads.values())
+    return {"metric": "backward tokens/s", "value": tokens / (ms / 1e3), "unit": "tokens/s", "ms_per_call": ms,
+            "workload": WORKLOAD_NAMES[1] + ", dL/dO ~ N(0,1) bf16, dL/dS_T = dL/dM_T = 0",
+            "flop_per_token_head": f, "TFLOPs": tflops, "mfma_frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+            "grads_finite": finite}
 
 
 def varlen_bench(args, torch, mdn, inputs):
@@ -376,6 +417,8 @@ def main():
         out["gates"] = gates_bench(args, torch, mdn, inputs)
     if not args.no_varlen:
         out["varlen"] = varlen_bench(args, torch, mdn, inputs)
+    if ch is not None and not args.no_bwd and args.workload == 1:
+        out["bwd"] = bwd_bench(args, torch, mdn, inputs, ch)
     if ch is not None and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, ch["x"])
     try:

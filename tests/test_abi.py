@@ -276,3 +276,48 @@ def test_varlen_validation(L):
     q[9] = q[0]                                          # O on top of q
     assert varlen_call(L, ptrs=q) == ALIAS
     assert varlen_call(L, cu=p[13]) == ALIAS             # sequence bounds inside the workspace
+
+
+def bwd_call(L, B=1, H=2, T=64, d=32, C=32, dt=1, ptrs=None, ws_bytes=None):
+    p = addrs(22) if ptrs is None else ptrs
+    n = L.mdn_chunk_bwd_workspace_bytes(B, H, T, d, d, C, dt) if ws_bytes is None else ws_bytes
+    return L.mdn_chunk_bwd(B, H, T, d, d, C, dt, *p[:21], p[21], n, None)
+
+
+def test_bwd_workspace_bytes(L):
+    # T^T, Aqk^T (bf16 C x C per chunk), 8 coefficient rows, four d x d states
+    # (bf16), two C x d fp32 partial gradients and 8 rows of coefficient adjoints
+    B, H, T, d, C = 8, 8, 4096, 128, 64
+    tiles = B * H * (T // C)
+    expect = (2 * tiles * C * C * 2 + tiles * 8 * C * 4 + 4 * tiles * d * d * 2 + 2 * tiles * C * d * 4
+              + tiles * 8 * C * 4)
+    assert mdn.chunk_bwd_workspace_bytes(B, H, T, d, d, C, mdn.MDN_BF16) == expect
+    bad = ctypes.c_size_t(-1).value
+    assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0) == bad     # fp32 needs d <= 64
+    assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 64, 64, 64, 0) == bad       # and C <= 32
+    assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 16, 16, 32, 1) == bad       # bf16 needs d >= 32
+
+
+def test_bwd_validation(L):
+    assert bwd_call(L, d=48) == UNSUPPORTED
+    assert bwd_call(L, dt=0, d=128, C=64) == UNSUPPORTED
+    assert bwd_call(L, T=-1) == BAD_SHAPE
+    assert bwd_call(L, B=0, ptrs=[None] * 22) == OK
+    p = addrs(22)
+    for i in (0, 1, 2, 3, 4, 5, 8, 9, 12, 13, 14, 15, 16, 17, 18, 19, 20):
+        q = list(p)
+        q[i] = None
+        assert bwd_call(L, ptrs=q) == NULL_ARG, i
+    q = list(p)
+    q[6] = q[7] = q[10] = q[11] = None       # S0, M0, dS_T, dM_T may be NULL
+    assert bwd_call(L, ptrs=q, ws_bytes=0) == WORKSPACE
+    assert bwd_call(L, ws_bytes=1) == WORKSPACE
+    q = list(p)
+    q[2] = ctypes.c_void_p(p[2].value + 4)
+    assert bwd_call(L, ptrs=q) == ALIGN
+    q = list(p)
+    q[12] = q[0]                               # dq on top of q
+    assert bwd_call(L, ptrs=q) == ALIAS
+    q = list(p)
+    q[21] = q[8]                               # workspace on Vtilde
+    assert bwd_call(L, ptrs=q) == ALIAS

@@ -78,3 +78,21 @@ def test_bwd_strong_momentum():
     dO, dST, dMT = upstream(x, 41)
     note("bwd bf16 long-context gates T=256")
     check(run_bwd(x, dO, dST, dMT), ref_bwd(x, dO, dST, dMT), TOL["bf16"], "bwd strong momentum")
+
+
+def test_bwd_full_size_sampled():
+    # the 400M-layer workload (B8 H8 T4096 d128 C64 bf16) in the launch
+    # configuration the benchmark times; three heads against the oracle
+    x = inputs.config_inputs(1)
+    dO, dST, dMT = upstream(x, 1)
+    note("bwd 400M-layer B8 H8 T4096 d128 C64 bf16")
+    got = run_bwd(x, dO, dST, dMT)
+    for n in GRADS:
+        assert np.all(np.isfinite(got[n])), n
+    heads = [(0, 0), (7, 7), (3, 5)]
+    bi = np.array([p[0] for p in heads])
+    hi = np.array([p[1] for p in heads])
+    sel = lambda a: None if a is None else a[bi, hi]
+    ref = oracle.bwd(*(sel(getattr(x, n)) for n in ("q", "k", "v", "alpha", "mu", "beta", "eta")),
+                     sel(x.S0), sel(x.M0), dO=sel(dO), dST=sel(dST), dMT=sel(dMT))
+    check({n: got[n][bi, hi] for n in GRADS}, ref, TOL["bf16"], f"bwd full size, heads {heads}")
