@@ -156,9 +156,8 @@ int mdn_chunk_inter(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int 
  * b_{r-1}) K M, vtilde = T W).  The chunk-start states are rebuilt from the
  * forward's materialised vtilde (the reason the forward stores it: summary,
  * step 7; article, section 6 and the Q&A), so v itself is not needed.
- *   B, H, T, dk, dv, C, dtype   as for mdn_chunk_fwd; supported: dk == dv
- *               in {16, 32, 64} with C in {16, 32} for MDN_F32, dk in
- *               {32, 64, 128} with C in {32, 64} for MDN_BF16.
+ *   B, H, T, dk, dv, C, dtype   as for mdn_chunk_fwd, with the same
+ *               supported sizes.
  *   q, k, alpha, mu, beta, eta, S0, M0   the forward's inputs (S0/M0 NULL
  *               for zero).
  *   Vtilde      [B][H][T][dv] (dtype): the forward's vtilde for these inputs.

@@ -54,9 +54,7 @@ bool dims_supported_chunk(int dtype, int dk, int dv, int C) {
 
 bool dims_supported_bwd(int dtype, int dk, int dv, int C) {
     if (dk != dv) return false;
-    if (dtype == MDN_F32) return (dk == 16 || dk == 32 || dk == 64) && (C == 16 || C == 32);
-    if (dtype == MDN_BF16) return (dk == 32 || dk == 64 || dk == 128) && (C == 32 || C == 64);
-    return false;
+    return dims_supported_chunk(dtype, dk, dv, C);
 }
 
 bool dims_supported_step(int dtype, int dk, int dv) {

@@ -476,12 +476,16 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
 // ---------------------------------------------------------------------------
 // sgrad: the products with the states, one workgroup per chunk tile
 //
-// Wave w owns chunk rows 16w .. 16w+15 (natural order; its A operands come
-// straight from global memory, zero past the end of a ragged chunk) and all
-// dk columns.  For each state X of the chunk the B operand X^T is read from
-// the workspace (rows of X are contiguous in the contraction index).  Row
-// dots with q and k give the coefficient adjoints; the state inner products
-// <S, dS'>, <M, dS'>, <M, dM'> are summed by the whole workgroup.
+// The A operands (the chunk's dO, dW and vtilde rows) are staged in LDS by
+// direct loads; wave w owns dk-column tiles [w*CPW, (w+1)*CPW) of the
+// outputs, so each state row (the B operand X^T: rows of X are contiguous
+// in the contraction index) is read from memory once per workgroup.  For
+// one column tile the four states' operands are held while the chunk's
+// row tiles run; each 16 x 16 output tile is folded and stored as soon as
+// its six products are done.  Row dots with q and k give the coefficient
+// adjoints (rows past a ragged end are masked: their staged rows repeat the
+// last one); the state inner products <S, dS'>, <M, dS'>, <M, dM'> come from
+// the same operands.
 // ---------------------------------------------------------------------------
 template <typename Tr, int D, int C>
 __global__ __launch_bounds__(256)
@@ -495,7 +499,12 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
 {
     using E = typename Tr::elem;
     using frag = typename Tr::frag;
+    constexpr int ES = sizeof(E);
     constexpr int NCT = C / 16, NDH = D / 16, KSD = D / Tr::KW;
+    constexpr int CPW = NDH >= 4 ? NDH / 4 : 1;       // column tiles per wave
+    constexpr int PK = D * ES / 16, TB = C * PK * 16;
+    __shared__ __attribute__((aligned(16))) char st[3 * TB];   // dO, dW, vtilde rows (swizzled)
+    __shared__ float rv[4][5][C];                                // per-wave row dots
     __shared__ float red[4][3];
 
     const int64_t tile = blockIdx.x;
@@ -511,123 +520,119 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     const float* cf = coef + tile * MDN_COEF_ROWS * C;
     float* vt = vec + tile * MDN_BWD_VEC_ROWS * C;
 
-    // the state inner products (all threads)
     {
-        constexpr int EPV = 16 / sizeof(E);
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
-        for (int p = tid; p < D * D / EPV; p += 256) {
-            union U { uint4 u; E e[EPV]; };
-            U a, b, c, d;
-            a.u = reinterpret_cast<const uint4*>(S)[p];
-            b.u = reinterpret_cast<const uint4*>(M)[p];
-            c.u = reinterpret_cast<const uint4*>(dS)[p];
-            d.u = reinterpret_cast<const uint4*>(dM)[p];
+        const unsigned vlast = (unsigned)vm - 1;
+        auto seq_row = [&](unsigned r) { return (r < vlast ? r : vlast) * (unsigned)(D * ES); };
+        const uint32_t base = lds_addr(st);
+        if (wave == 0) dma_tile<C, PK>(base, reinterpret_cast<const char*>(dO + rowbase * D), seq_row, lane);
+        else if (wave == 1) dma_tile<C, PK>(base + TB, reinterpret_cast<const char*>(dW + rowbase * D), seq_row, lane);
+        else if (wave == 2) dma_tile<C, PK>(base + 2 * TB, reinterpret_cast<const char*>(Vt + rowbase * D), seq_row, lane);
+    }
+    for (int i = tid; i < 4 * 5 * C; i += 256) (&rv[0][0][0])[i] = 0.f;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    float ip0 = 0.f, ip1 = 0.f, ip2 = 0.f;
 #pragma unroll
-            for (int j = 0; j < EPV; ++j) {
-                const float xs = Tr::to_f(a.e[j]), xm = Tr::to_f(b.e[j]);
-                const float ys = Tr::to_f(c.e[j]), ym = Tr::to_f(d.e[j]);
-                s0 = fmaf(xs, ys, s0);
-                s1 = fmaf(xm, ys, s1);
-                s2 = fmaf(xm, ym, s2);
+    for (int cc = 0; cc < CPW; ++cc) {
+        const int ct = wave * CPW + cc;
+        if (ct >= NDH) break;                         // uniform
+        const int c = 16 * ct + nn;                   // dk column of this lane's outputs / state row
+        frag bS[KSD], bM[KSD], bdS[KSD], bdM[KSD];
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            bS[ks] = SlotRow<Tr>::load(S + (size_t)c * D, ks, g);
+            bM[ks] = SlotRow<Tr>::load(M + (size_t)c * D, ks, g);
+            bdS[ks] = SlotRow<Tr>::load(dS + (size_t)c * D, ks, g);
+            bdM[ks] = SlotRow<Tr>::load(dM + (size_t)c * D, ks, g);
+        }
+        // the state inner products over these rows
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            if constexpr (std::is_same<Tr, TraitsBf16>::value) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float xs = (float)bS[ks][j], xm = (float)bM[ks][j];
+                    const float ys = (float)bdS[ks][j], ym = (float)bdM[ks][j];
+                    ip0 = fmaf(xs, ys, ip0);
+                    ip1 = fmaf(xm, ys, ip1);
+                    ip2 = fmaf(xm, ym, ip2);
+                }
+            } else {
+                ip0 = fmaf(bS[ks], bdS[ks], ip0);
+                ip1 = fmaf(bM[ks], bdS[ks], ip1);
+                ip2 = fmaf(bM[ks], bdM[ks], ip2);
             }
         }
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            s0 += __shfl_xor(s0, m, 64);
-            s1 += __shfl_xor(s1, m, 64);
-            s2 += __shfl_xor(s2, m, 64);
+        for (int rt = 0; rt < NCT; ++rt) {
+            floatx4 oS = zero4(), wS = zero4(), oM = zero4(), wM = zero4(), vS = zero4(), vM = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                const frag aO = LdsA<Tr, PK>::load(st, 16 * rt + nn, ks, g);
+                const frag aW = LdsA<Tr, PK>::load(st + TB, 16 * rt + nn, ks, g);
+                const frag aV = LdsA<Tr, PK>::load(st + 2 * TB, 16 * rt + nn, ks, g);
+                oS = Tr::mma(aO, bS[ks], oS);
+                oM = Tr::mma(aO, bM[ks], oM);
+                wS = Tr::mma(aW, bS[ks], wS);
+                wM = Tr::mma(aW, bM[ks], wM);
+                vS = Tr::mma(aV, bdS[ks], vS);
+                vM = Tr::mma(aV, bdM[ks], vM);
+            }
+            const int r0 = 16 * rt + 4 * g;
+            const floatx4 ca = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_ABAR * C + r0);
+            const floatx4 cb = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_B * C + r0);
+            const floatx4 cab = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_ABP * C + r0);
+            const floatx4 cgs = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_GS * C + r0);
+            const floatx4 cgm = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_GM * C + r0);
+            float* qo = dqp + (tile * C + r0) * D + c;
+            float* ko = dkp + (tile * C + r0) * D + c;
+            float pd[5][4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = r0 + e;
+                const bool in = r < vm;
+                const float m = in ? 1.f : 0.f;
+                const float os = m * oS[e], om = m * oM[e], ws = m * wS[e], wm = m * wM[e];
+                const float vs = m * vS[e], vmm = m * vM[e];
+                qo[e * D] = ca[e] * os - cb[e] * om;
+                ko[e * D] = -ca[e] * ws + cab[e] * wm + cgs[e] * vs - cgm[e] * vmm;
+                const float qv = in ? Tr::to_f(q[(rowbase + r) * D + c]) : 0.f;
+                const float kv = in ? Tr::to_f(k[(rowbase + r) * D + c]) : 0.f;
+                pd[0][e] = qv * os - kv * ws;
+                pd[1][e] = -qv * om;
+                pd[2][e] = kv * wm;
+                pd[3][e] = kv * vs;
+                pd[4][e] = -kv * vmm;
+            }
+#pragma unroll
+            for (int a = 0; a < 5; ++a)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                    for (int sft = 8; sft >= 1; sft >>= 1) pd[a][e] += __shfl_xor(pd[a][e], sft, 64);
+                }
+            if (nn == 0) {
+#pragma unroll
+                for (int a = 0; a < 5; ++a)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rv[wave][a][r0 + e] += pd[a][e];
+            }
         }
-        if (lane == 0) { red[wave][0] = s0; red[wave][1] = s1; red[wave][2] = s2; }
     }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        ip0 += __shfl_xor(ip0, m, 64);
+        ip1 += __shfl_xor(ip1, m, 64);
+        ip2 += __shfl_xor(ip2, m, 64);
+    }
+    if (lane == 0) { red[wave][0] = ip0; red[wave][1] = ip1; red[wave][2] = ip2; }
     __syncthreads();
+    for (int i = tid; i < 5 * C; i += 256) {
+        const int a = i / C, r = i % C;
+        vt[a * C + r] = rv[0][a][r] + rv[1][a][r] + rv[2][a][r] + rv[3][a][r];
+    }
     if (tid < 3) vt[5 * C + tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-
-    if (wave >= NCT) return;
-    const int rA = 16 * wave + nn;                    // A-operand row of this lane
-    frag aO[KSD], aW[KSD], aV[KSD];
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-        if (rA < vm) {
-            aO[ks] = Contig<Tr>::load(dO + (rowbase + rA) * D, ks, g);
-            aW[ks] = Contig<Tr>::load(dW + (rowbase + rA) * D, ks, g);
-            aV[ks] = Contig<Tr>::load(Vt + (rowbase + rA) * D, ks, g);
-        } else {
-            aO[ks] = Contig<Tr>::zero();
-            aW[ks] = Contig<Tr>::zero();
-            aV[ks] = Contig<Tr>::zero();
-        }
-    }
-    const int r0 = 16 * wave + 4 * g;                 // accumulator rows r0 + e
-    const floatx4 ca = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_ABAR * C + r0);
-    const floatx4 cb = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_B * C + r0);
-    const floatx4 cab = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_ABP * C + r0);
-    const floatx4 cgs = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_GS * C + r0);
-    const floatx4 cgm = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_GM * C + r0);
-    floatx4 dq[NDH], dk[NDH];
-    float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f}, pab[4] = {0.f, 0.f, 0.f, 0.f};
-    float pgs[4] = {0.f, 0.f, 0.f, 0.f}, pgm[4] = {0.f, 0.f, 0.f, 0.f};
-    auto qk_at = [&](const E* x, int e, int c) __attribute__((always_inline)) {
-        return (r0 + e < vm) ? Tr::to_f(x[(rowbase + r0 + e) * D + c]) : 0.f;
-    };
-#pragma unroll
-    for (int ct = 0; ct < NDH; ++ct) {
-        const int c = 16 * ct + nn;
-        floatx4 oS = zero4(), wS = zero4(), oM = zero4(), wM = zero4(), vS = zero4(), vM = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-            const frag bS = Contig<Tr>::load(S + (size_t)c * D, ks, g);
-            const frag bM = Contig<Tr>::load(M + (size_t)c * D, ks, g);
-            const frag bdS = Contig<Tr>::load(dS + (size_t)c * D, ks, g);
-            const frag bdM = Contig<Tr>::load(dM + (size_t)c * D, ks, g);
-            oS = Tr::mma(aO[ks], bS, oS);
-            wS = Tr::mma(aW[ks], bS, wS);
-            oM = Tr::mma(aO[ks], bM, oM);
-            wM = Tr::mma(aW[ks], bM, wM);
-            vS = Tr::mma(aV[ks], bdS, vS);
-            vM = Tr::mma(aV[ks], bdM, vM);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            dq[ct][e] = ca[e] * oS[e] - cb[e] * oM[e];
-            dk[ct][e] = -ca[e] * wS[e] + cab[e] * wM[e] + cgs[e] * vS[e] - cgm[e] * vM[e];
-            const float qv = qk_at(q, e, c), kv = qk_at(k, e, c);
-            pa[e] += qv * oS[e] - kv * wS[e];
-            pb[e] -= qv * oM[e];
-            pab[e] += kv * wM[e];
-            pgs[e] += kv * vS[e];
-            pgm[e] -= kv * vM[e];
-        }
-    }
-    float* qo = dqp + (tile * C + r0) * D;
-    float* ko = dkp + (tile * C + r0) * D;
-#pragma unroll
-    for (int ct = 0; ct < NDH; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            qo[e * D + 16 * ct + nn] = dq[ct][e];
-            ko[e * D + 16 * ct + nn] = dk[ct][e];
-        }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-#pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) {
-            pa[e] += __shfl_xor(pa[e], m, 64);
-            pb[e] += __shfl_xor(pb[e], m, 64);
-            pab[e] += __shfl_xor(pab[e], m, 64);
-            pgs[e] += __shfl_xor(pgs[e], m, 64);
-            pgm[e] += __shfl_xor(pgm[e], m, 64);
-        }
-    }
-    if (nn == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vt[0 * C + r0 + e] = pa[e];
-            vt[1 * C + r0 + e] = pb[e];
-            vt[2 * C + r0 + e] = pab[e];
-            vt[3 * C + r0 + e] = pgs[e];
-            vt[4 * C + r0 + e] = pgm[e];
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -657,10 +662,9 @@ struct CgradLayout {
     static constexpr int FB = C * FS * 4;
     static constexpr int XB = C * XS * ES;
     static constexpr int QT = C * D * ES;             // Q or K tile (plain rows of D)
-    // fp32 C x C: QK -> DGamma, PK, dAqk, dA', Psi;  element C x C: X1, X1^T, X2, X2a^T
-    static constexpr int F0 = 0, F1 = FB, F2 = 2 * FB, F3 = 3 * FB, F4 = 4 * FB;
-    static constexpr int X0 = 5 * FB;
-    static constexpr int Q0 = X0 + 4 * XB, K0 = Q0 + QT;
+    static constexpr int G0 = 0;                      // DGamma (fp32)
+    static constexpr int X0 = FB;                     // X1, then Diag(alpha) X2 (elements)
+    static constexpr int Q0 = X0 + 2 * XB, K0 = Q0 + QT;
     static constexpr int V0 = K0 + QT;
     static constexpr int NV = 20;                     // vectors of C floats
     static constexpr int TOTAL = V0 + NV * C * 4;
@@ -685,15 +689,9 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     using F32 = TraitsF32;
     constexpr int NCT = C / 16, NDH = D / 16, KSD = D / Tr::KW, KSC = C / Tr::KW, FS = L::FS, XS = L::XS;
     __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
-    float* fQK = reinterpret_cast<float*>(lds + L::F0);     // Q K^T, then DGamma
-    float* fPK = reinterpret_cast<float*>(lds + L::F1);     // P K^T
-    float* fAq = reinterpret_cast<float*>(lds + L::F2);     // dO vtilde^T
-    float* fAw = reinterpret_cast<float*>(lds + L::F3);     // dW vtilde^T
-    float* fPs = reinterpret_cast<float*>(lds + L::F4);     // Psi
+    float* fDG = reinterpret_cast<float*>(lds + L::G0);
     E* x1 = reinterpret_cast<E*>(lds + L::X0);
-    E* x1t = reinterpret_cast<E*>(lds + L::X0 + L::XB);
-    E* x2 = reinterpret_cast<E*>(lds + L::X0 + 2 * L::XB);
-    E* x2t = reinterpret_cast<E*>(lds + L::X0 + 3 * L::XB);
+    E* x2a = reinterpret_cast<E*>(lds + L::X0 + L::XB);
     E* Ql = reinterpret_cast<E*>(lds + L::Q0);
     E* Kl = reinterpret_cast<E*>(lds + L::K0);
     float* vv = reinterpret_cast<float*>(lds + L::V0);
@@ -701,7 +699,7 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     float* sBe = vv + 4 * C; float* sEt = vv + 5 * C; float* sAb = vv + 6 * C; float* sB = vv + 7 * C;
     float* sGM = vv + 8 * C; float* sDa = vv + 9 * C; float* sDb = vv + 10 * C; float* sDab = vv + 11 * C;
     float* sDgM = vv + 12 * C; float* sDgS = vv + 13 * C; float* sZ = vv + 14 * C; float* sAd = vv + 15 * C;
-    float* sMisc = vv + 16 * C;
+    float* sRow = vv + 16 * C; float* sCol = vv + 17 * C; float* sZb = vv + 18 * C; float* sMisc = vv + 19 * C;
 
     const int64_t tile = blockIdx.x;
     const int64_t bh = tile / NT, n = tile % NT;
@@ -743,6 +741,8 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
             sDgS[r] = vt[3 * C + r];
             sDgM[r] = vt[4 * C + r];
             sAd[r] = 0.f;
+            sRow[r] = 0.f;
+            sCol[r] = 0.f;
         }
         if (tid < 3) sMisc[tid] = vt[5 * C + tid];    // <S,dS'>, <M,dS'>, <M,dM'>
     }
@@ -757,9 +757,11 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         if (r == LR) sDa[r] += sMisc[0];
     }
 
-    // ---- 2. Q K^T, K K^T, dO vtilde^T, dW vtilde^T (row block = wave) -----------
+    // ---- 2. per row block (wave): Psi, the C x C products and what they feed --
+    float apv[NCT][4];                                // dA o (P K^T) of the wave's rows, for DGamma of the row above
     if (wave < NCT) {
-        const int rA = 16 * wave + nn;
+        const int rA = 16 * wave + nn, r0 = 16 * wave + 4 * g;
+        const float laA = sLA[rA], laP = rA > 0 ? sLA[rA - 1] : 0.f;
         frag aQ[KSD], aK[KSD], aO[KSD], aW[KSD];
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
@@ -773,96 +775,105 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 aW[ks] = Contig<Tr>::zero();
             }
         }
+        float rowd[4] = {0.f, 0.f, 0.f, 0.f}, rsum[4] = {0.f, 0.f, 0.f, 0.f}, rsp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) apv[ct][e] = 0.f;
+            const int i = 16 * ct + nn;
+            if (ct > wave) {                           // uniform: above the diagonal blocks
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x1[(r0 + e) * XS + i] = Tr::from_f(0.f);
+                    x2a[(r0 + e) * XS + i] = Tr::from_f(0.f);
+                }
+                continue;
+            }
+            const float lmi = sLM[i], eti = sEt[i];
+            // Psi rows r and r - 1 (fp32 matrix cores; E, F formed on the fly)
+            floatx4 ps = zero4(), pp = zero4();
+            for (int ks = 4 * ct; ks < 4 * wave + 4; ++ks) {
+                const int j = 4 * ks + g;
+                const float lj = sLA[j];
+                const float bf = (i <= j) ? sBe[j] * expf(sLM[j] - lmi) : 0.f;
+                const float a = (j <= rA) ? expf(laA - lj) : 0.f;
+                const float ap = (j <= rA - 1) ? expf(laP - lj) : 0.f;
+                ps = F32::mma(a, bf, ps);
+                pp = F32::mma(ap, bf, pp);
+            }
+            floatx4 aqk = zero4(), akk = zero4(), ao = zero4(), aw = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                const frag bK = Contig<Tr>::load(Kl + i * D, ks, g);
+                const frag bV = (i < vm) ? Contig<Tr>::load(Vt + (rowbase + i) * D, ks, g) : Contig<Tr>::zero();
+                aqk = Tr::mma(aQ[ks], bK, aqk);
+                akk = Tr::mma(aK[ks], bK, akk);
+                ao = Tr::mma(aO[ks], bV, ao);
+                aw = Tr::mma(aW[ks], bV, aw);
+            }
+            float csum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = r0 + e;
+                const float al = sAl[r];
+                const bool low = i <= r, strict = i < r;
+                const float x1v = low ? ao[e] * ps[e] * eti : 0.f;
+                const float x2v = strict ? -aw[e] * pp[e] * eti : 0.f;
+                const float dg0 = low ? ao[e] * aqk[e] : 0.f;
+                const float ap = strict ? -aw[e] * al * akk[e] : 0.f;
+                x1[r * XS + i] = Tr::from_f(x1v);
+                x2a[r * XS + i] = Tr::from_f(al * x2v);
+                fDG[r * FS + i] = dg0;
+                apv[ct][e] = ap;
+                rowd[e] += x2v * akk[e];               // k_r . (X2 K)_r
+                // DGamma o Psi: the own entry, and the row-above entry of ap
+                rsum[e] += dg0 * eti * ps[e];
+                rsp[e] += ap * eti * pp[e];
+                csum += dg0 * ps[e] + ap * pp[e];
+                if (r == LR && low) {                  // DgS enters DGamma at the last row
+                    rsum[e] += sDgS[i] * eti * ps[e];
+                    csum += sDgS[i] * ps[e];
+                }
+            }
+            atomicAdd(&sCol[i], csum);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int sft = 8; sft >= 1; sft >>= 1) {
+                rowd[e] += __shfl_xor(rowd[e], sft, 64);
+                rsum[e] += __shfl_xor(rsum[e], sft, 64);
+                rsp[e] += __shfl_xor(rsp[e], sft, 64);
+            }
+        }
+        if (nn == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sAd[r0 + e] = rowd[e];
+                atomicAdd(&sRow[r0 + e], rsum[e]);
+                if (r0 + e > 0) atomicAdd(&sRow[r0 + e - 1], rsp[e]);
+            }
+        }
+    }
+    __syncthreads();
+    // DGamma[r-1][i] += (dA o P K^T)[r][i];  DGamma[L][i] += DgS_i
+    if (wave < NCT) {
         const int r0 = 16 * wave + 4 * g;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            floatx4 aqk = zero4(), akk = zero4(), ao = zero4(), aw = zero4();
-            if (ct <= wave) {
-                const int cB = 16 * ct + nn;
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) {
-                    const frag bK = Contig<Tr>::load(Kl + cB * D, ks, g);
-                    const frag bV = (cB < vm) ? Contig<Tr>::load(Vt + (rowbase + cB) * D, ks, g) : Contig<Tr>::zero();
-                    aqk = Tr::mma(aQ[ks], bK, aqk);
-                    akk = Tr::mma(aK[ks], bK, akk);
-                    ao = Tr::mma(aO[ks], bV, ao);
-                    aw = Tr::mma(aW[ks], bV, aw);
-                }
-            }
+            if (ct > wave) continue;
             const int i = 16 * ct + nn;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = r0 + e;
-                fQK[r * FS + i] = aqk[e];
-                fPK[r * FS + i] = sAl[r] * akk[e];
-                fAq[r * FS + i] = ao[e];
-                fAw[r * FS + i] = aw[e];
-            }
-        }
-    }
-    // ---- 3. Psi = E Diag(beta) F on the fp32 matrix cores ----------------------
-    if (wave < NCT) {
-        const int rA = 16 * wave + nn, r0 = 16 * wave + 4 * g;
-        const float laA = sLA[rA];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            floatx4 acc = zero4();
-            if (ct <= wave) {
-                const int i = 16 * ct + nn;
-                const float lmi = sLM[i];
-                for (int ks = 4 * ct; ks < 4 * wave + 4; ++ks) {
-                    const int j = 4 * ks + g;
-                    const float a = (j <= rA) ? expf(laA - sLA[j]) : 0.f;
-                    const float b = (i <= j) ? sBe[j] * expf(sLM[j] - lmi) : 0.f;
-                    acc = F32::mma(a, b, acc);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) fPs[(r0 + e) * FS + 16 * ct + nn] = acc[e];
-        }
-    }
-    __syncthreads();
-
-    // ---- 4. X1, X2 and DGamma (values first, then the stores) -----------------
-    {
-        constexpr int PER = C * C / 256 > 0 ? C * C / 256 : 1;
-        float vX1[PER], vX2[PER], vDG[PER];
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            const int idx = tid + 256 * m;
-            vX1[m] = vX2[m] = vDG[m] = 0.f;
-            if (idx < C * C) {
-                const int r = idx / C, i = idx % C;
-                const float et = sEt[i];
-                if (i <= r) {
-                    const float gam = fPs[r * FS + i] * et;
-                    vX1[m] = fAq[r * FS + i] * gam;
-                    float dg = fAq[r * FS + i] * fQK[r * FS + i];
-                    if (r + 1 < C) dg -= fAw[(r + 1) * FS + i] * fPK[(r + 1) * FS + i];
-                    if (r == LR) dg += sDgS[i];
-                    vDG[m] = dg;
-                }
-                if (i < r) vX2[m] = -fAw[r * FS + i] * fPs[(r - 1) * FS + i] * et;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            const int idx = tid + 256 * m;
-            if (idx < C * C) {
-                const int r = idx / C, i = idx % C;
-                fQK[r * FS + i] = vDG[m];
-                x1[r * XS + i] = Tr::from_f(vX1[m]);
-                x1t[i * XS + r] = Tr::from_f(vX1[m]);
-                x2[r * XS + i] = Tr::from_f(vX2[m]);
-                x2t[i * XS + r] = Tr::from_f(vX2[m] * sAl[r]);
+                if (i < r) fDG[(r - 1) * FS + i] += apv[ct][e];
+                if (r == LR) fDG[r * FS + i] += sDgS[i];
             }
         }
     }
     __syncthreads();
-    float* fDG = fQK;
 
-    // ---- 5. Z: G = E^T (DGamma Diag(eta)) on the fp32 matrix cores, G o F row sums
+    // ---- 3. Z: G = E^T (DGamma Diag(eta)) on the fp32 matrix cores, G o F row sums
     if (wave < NCT) {
         const int mA = 16 * wave + nn, m0 = 16 * wave + 4 * g;
         const float laA = sLA[mA];
@@ -891,26 +902,35 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
             if (nn == 0) sZ[m0 + e] = zp[e];
         }
     }
+    // the b part of Z, mubar_m sum_{r >= m} E[r,m] Db_r: a spare wave, or
+    // the last one (which has the fewest Z steps)
+    if (wave == (NCT < 4 ? NCT : 3) && lane < C) {
+        const int m = lane;
+        float sz = 0.f;
+        for (int r = m; r < C; ++r) sz += expf(sLA[r] - sLA[m]) * sDb[r];
+        sZb[m] = sz * expf(sLM[m]);
+    }
 
-    // ---- 6. dq, dk: X1 K, X1^T Q + (Diag(alpha) X2)^T K + Diag(alpha) X2 K ------
+    // ---- 4. dq, dk: X1 K, X1^T Q + (Diag(alpha) X2)^T K + Diag(alpha) X2 K -----
     if (wave < NCT) {
         const int rA = 16 * wave + nn, r0 = 16 * wave + 4 * g;
+        const char* X1c = reinterpret_cast<const char*>(x1);
+        const char* X2c = reinterpret_cast<const char*>(x2a);
         frag a1[KSC], a1t[KSC], a2[KSC], a2t[KSC];
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
             a1[ks] = SlotRow<Tr>::load(x1 + rA * XS, ks, g);
-            a1t[ks] = SlotRow<Tr>::load(x1t + rA * XS, ks, g);
-            a2[ks] = SlotRow<Tr>::load(x2 + rA * XS, ks, g);
-            a2t[ks] = SlotRow<Tr>::load(x2t + rA * XS, ks, g);
+            a2[ks] = SlotRow<Tr>::load(x2a + rA * XS, ks, g);
+            a1t[ks] = ColOperand<Tr, XS>::load(X1c, wave, ks, lane);
+            a2t[ks] = ColOperand<Tr, XS>::load(X2c, wave, ks, lane);
         }
         const char* Qc = reinterpret_cast<const char*>(Ql);
         const char* Kc = reinterpret_cast<const char*>(Kl);
-        float pad[4] = {0.f, 0.f, 0.f, 0.f};
         const float* qp = dqp + (tile * C + r0) * D;
         const float* kp = dkp + (tile * C + r0) * D;
 #pragma unroll
         for (int ct = 0; ct < NDH; ++ct) {
-            floatx4 aq = zero4(), ak = zero4(), x2k = zero4();
+            floatx4 aq = zero4(), ak = zero4();
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
                 const frag bK = ColOperand<Tr, D>::load(Kc, ct, ks, lane);
@@ -918,62 +938,31 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 aq = Tr::mma(a1[ks], bK, aq);
                 ak = Tr::mma(a1t[ks], bQ, ak);
                 ak = Tr::mma(a2t[ks], bK, ak);
-                x2k = Tr::mma(a2[ks], bK, x2k);
+                ak = Tr::mma(a2[ks], bK, ak);
             }
             const int c = 16 * ct + nn;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = r0 + e;
-                const float kv = Tr::to_f(Kl[r * D + c]);
-                pad[e] += kv * x2k[e];
-                const float vq = aq[e] + qp[e * D + c];
-                const float vk = ak[e] + sAl[r] * x2k[e] + kp[e * D + c];
                 if (r < vm) {
-                    dq[(rowbase + r) * D + c] = Tr::from_f(vq);
-                    dk[(rowbase + r) * D + c] = Tr::from_f(vk);
+                    dq[(rowbase + r) * D + c] = Tr::from_f(aq[e] + qp[e * D + c]);
+                    dk[(rowbase + r) * D + c] = Tr::from_f(ak[e] + kp[e * D + c]);
                 }
             }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-#pragma unroll
-            for (int s = 8; s >= 1; s >>= 1) pad[e] += __shfl_xor(pad[e], s, 64);
-            if (nn == 0) sAd[r0 + e] = pad[e];
         }
     }
     __syncthreads();
 
-    // ---- 7. the gate gradients ------------------------------------------------
-    // row sums of DGamma Diag(eta) o Psi (threads 0..C-1), column sums of
-    // DGamma o Psi (threads 64..64+C-1), the b part of Z (threads 128..)
-    if (tid < C) {
-        const int m = tid;
-        float s = 0.f;
-        for (int i = 0; i <= m; ++i) s += fDG[m * FS + i] * sEt[i] * fPs[m * FS + i];
-        sMisc[8 + m] = s;
-    } else if (tid >= 64 && tid < 64 + C) {
-        const int i = tid - 64;
-        float s = 0.f;
-        for (int r = i; r < C; ++r) s += fDG[r * FS + i] * fPs[r * FS + i];
-        sMisc[8 + C + i] = s;
-    } else if (tid >= 128 && tid < 128 + C) {
-        const int m = tid - 128;
-        float s = 0.f;
-        for (int r = m; r < C; ++r) s += expf(sLA[r] - sLA[m]) * sDb[r];
-        sMisc[8 + 2 * C + m] = s * expf(sLM[m]);
-    }
-    __syncthreads();
+    // ---- 5. the gate gradients ------------------------------------------------
     if (wave == 0) {
         const int m = lane;
         const bool in = m < C;
-        float dla = 0.f, dlm = 0.f, z = 0.f, de = 0.f;
-        float tail = 0.f;
+        float dla = 0.f, dlm = 0.f, z = 0.f, de = 0.f, tail = 0.f;
         if (in) {
-            z = sZ[m] + sMisc[8 + 2 * C + m];
-            const float cs = sMisc[8 + C + m];
-            const float gmL = expf(sLM[LR] - sLM[m]);
-            de = cs + sDgM[m] * gmL;
-            dla = sMisc[8 + m] + sDb[m] * sB[m] - sBe[m] * z + sDa[m] * sAb[m];
+            z = sZ[m] + sZb[m];
+            const float cs = sCol[m];
+            de = cs + sDgM[m] * expf(sLM[LR] - sLM[m]);
+            dla = sRow[m] + sDb[m] * sB[m] - sBe[m] * z + sDa[m] * sAb[m];
             dlm = sBe[m] * z - sEt[m] * cs - sDgM[m] * sGM[m];
             tail = sDgM[m] * sGM[m];
         }
@@ -1052,10 +1041,16 @@ static hipError_t bwd_dispatch(const BwdArgs& a)
         switch (a.f.dk * 1000 + a.f.C) {
         case 16016: return launch_bwd_t<Tr, 16, 16>(a);
         case 16032: return launch_bwd_t<Tr, 16, 32>(a);
+        case 16064: return launch_bwd_t<Tr, 16, 64>(a);
         case 32016: return launch_bwd_t<Tr, 32, 16>(a);
         case 32032: return launch_bwd_t<Tr, 32, 32>(a);
+        case 32064: return launch_bwd_t<Tr, 32, 64>(a);
         case 64016: return launch_bwd_t<Tr, 64, 16>(a);
         case 64032: return launch_bwd_t<Tr, 64, 32>(a);
+        case 64064: return launch_bwd_t<Tr, 64, 64>(a);
+        case 128016: return launch_bwd_t<Tr, 128, 16>(a);
+        case 128032: return launch_bwd_t<Tr, 128, 32>(a);
+        case 128064: return launch_bwd_t<Tr, 128, 64>(a);
         default: return hipErrorInvalidValue;
         }
     }

@@ -293,14 +293,14 @@ def test_bwd_workspace_bytes(L):
               + tiles * 8 * C * 4)
     assert mdn.chunk_bwd_workspace_bytes(B, H, T, d, d, C, mdn.MDN_BF16) == expect
     bad = ctypes.c_size_t(-1).value
-    assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0) == bad     # fp32 needs d <= 64
-    assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 64, 64, 64, 0) == bad       # and C <= 32
+    assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 48, 48, 16, 0) == bad
     assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 16, 16, 32, 1) == bad       # bf16 needs d >= 32
+    assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 128, 128, 16, 1) == bad     # and C >= 32
 
 
 def test_bwd_validation(L):
     assert bwd_call(L, d=48) == UNSUPPORTED
-    assert bwd_call(L, dt=0, d=128, C=64) == UNSUPPORTED
+    assert bwd_call(L, dt=1, d=16, C=32) == UNSUPPORTED
     assert bwd_call(L, T=-1) == BAD_SHAPE
     assert bwd_call(L, B=0, ptrs=[None] * 22) == OK
     p = addrs(22)

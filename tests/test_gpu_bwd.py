@@ -49,7 +49,8 @@ def check(got, ref, tol, label):
         assert e <= tol, (label, n, e)
 
 
-@pytest.mark.parametrize("d,C,T", [(16, 16, 50), (32, 32, 70), (64, 16, 40), (64, 32, 64), (16, 32, 33)])
+@pytest.mark.parametrize("d,C,T", [(16, 16, 50), (32, 32, 70), (64, 16, 40), (64, 32, 64), (16, 32, 33),
+                                   (64, 64, 130), (128, 64, 100), (128, 16, 50), (32, 64, 64)])
 def test_bwd_fp32_small(d, C, T):
     x = inputs.make_chunk_inputs(1, 2, T, d, C=C, dtype="f32", seed=d + C + T, state_std=0.3)
     dO, dST, dMT = upstream(x, d + T)
