@@ -99,6 +99,41 @@ template <> struct SlotRow<TraitsF32> {
     }
 };
 
+// Sum over the 16 lanes of a row (lanes 16g .. 16g+15) on DPP row shifts:
+// lane 16g + 15 ends with the row's sum.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp_move<DPP_ROW_SHR1>(x, 0.f);
+    x += dpp_move<DPP_ROW_SHR2>(x, 0.f);
+    x += dpp_move<DPP_ROW_SHR4>(x, 0.f);
+    x += dpp_move<DPP_ROW_SHR8>(x, 0.f);
+    return x;
+}
+
+// A chain wave's 16-column slice of a D x D state (accumulator tiles t,
+// rows perm(16t + 4g + e), column nn) to rows of a row-major [D][D] array,
+// through an LDS tile so that every global store is 16 bytes.
+template <typename Tr, int D>
+__device__ __forceinline__ void store_slice(const floatx4 (&X)[D / 16], typename Tr::elem* __restrict__ lt,
+                                            typename Tr::elem* __restrict__ dst, int lane)
+{
+    using E = typename Tr::elem;
+    using SL = Slots<Tr>;
+    constexpr int EPV = 16 / sizeof(E), PPR = 16 / EPV, NP = D * PPR;
+    const int g = lane >> 4, nn = lane & 15;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lt[SL::perm(16 * t + 4 * g + e) * 16 + nn] = Tr::from_f(X[t][e]);
+#pragma unroll
+    for (int i = 0; i < (NP + 63) / 64; ++i) {
+        const int p = i * 64 + lane;
+        if (NP % 64 == 0 || p < NP) {
+            const int r = p / PPR, c = (p % PPR) * EPV;
+            *reinterpret_cast<uint4*>(dst + (size_t)r * D + c) = reinterpret_cast<const uint4*>(lt)[p];
+        }
+    }
+}
+
 // Each contraction slot of an operand scaled by its own factor.
 template <typename Tr> struct FragScale;
 template <> struct FragScale<TraitsBf16> {
@@ -143,6 +178,7 @@ void mdn_bwd_replay_kernel(const typename Tr::elem* __restrict__ k, const typena
     constexpr int NSL = SL::NSLOT, KSC = C / Tr::KW, NDH = D / 16, SLABS = D / (16 * NCOL), OW = 16 * NCOL;
     __shared__ __attribute__((aligned(16))) char stA[LT::BUF];
     __shared__ __attribute__((aligned(16))) char stB[LT::BUF];
+    __shared__ __attribute__((aligned(16))) E stg[NCOL][2][D * 16];   // state slices on their way out
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, nn = lane & 15;
@@ -195,16 +231,11 @@ void mdn_bwd_replay_kernel(const typename Tr::elem* __restrict__ k, const typena
         const char* Vl = cur + LT::V0;
         const float* cf = reinterpret_cast<const float*>(cur + LT::CF0);
         // the chunk-start state of chunk n
-        E* so = Sst + ((size_t)bh * NT + n) * D * D;
-        E* mo = Mst + ((size_t)bh * NT + n) * D * D;
-#pragma unroll
-        for (int t = 0; t < NDH; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const size_t off = (size_t)SL::perm(16 * t + 4 * g + e) * D + col;
-                so[off] = Tr::from_f(XS[t][e]);
-                mo[off] = Tr::from_f(XM[t][e]);
-            }
+        {
+            const size_t off = ((size_t)bh * NT + n) * D * D + col0 + 16 * ct;
+            store_slice<Tr, D>(XS, stg[ct][0], Sst + off, lane);
+            store_slice<Tr, D>(XM, stg[ct][1], Mst + off, lane);
+        }
         const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
         const float bC = cf[MDN_COEF_B * C + C - 1];
         const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
@@ -252,7 +283,9 @@ struct CarryLayout {
     static constexpr int O0 = AT0 + C * PT * 16;
     static constexpr int CF0 = O0 + C * PV * 16;
     static constexpr int BUF = CF0 + PC * 16;
-    static constexpr int TOTAL = NBUF * BUF;
+    static constexpr int SR = D > C ? D : C;          // staging rows: adjoint slices and dV rows
+    static constexpr int STG = NCOL * 2 * SR * 16 * ES;
+    static constexpr int TOTAL = NBUF * BUF + STG;
 };
 
 template <typename Tr, int D, int C>
@@ -281,6 +314,7 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
     constexpr int SLABS = D / (16 * NCOL), OW = 16 * NCOL;
     __shared__ __attribute__((aligned(16))) char stA[LT::BUF];
     __shared__ __attribute__((aligned(16))) char stB[NBUF == 2 ? LT::BUF : 16];
+    __shared__ __attribute__((aligned(16))) E stg[NCOL][2][LT::SR * 16];   // adjoint slices, dV rows on their way out
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, nn = lane & 15;
@@ -359,16 +393,9 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
 
         // the chunk-end adjoints of chunk n
         {
-            E* so = dSst + tile * D * D;
-            E* mo = dMst + tile * D * D;
-#pragma unroll
-            for (int t = 0; t < NDH; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const size_t off = (size_t)SL::perm(16 * t + 4 * g + e) * D + col;
-                    so[off] = Tr::from_f(XS[t][e]);
-                    mo[off] = Tr::from_f(XM[t][e]);
-                }
+            const size_t off = tile * D * D + col0 + 16 * ct;
+            store_slice<Tr, D>(XS, stg[ct][0], dSst + off, lane);
+            store_slice<Tr, D>(XM, stg[ct][1], dMst + off, lane);
         }
         // dvt = Aqk^T dO + Diag(gS) K dS - Diag(gM) K dM
         floatx4 dV[NCT];
@@ -415,14 +442,21 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
             }
         }
         {
-            E* dst = dv + ((size_t)bh * T + n * C) * D + col;
+            // dV rows of the chunk: C x 16 through the first staging tile
+            E* lt = stg[ct][0];
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = SL::perm(16 * tc + 4 * g + e);
-                    if (r < vm) dst[(size_t)r * D] = Tr::from_f(dW[tc][e]);
-                }
+                for (int e = 0; e < 4; ++e) lt[SL::perm(16 * tc + 4 * g + e) * 16 + nn] = Tr::from_f(dW[tc][e]);
+            constexpr int EPV = 16 / sizeof(E), PPR = 16 / EPV, NP = C * PPR;
+            E* dst = dv + ((size_t)bh * T + n * C) * D + col0 + 16 * ct;
+#pragma unroll
+            for (int i = 0; i < (NP + 63) / 64; ++i) {
+                const int p = i * 64 + lane;
+                const int r = p / PPR, c = (p % PPR) * EPV;
+                if ((NP % 64 == 0 || p < NP) && r < vm)
+                    *reinterpret_cast<uint4*>(dst + (size_t)r * D + c) = reinterpret_cast<const uint4*>(lt)[p];
+            }
         }
         // chunk-start adjoints
         const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
@@ -608,11 +642,8 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
 #pragma unroll
             for (int a = 0; a < 5; ++a)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-#pragma unroll
-                    for (int sft = 8; sft >= 1; sft >>= 1) pd[a][e] += __shfl_xor(pd[a][e], sft, 64);
-                }
-            if (nn == 0) {
+                for (int e = 0; e < 4; ++e) pd[a][e] = row_sum16(pd[a][e]);
+            if (nn == 15) {
 #pragma unroll
                 for (int a = 0; a < 5; ++a)
 #pragma unroll
@@ -839,14 +870,11 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-#pragma unroll
-            for (int sft = 8; sft >= 1; sft >>= 1) {
-                rowd[e] += __shfl_xor(rowd[e], sft, 64);
-                rsum[e] += __shfl_xor(rsum[e], sft, 64);
-                rsp[e] += __shfl_xor(rsp[e], sft, 64);
-            }
+            rowd[e] = row_sum16(rowd[e]);
+            rsum[e] = row_sum16(rsum[e]);
+            rsp[e] = row_sum16(rsp[e]);
         }
-        if (nn == 0) {
+        if (nn == 15) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 sAd[r0 + e] = rowd[e];
@@ -897,9 +925,8 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-#pragma unroll
-            for (int s = 8; s >= 1; s >>= 1) zp[e] += __shfl_xor(zp[e], s, 64);
-            if (nn == 0) sZ[m0 + e] = zp[e];
+            zp[e] = row_sum16(zp[e]);
+            if (nn == 15) sZ[m0 + e] = zp[e];
         }
     }
     // the b part of Z, mubar_m sum_{r >= m} E[r,m] Db_r: a spare wave, or
