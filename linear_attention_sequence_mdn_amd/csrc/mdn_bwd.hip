@@ -165,7 +165,7 @@ struct ReplayLayout {
 };
 
 template <typename Tr, int D, int C, int NCOL>
-__global__ __launch_bounds__(64 * (NCOL + 2))
+__global__ __launch_bounds__(64 * (NCOL + 4))
 void mdn_bwd_replay_kernel(const typename Tr::elem* __restrict__ k, const typename Tr::elem* __restrict__ Vt,
                            const float* __restrict__ coef, const float* __restrict__ S0,
                            const float* __restrict__ M0, typename Tr::elem* __restrict__ Sst,
@@ -194,13 +194,14 @@ void mdn_bwd_replay_kernel(const typename Tr::elem* __restrict__ k, const typena
             const unsigned vlast = (unsigned)valid_of(m) - 1;
             auto seq_row = [&](unsigned r) { return (r < vlast ? r : vlast) * (unsigned)(D * LT::ES); };
             auto cf_row = [](unsigned) { return 0u; };
-            if (lw == 0) {
-                dma_tile<C, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rb * D), seq_row, lane);
-            } else {
+            // four loaders: K by rows, the vtilde slab and the coefficients
+            constexpr int RPL = C / 4;
+            dma_tile<RPL, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rb * D), seq_row, lane, lw * RPL);
+            if (lw == 0)
                 dma_plain<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(Vt + rb * D + col0), seq_row, lane);
+            else if (lw == 1)
                 dma_plain<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
                                      cf_row, lane);
-            }
         };
         const uint32_t aA = lds_addr(stA), aB = lds_addr(stB);
         if (NT > 0) issue(aA, 0);
@@ -297,7 +298,7 @@ struct CarryPick {
 };
 
 template <typename Tr, int D, int C, int NCOL, int NBUF>
-__global__ __launch_bounds__(64 * (NCOL + 2))
+__global__ __launch_bounds__(64 * (NCOL + 4))
 void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typename Tr::elem* __restrict__ k,
                           const typename Tr::elem* __restrict__ TT, const typename Tr::elem* __restrict__ AT,
                           const float* __restrict__ coef, const typename Tr::elem* __restrict__ dO,
@@ -332,16 +333,18 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
             auto seq_row = [&](unsigned r) { return (r < vlast ? r : vlast) * (unsigned)(D * LT::ES); };
             auto t_row = [](unsigned r) { return r * (unsigned)(C * LT::ES); };
             auto cf_row = [](unsigned) { return 0u; };
-            if (lw == 0) {
-                dma_tile<C, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rb * D), seq_row, lane);
-                dma_tile<C, LT::PK>(buf + LT::Q0, reinterpret_cast<const char*>(q + rb * D), seq_row, lane);
+            // four loaders: K, Q, T^T and Aqk^T by rows; the dO slab; the coefficients
+            constexpr int RPL = C / 4;
+            const int r0 = lw * RPL;
+            dma_tile<RPL, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rb * D), seq_row, lane, r0);
+            dma_tile<RPL, LT::PK>(buf + LT::Q0, reinterpret_cast<const char*>(q + rb * D), seq_row, lane, r0);
+            dma_tile<RPL, LT::PT>(buf + LT::TT0, reinterpret_cast<const char*>(TT + tile * C * C), t_row, lane, r0);
+            dma_tile<RPL, LT::PT>(buf + LT::AT0, reinterpret_cast<const char*>(AT + tile * C * C), t_row, lane, r0);
+            if (lw == 2)
+                dma_plain<C, LT::PV>(buf + LT::O0, reinterpret_cast<const char*>(dO + rb * D + col0), seq_row, lane);
+            else if (lw == 3)
                 dma_plain<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
                                      cf_row, lane);
-            } else {
-                dma_tile<C, LT::PT>(buf + LT::TT0, reinterpret_cast<const char*>(TT + tile * C * C), t_row, lane);
-                dma_tile<C, LT::PT>(buf + LT::AT0, reinterpret_cast<const char*>(AT + tile * C * C), t_row, lane);
-                dma_plain<C, LT::PV>(buf + LT::O0, reinterpret_cast<const char*>(dO + rb * D + col0), seq_row, lane);
-            }
         };
         const uint32_t aA = lds_addr(stA), aB = lds_addr(stB);
         if constexpr (NBUF == 2) {
@@ -522,7 +525,7 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
 // the same operands.
 // ---------------------------------------------------------------------------
 template <typename Tr, int D, int C>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typename Tr::elem* __restrict__ k,
                           const typename Tr::elem* __restrict__ Vt, const typename Tr::elem* __restrict__ dO,
                           const typename Tr::elem* __restrict__ dW, const float* __restrict__ coef,
@@ -536,9 +539,9 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     constexpr int ES = sizeof(E);
     constexpr int NCT = C / 16, NDH = D / 16, KSD = D / Tr::KW;
     constexpr int CPW = NDH >= 4 ? NDH / 4 : 1;       // column tiles per wave
-    constexpr int PK = D * ES / 16, TB = C * PK * 16;
-    __shared__ __attribute__((aligned(16))) char st[3 * TB];   // dO, dW, vtilde rows (swizzled)
-    __shared__ float rv[4][5][C];                                // per-wave row dots
+    constexpr int PK = D * ES / 16, TB = C * PK * 16, PC = MDN_COEF_ROWS * C * 4 / 16;
+    __shared__ __attribute__((aligned(16))) char st[3 * TB + PC * 16];   // dO, dW, vtilde rows (swizzled), coefficients
+    __shared__ float rv[5][C];                                   // row dots
     __shared__ float red[4][3];
 
     const int64_t tile = blockIdx.x;
@@ -561,8 +564,10 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         if (wave == 0) dma_tile<C, PK>(base, reinterpret_cast<const char*>(dO + rowbase * D), seq_row, lane);
         else if (wave == 1) dma_tile<C, PK>(base + TB, reinterpret_cast<const char*>(dW + rowbase * D), seq_row, lane);
         else if (wave == 2) dma_tile<C, PK>(base + 2 * TB, reinterpret_cast<const char*>(Vt + rowbase * D), seq_row, lane);
+        else dma_plain<1, PC>(base + 3 * TB, reinterpret_cast<const char*>(cf), [](unsigned) { return 0u; }, lane);
     }
-    for (int i = tid; i < 4 * 5 * C; i += 256) (&rv[0][0][0])[i] = 0.f;
+    const float* cfl = reinterpret_cast<const float*>(st + 3 * TB);
+    for (int i = tid; i < 5 * C; i += 256) (&rv[0][0])[i] = 0.f;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -598,8 +603,21 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 ip2 = fmaf(bM[ks], bdM[ks], ip2);
             }
         }
+        // q and k at this lane's output positions, one row tile ahead
+        auto qk_load = [&](int rt, float (&qv)[4], float (&kv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + 4 * g + e;
+                qv[e] = r < vm ? Tr::to_f(q[(rowbase + r) * D + c]) : 0.f;
+                kv[e] = r < vm ? Tr::to_f(k[(rowbase + r) * D + c]) : 0.f;
+            }
+        };
+        float qcur[4], kcur[4];
+        qk_load(0, qcur, kcur);
 #pragma unroll
         for (int rt = 0; rt < NCT; ++rt) {
+            float qnx[4], knx[4];
+            if (rt + 1 < NCT) qk_load(rt + 1, qnx, knx);
             floatx4 oS = zero4(), wS = zero4(), oM = zero4(), wM = zero4(), vS = zero4(), vM = zero4();
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
@@ -614,11 +632,11 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 vM = Tr::mma(aV, bdM[ks], vM);
             }
             const int r0 = 16 * rt + 4 * g;
-            const floatx4 ca = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_ABAR * C + r0);
-            const floatx4 cb = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_B * C + r0);
-            const floatx4 cab = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_ABP * C + r0);
-            const floatx4 cgs = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_GS * C + r0);
-            const floatx4 cgm = *reinterpret_cast<const floatx4*>(cf + MDN_COEF_GM * C + r0);
+            const floatx4 ca = *reinterpret_cast<const floatx4*>(cfl + MDN_COEF_ABAR * C + r0);
+            const floatx4 cb = *reinterpret_cast<const floatx4*>(cfl + MDN_COEF_B * C + r0);
+            const floatx4 cab = *reinterpret_cast<const floatx4*>(cfl + MDN_COEF_ABP * C + r0);
+            const floatx4 cgs = *reinterpret_cast<const floatx4*>(cfl + MDN_COEF_GS * C + r0);
+            const floatx4 cgm = *reinterpret_cast<const floatx4*>(cfl + MDN_COEF_GM * C + r0);
             float* qo = dqp + (tile * C + r0) * D + c;
             float* ko = dkp + (tile * C + r0) * D + c;
             float pd[5][4];
@@ -631,8 +649,7 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 const float vs = m * vS[e], vmm = m * vM[e];
                 qo[e * D] = ca[e] * os - cb[e] * om;
                 ko[e * D] = -ca[e] * ws + cab[e] * wm + cgs[e] * vs - cgm[e] * vmm;
-                const float qv = in ? Tr::to_f(q[(rowbase + r) * D + c]) : 0.f;
-                const float kv = in ? Tr::to_f(k[(rowbase + r) * D + c]) : 0.f;
+                const float qv = qcur[e], kv = kcur[e];
                 pd[0][e] = qv * os - kv * ws;
                 pd[1][e] = -qv * om;
                 pd[2][e] = kv * wm;
@@ -647,7 +664,11 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
 #pragma unroll
                 for (int a = 0; a < 5; ++a)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) rv[wave][a][r0 + e] += pd[a][e];
+                    for (int e = 0; e < 4; ++e) atomicAdd(&rv[a][r0 + e], pd[a][e]);
+            }
+            if (rt + 1 < NCT) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { qcur[e] = qnx[e]; kcur[e] = knx[e]; }
             }
         }
     }
@@ -659,10 +680,7 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     }
     if (lane == 0) { red[wave][0] = ip0; red[wave][1] = ip1; red[wave][2] = ip2; }
     __syncthreads();
-    for (int i = tid; i < 5 * C; i += 256) {
-        const int a = i / C, r = i % C;
-        vt[a * C + r] = rv[0][a][r] + rv[1][a][r] + rv[2][a][r] + rv[3][a][r];
-    }
+    for (int i = tid; i < 5 * C; i += 256) vt[i] = (&rv[0][0])[i];
     if (tid < 3) vt[5 * C + tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
 }
 
@@ -807,6 +825,10 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
             }
         }
         float rowd[4] = {0.f, 0.f, 0.f, 0.f}, rsum[4] = {0.f, 0.f, 0.f, 0.f}, rsp[4] = {0.f, 0.f, 0.f, 0.f};
+        frag bVc[KSD];                                 // vtilde rows of column tile ct (B operand)
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+            bVc[ks] = (nn < vm) ? Contig<Tr>::load(Vt + (rowbase + nn) * D, ks, g) : Contig<Tr>::zero();
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
@@ -821,6 +843,14 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 continue;
             }
             const float lmi = sLM[i], eti = sEt[i];
+            // the vtilde rows of the next column tile, in flight meanwhile
+            frag bVn[KSD];
+            if (ct + 1 <= wave) {
+                const int inx = i + 16;
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+                    bVn[ks] = (inx < vm) ? Contig<Tr>::load(Vt + (rowbase + inx) * D, ks, g) : Contig<Tr>::zero();
+            }
             // Psi rows r and r - 1 (fp32 matrix cores; E, F formed on the fly)
             floatx4 ps = zero4(), pp = zero4();
             for (int ks = 4 * ct; ks < 4 * wave + 4; ++ks) {
@@ -836,11 +866,14 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
                 const frag bK = Contig<Tr>::load(Kl + i * D, ks, g);
-                const frag bV = (i < vm) ? Contig<Tr>::load(Vt + (rowbase + i) * D, ks, g) : Contig<Tr>::zero();
                 aqk = Tr::mma(aQ[ks], bK, aqk);
                 akk = Tr::mma(aK[ks], bK, akk);
-                ao = Tr::mma(aO[ks], bV, ao);
-                aw = Tr::mma(aW[ks], bV, aw);
+                ao = Tr::mma(aO[ks], bVc[ks], ao);
+                aw = Tr::mma(aW[ks], bVc[ks], aw);
+            }
+            if (ct + 1 <= wave) {
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) bVc[ks] = bVn[ks];
             }
             float csum = 0.f;
 #pragma unroll
@@ -955,8 +988,16 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         const char* Kc = reinterpret_cast<const char*>(Kl);
         const float* qp = dqp + (tile * C + r0) * D;
         const float* kp = dkp + (tile * C + r0) * D;
+        float pq[4], pk[4];                            // state-product parts, one column tile ahead
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { pq[e] = qp[e * D + nn]; pk[e] = kp[e * D + nn]; }
 #pragma unroll
         for (int ct = 0; ct < NDH; ++ct) {
+            float nq[4], nk[4];
+            if (ct + 1 < NDH) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { nq[e] = qp[e * D + 16 * (ct + 1) + nn]; nk[e] = kp[e * D + 16 * (ct + 1) + nn]; }
+            }
             floatx4 aq = zero4(), ak = zero4();
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
@@ -972,9 +1013,13 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
             for (int e = 0; e < 4; ++e) {
                 const int r = r0 + e;
                 if (r < vm) {
-                    dq[(rowbase + r) * D + c] = Tr::from_f(aq[e] + qp[e * D + c]);
-                    dk[(rowbase + r) * D + c] = Tr::from_f(ak[e] + kp[e * D + c]);
+                    dq[(rowbase + r) * D + c] = Tr::from_f(aq[e] + pq[e]);
+                    dk[(rowbase + r) * D + c] = Tr::from_f(ak[e] + pk[e]);
                 }
+            }
+            if (ct + 1 < NDH) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { pq[e] = nq[e]; pk[e] = nk[e]; }
             }
         }
     }
@@ -1023,14 +1068,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a)
     const ChunkArgs& f = a.f;
     constexpr int NCOL = D >= 32 ? 2 : 1;
     const int64_t grid = f.BH * (D / (16 * NCOL));
-    hipLaunchKernelGGL((mdn_bwd_replay_kernel<Tr, D, C, NCOL>), dim3((unsigned)grid), dim3(64 * (NCOL + 2)), 0,
+    hipLaunchKernelGGL((mdn_bwd_replay_kernel<Tr, D, C, NCOL>), dim3((unsigned)grid), dim3(64 * (NCOL + 4)), 0,
                        (hipStream_t)f.stream, (const E*)f.k, (const E*)a.Vt, f.coef, f.S0, f.M0,
                        (E*)a.Sst, (E*)a.Mst, f.T, f.NT, (int)f.BH);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     using CP = CarryPick<Tr, D, C>;
     hipLaunchKernelGGL((mdn_bwd_carry_kernel<Tr, D, C, CP::NCOL, CP::NBUF>), dim3((unsigned)grid),
-                       dim3(64 * (CP::NCOL + 2)), 0, (hipStream_t)f.stream, (const E*)f.q, (const E*)f.k,
+                       dim3(64 * (CP::NCOL + 4)), 0, (hipStream_t)f.stream, (const E*)f.q, (const E*)f.k,
                        (const E*)f.Tmat, (const E*)f.Aqk, f.coef, (const E*)a.dO, a.dST, a.dMT, (E*)a.dv,
                        (E*)a.dSst, (E*)a.dMst, a.dS0, a.dM0, f.T, f.NT, (int)f.BH);
     e = hipGetLastError();
