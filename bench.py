@@ -46,6 +46,7 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 # FLOP per token*head of the whole chunk forward (d = 128, C = 64), counting
 # only the causal triangles: 12 d^2 + 6 C d + (2/3) C^2.
 F_TOKEN_HEAD = 248_491
+F_TOKEN_HEAD_FULL = 297_643       # the same work counting full C x C tiles
 
 
 def parse():
@@ -182,8 +183,12 @@ def chunk_bench(args, torch, mdn, inputs):
                  "source_sha": sha})
     tps = tokens / (ms_step / 1e3)
     mfma_frac = tps * H * F_TOKEN_HEAD / (PEAK_BF16_TFLOPS * 1e12)
+    # the whole call's ideal HBM traffic: q, k, v, the gates, O and vtilde per
+    # token-head, the final states (and the initial ones when given) per head
+    call_bytes = tok_head * (3 * d * es + 16 + 2 * d * es) + B * H * nstate * d * d * 4
+    hbm_cap = tokens / (call_bytes / (PEAK_HBM_GBS * 1e9))
     return dict(ms_step=ms_step, tokens_per_s=tps, mfma_frac=mfma_frac, kernels=kernels,
-                roofline=roof, finite=finite, x=x, cfg=cfg, call=call)
+                roofline=roof, finite=finite, x=x, cfg=cfg, call=call, call_bytes=call_bytes, hbm_cap=hbm_cap)
 
 
 def decode_bench(args, torch, mdn, inputs):
@@ -226,12 +231,26 @@ def decode_bench(args, torch, mdn, inputs):
     ms = float(np.median(times))
     bytes_step = B * H * (16 * d * d + 2 * (2 * d + d) + 16 + 2 * d)
     gbs = n * bytes_step / (ms / 1e3) / 1e9
+    # a device-to-device copy of the state's size, the same way, as the
+    # attainable bandwidth next to the peak
+    src = torch.empty(2 * B * H * d * d, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
     sha = kernel_sources_sha(["mdn_step.hip", "mdn_device.h"])
     traffic = load_traffic("traffic_mdn_step_kernel_decode.md", sha)
     return {"metric": "decode GB/s", "value": gbs, "unit": "GB/s",
             "workload": f"decode B{B} H{H} d{d} bf16, {n} consecutive mdn_step calls",
             "ms_per_decode_step": ms / n, "reps": args.decode_reps,
-            "alg_bytes_per_step": bytes_step,
+            "alg_bytes_per_step": bytes_step, "copy_GBps": copy_gbs, "frac_of_copy": gbs / copy_gbs,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "kernel": "mdn_step_kernel",
                          "source_sha": sha}}
@@ -410,6 +429,9 @@ def main():
                     "config": {"workload": WORKLOAD_NAMES[args.workload], "B": x.B, "H": x.H, "T": x.T,
                                "dk": x.dk, "dv": x.dv, "C": x.C, "tokens_per_step": x.B * x.T},
                     "mfma_frac_of_bf16_peak": ch["mfma_frac"], "flop_per_token_head": F_TOKEN_HEAD,
+                    "mfma_frac_full_tiles": ch["mfma_frac"] * F_TOKEN_HEAD_FULL / F_TOKEN_HEAD,
+                    "call_alg_bytes": ch["call_bytes"], "hbm_capped_tokens_per_s": ch["hbm_cap"],
+                    "frac_of_hbm_cap": ch["tokens_per_s"] / ch["hbm_cap"],
                     "kernels": ch["kernels"], "roofline": ch["roofline"], "outputs_finite": ch["finite"]})
     if not args.no_decode:
         out["decode"] = decode_bench(args, torch, mdn, inputs)
