@@ -568,6 +568,20 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     }
     const float* cfl = reinterpret_cast<const float*>(st + 3 * TB);
     for (int i = tid; i < 5 * C; i += 256) (&rv[0][0])[i] = 0.f;
+    // the first column tile's state operands are issued before the wait, so
+    // that they travel with the staging copies
+    frag bS[KSD], bM[KSD], bdS[KSD], bdM[KSD];
+    auto load_states = [&](int ct) __attribute__((always_inline)) {
+        const size_t ro = (size_t)(16 * ct + nn) * D;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            bS[ks] = SlotRow<Tr>::load(S + ro, ks, g);
+            bM[ks] = SlotRow<Tr>::load(M + ro, ks, g);
+            bdS[ks] = SlotRow<Tr>::load(dS + ro, ks, g);
+            bdM[ks] = SlotRow<Tr>::load(dM + ro, ks, g);
+        }
+    };
+    if (wave * CPW < NDH) load_states(wave * CPW);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -577,14 +591,7 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         const int ct = wave * CPW + cc;
         if (ct >= NDH) break;                         // uniform
         const int c = 16 * ct + nn;                   // dk column of this lane's outputs / state row
-        frag bS[KSD], bM[KSD], bdS[KSD], bdM[KSD];
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-            bS[ks] = SlotRow<Tr>::load(S + (size_t)c * D, ks, g);
-            bM[ks] = SlotRow<Tr>::load(M + (size_t)c * D, ks, g);
-            bdS[ks] = SlotRow<Tr>::load(dS + (size_t)c * D, ks, g);
-            bdM[ks] = SlotRow<Tr>::load(dM + (size_t)c * D, ks, g);
-        }
+        if (cc > 0) load_states(ct);
         // the state inner products over these rows
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
