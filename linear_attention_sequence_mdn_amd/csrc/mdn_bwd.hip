@@ -813,11 +813,59 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         if (r == LR) sDa[r] += sMisc[0];
     }
 
-    // ---- 2. per row block (wave): Psi, the C x C products and what they feed --
+    // ---- 1b. Psi = E Diag(beta) F by its column recurrence ---------------------
+    // Psi[r][i] = alpha_r Psi[r-1][i] + beta_r w_{r,i},  w_{r,i} = mubar_r / mubar_i
+    // (w_{i,i} = 1, w_{r,i} = mu_r w_{r-1,i}); wave w runs rows [16w, 16w + 16)
+    // of column i = lane from zero and the carry of the blocks above enters
+    // scaled by their alpha products.  Psi is lower triangular with diagonal
+    // beta, DGamma is lower triangular: Psi[r][i] (r > i) is kept at
+    // fDG[i][r], the strictly upper triangle of the DGamma table.
+    {
+        float* xe = reinterpret_cast<float*>(lds + L::X0);    // [NCT][C] block ends (X1 comes later)
+        float* xd = xe + NCT * C;                             // [NCT] block alpha products
+        const int i = lane, rb = 16 * wave;
+        const bool act = wave < NCT && i < C;
+        float lv[16], dv[16];
+        if (act) {
+            float w = (rb > i) ? expf(sLM[rb - 1] - sLM[i]) : 0.f;
+            float loc = 0.f, d = 1.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int r = rb + j;
+                const float al = sAl[r];
+                w = (r == i) ? 1.f : w * sMu[r];
+                loc = fmaf(al, loc, sBe[r] * w);
+                d *= al;
+                lv[j] = loc;
+                dv[j] = d;
+            }
+            xe[wave * C + i] = loc;
+            if (i == 0) xd[wave] = d;
+        }
+        __syncthreads();
+        if (act) {
+            float G = 0.f;
+#pragma unroll
+            for (int bb = 0; bb < NCT - 1; ++bb)
+                if (bb < wave) G = fmaf(xd[bb], G, xe[bb * C + i]);
+            // entries r <= i land in the lower triangle of row i, which the
+            // DGamma writes below cover before anything reads them as DGamma
+            floatx4* row = reinterpret_cast<floatx4*>(fDG + i * FS + rb);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                floatx4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = fmaf(dv[4 * u + e], G, lv[4 * u + e]);
+                row[u] = o;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. per row block (wave): the C x C products and what they feed -------
     float apv[NCT][4];                                // dA o (P K^T) of the wave's rows, for DGamma of the row above
     if (wave < NCT) {
         const int rA = 16 * wave + nn, r0 = 16 * wave + 4 * g;
-        const float laA = sLA[rA], laP = rA > 0 ? sLA[rA - 1] : 0.f;
         frag aQ[KSD], aK[KSD], aO[KSD], aW[KSD];
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
@@ -849,7 +897,7 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 }
                 continue;
             }
-            const float lmi = sLM[i], eti = sEt[i];
+            const float eti = sEt[i];
             // the vtilde rows of the next column tile, in flight meanwhile
             frag bVn[KSD];
             if (ct + 1 <= wave) {
@@ -858,16 +906,17 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 for (int ks = 0; ks < KSD; ++ks)
                     bVn[ks] = (inx < vm) ? Contig<Tr>::load(Vt + (rowbase + inx) * D, ks, g) : Contig<Tr>::zero();
             }
-            // Psi rows r and r - 1 (fp32 matrix cores; E, F formed on the fly)
-            floatx4 ps = zero4(), pp = zero4();
-            for (int ks = 4 * ct; ks < 4 * wave + 4; ++ks) {
-                const int j = 4 * ks + g;
-                const float lj = sLA[j];
-                const float bf = (i <= j) ? sBe[j] * expf(sLM[j] - lmi) : 0.f;
-                const float a = (j <= rA) ? expf(laA - lj) : 0.f;
-                const float ap = (j <= rA - 1) ? expf(laP - lj) : 0.f;
-                ps = F32::mma(a, bf, ps);
-                pp = F32::mma(ap, bf, pp);
+            // Psi rows r and r - 1 from the transposed table (diagonal beta_i)
+            floatx4 ps, pp;
+            {
+                const float bi = sBe[i];
+                const floatx4 raw = *reinterpret_cast<const floatx4*>(fDG + i * FS + r0);
+                const float rm = fDG[i * FS + (r0 > 0 ? r0 - 1 : 0)];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ps[e] = (r0 + e > i) ? raw[e] : (r0 + e == i ? bi : 0.f);
+                pp[0] = (r0 - 1 > i) ? rm : (r0 - 1 == i ? bi : 0.f);
+#pragma unroll
+                for (int e = 1; e < 4; ++e) pp[e] = ps[e - 1];
             }
             floatx4 aqk = zero4(), akk = zero4(), ao = zero4(), aw = zero4();
 #pragma unroll
@@ -894,7 +943,7 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 const float ap = strict ? -aw[e] * al * akk[e] : 0.f;
                 x1[r * XS + i] = Tr::from_f(x1v);
                 x2a[r * XS + i] = Tr::from_f(al * x2v);
-                fDG[r * FS + i] = dg0;
+                if (low) fDG[r * FS + i] = dg0;        // the upper triangle holds Psi
                 apv[ct][e] = ap;
                 rowd[e] += x2v * akk[e];               // k_r . (X2 K)_r
                 // DGamma o Psi: the own entry, and the row-above entry of ap
@@ -942,25 +991,41 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     __syncthreads();
 
     // ---- 3. Z: G = E^T (DGamma Diag(eta)) on the fp32 matrix cores, G o F row sums
+    // (the E entries of a k-step are shared by the column tiles; DGamma is
+    // read from the lower triangle only)
     if (wave < NCT) {
         const int mA = 16 * wave + nn, m0 = 16 * wave + 4 * g;
         const float laA = sLA[mA];
+        floatx4 acc[NCT];
+        float etc[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            acc[ct] = zero4();
+            etc[ct] = sEt[16 * ct + nn];
+        }
+#pragma unroll
+        for (int ks = 0; ks < C / 4; ++ks) {
+            if (ks < 4 * wave) continue;               // uniform: rows above the wave's block
+            const int r = 4 * ks + g;
+            const float a = (r >= mA) ? expf(sLA[r] - laA) : 0.f;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                if (ct > wave) continue;
+                const int i = 16 * ct + nn;
+                const float dg = (i <= r) ? fDG[r * FS + i] : 0.f;
+                acc[ct] = F32::mma(a, dg * etc[ct], acc[ct]);
+            }
+        }
         float zp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             if (ct > wave) continue;
             const int i = 16 * ct + nn;
-            const float et = sEt[i], lmi = sLM[i];
-            floatx4 acc = zero4();
-            for (int ks = 4 * wave; ks < C / 4; ++ks) {
-                const int r = 4 * ks + g;
-                const float a = (r >= mA) ? expf(sLA[r] - laA) : 0.f;
-                acc = F32::mma(a, fDG[r * FS + i] * et, acc);
-            }
+            const float lmi = sLM[i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = m0 + e;
-                zp[e] += (i <= m) ? acc[e] * expf(sLM[m] - lmi) : 0.f;
+                zp[e] += (i <= m) ? acc[ct][e] * expf(sLM[m] - lmi) : 0.f;
             }
         }
 #pragma unroll
@@ -969,13 +1034,18 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
             if (nn == 15) sZ[m0 + e] = zp[e];
         }
     }
-    // the b part of Z, mubar_m sum_{r >= m} E[r,m] Db_r: a spare wave, or
-    // the last one (which has the fewest Z steps)
-    if (wave == (NCT < 4 ? NCT : 3) && lane < C) {
-        const int m = lane;
-        float sz = 0.f;
-        for (int r = m; r < C; ++r) sz += expf(sLA[r] - sLA[m]) * sDb[r];
-        sZb[m] = sz * expf(sLM[m]);
+    // the b part of Z, mubar_m sum_{r >= m} E[r,m] Db_r: x_m = Db_m + alpha_{m+1}
+    // x_{m+1} as a scan of affine maps with the rows reversed over the lanes,
+    // on a spare wave or the last one (which has the fewest Z steps)
+    if (wave == (NCT < 4 ? NCT : 3)) {
+        const int m = C - 1 - lane;
+        float A = 1.f, B = 0.f;
+        if (m >= 0) {
+            A = (m + 1 < C) ? sAl[m + 1] : 1.f;
+            B = sDb[m];
+        }
+        wave_scan_affine(A, B);
+        if (m >= 0) sZb[m] = B * expf(sLM[m]);
     }
 
     // ---- 4. dq, dk: X1 K, X1^T Q + (Diag(alpha) X2)^T K + Diag(alpha) X2 K -----
