@@ -156,8 +156,8 @@ size_t mdn_chunk_fwd_varlen_workspace_bytes(int64_t H, int64_t T, int64_t nseq, 
 
 // Backward workspace: the forward's sections (T^T and Aqk^T in place of T and
 // Aqk, the coefficients), then per tile the chunk-start states S, M and the
-// chunk-end adjoints dS, dM (element type), the state-product parts of dq
-// and dk (fp32) and the coefficient adjoints (fp32).
+// chunk-end adjoints dS, dM and the state-product parts of dq and dk (element
+// type), and the coefficient adjoints (fp32).
 struct BwdSections {
     size_t mat, cf, st, part, vec, total;
 };
@@ -168,7 +168,7 @@ BwdSections bwd_sections(const ChunkSizes& s, int dk, int C, int dtype) {
     b.mat = align256((size_t)s.tiles * C * C * es);
     b.cf = align256((size_t)s.tiles * MDN_COEF_ROWS * C * sizeof(float));
     b.st = align256((size_t)s.tiles * dk * dk * es);
-    b.part = align256((size_t)s.tiles * C * dk * sizeof(float));
+    b.part = align256((size_t)s.tiles * C * dk * es);
     b.vec = align256((size_t)s.tiles * mdn::MDN_BWD_VEC_ROWS * C * sizeof(float));
     b.total = 2 * b.mat + b.cf + 4 * b.st + 2 * b.part + b.vec;
     return b;
@@ -382,8 +382,8 @@ int mdn_chunk_bwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dt
     f.stream = stream;
     char* st0 = w + 2 * sec.mat + sec.cf;
     a.Sst = st0; a.Mst = st0 + sec.st; a.dSst = st0 + 2 * sec.st; a.dMst = st0 + 3 * sec.st;
-    a.dqp = (float*)(st0 + 4 * sec.st);
-    a.dkp = (float*)(st0 + 4 * sec.st + sec.part);
+    a.dqp = st0 + 4 * sec.st;
+    a.dkp = st0 + 4 * sec.st + sec.part;
     a.vec = (float*)(st0 + 4 * sec.st + 2 * sec.part);
     a.Vt = Vtilde; a.dO = dO; a.dST = dS_T; a.dMT = dM_T;
     a.dq = dq; a.dk = dk_out; a.dv = dv_out;

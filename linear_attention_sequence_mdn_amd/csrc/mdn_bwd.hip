@@ -531,7 +531,8 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                           const typename Tr::elem* __restrict__ dW, const float* __restrict__ coef,
                           const typename Tr::elem* __restrict__ Sst, const typename Tr::elem* __restrict__ Mst,
                           const typename Tr::elem* __restrict__ dSst, const typename Tr::elem* __restrict__ dMst,
-                          float* __restrict__ dqp, float* __restrict__ dkp, float* __restrict__ vec,
+                          typename Tr::elem* __restrict__ dqp, typename Tr::elem* __restrict__ dkp,
+                          float* __restrict__ vec,
                           int64_t T, int64_t NT)
 {
     using E = typename Tr::elem;
@@ -644,8 +645,8 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
             const floatx4 cab = *reinterpret_cast<const floatx4*>(cfl + MDN_COEF_ABP * C + r0);
             const floatx4 cgs = *reinterpret_cast<const floatx4*>(cfl + MDN_COEF_GS * C + r0);
             const floatx4 cgm = *reinterpret_cast<const floatx4*>(cfl + MDN_COEF_GM * C + r0);
-            float* qo = dqp + (tile * C + r0) * D + c;
-            float* ko = dkp + (tile * C + r0) * D + c;
+            E* qo = dqp + (tile * C + r0) * D + c;
+            E* ko = dkp + (tile * C + r0) * D + c;
             float pd[5][4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -654,8 +655,8 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 const float m = in ? 1.f : 0.f;
                 const float os = m * oS[e], om = m * oM[e], ws = m * wS[e], wm = m * wM[e];
                 const float vs = m * vS[e], vmm = m * vM[e];
-                qo[e * D] = ca[e] * os - cb[e] * om;
-                ko[e * D] = -ca[e] * ws + cab[e] * wm + cgs[e] * vs - cgm[e] * vmm;
+                qo[e * D] = Tr::from_f(ca[e] * os - cb[e] * om);
+                ko[e * D] = Tr::from_f(-ca[e] * ws + cab[e] * wm + cgs[e] * vs - cgm[e] * vmm);
                 const float qv = qcur[e], kv = kcur[e];
                 pd[0][e] = qv * os - kv * ws;
                 pd[1][e] = -qv * om;
@@ -733,7 +734,7 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                           const float* __restrict__ beta, const float* __restrict__ eta,
                           const typename Tr::elem* __restrict__ Vt, const typename Tr::elem* __restrict__ dO,
                           const typename Tr::elem* __restrict__ dW, const float* __restrict__ coef,
-                          const float* __restrict__ dqp, const float* __restrict__ dkp,
+                          const typename Tr::elem* __restrict__ dqp, const typename Tr::elem* __restrict__ dkp,
                           const float* __restrict__ vec, typename Tr::elem* __restrict__ dq,
                           typename Tr::elem* __restrict__ dk, float* __restrict__ dalpha,
                           float* __restrict__ dmu, float* __restrict__ dbeta, float* __restrict__ deta,
@@ -1063,17 +1064,20 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         }
         const char* Qc = reinterpret_cast<const char*>(Ql);
         const char* Kc = reinterpret_cast<const char*>(Kl);
-        const float* qp = dqp + (tile * C + r0) * D;
-        const float* kp = dkp + (tile * C + r0) * D;
+        const E* qp = dqp + (tile * C + r0) * D;
+        const E* kp = dkp + (tile * C + r0) * D;
         float pq[4], pk[4];                            // state-product parts, one column tile ahead
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { pq[e] = qp[e * D + nn]; pk[e] = kp[e * D + nn]; }
+        for (int e = 0; e < 4; ++e) { pq[e] = Tr::to_f(qp[e * D + nn]); pk[e] = Tr::to_f(kp[e * D + nn]); }
 #pragma unroll
         for (int ct = 0; ct < NDH; ++ct) {
             float nq[4], nk[4];
             if (ct + 1 < NDH) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { nq[e] = qp[e * D + 16 * (ct + 1) + nn]; nk[e] = kp[e * D + 16 * (ct + 1) + nn]; }
+                for (int e = 0; e < 4; ++e) {
+                    nq[e] = Tr::to_f(qp[e * D + 16 * (ct + 1) + nn]);
+                    nk[e] = Tr::to_f(kp[e * D + 16 * (ct + 1) + nn]);
+                }
             }
             floatx4 aq = zero4(), ak = zero4();
 #pragma unroll
@@ -1161,14 +1165,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a)
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL((mdn_bwd_sgrad_kernel<Tr, D, C>), dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)f.stream,
                        (const E*)f.q, (const E*)f.k, (const E*)a.Vt, (const E*)a.dO, (const E*)a.dv, f.coef,
-                       (const E*)a.Sst, (const E*)a.Mst, (const E*)a.dSst, (const E*)a.dMst, a.dqp, a.dkp, a.vec,
+                       (const E*)a.Sst, (const E*)a.Mst, (const E*)a.dSst, (const E*)a.dMst, (E*)a.dqp, (E*)a.dkp, a.vec,
                        f.T, f.NT);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     static_assert(CgradLayout<Tr, D, C>::TOTAL <= 160 * 1024 - 1024, "LDS");
     hipLaunchKernelGGL((mdn_bwd_cgrad_kernel<Tr, D, C>), dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)f.stream,
                        (const E*)f.q, (const E*)f.k, f.alpha, f.mu, f.beta, f.eta, (const E*)a.Vt, (const E*)a.dO,
-                       (const E*)a.dv, f.coef, a.dqp, a.dkp, a.vec, (E*)a.dq, (E*)a.dk, a.dalpha, a.dmu, a.dbeta,
+                       (const E*)a.dv, f.coef, (const E*)a.dqp, (const E*)a.dkp, a.vec, (E*)a.dq, (E*)a.dk, a.dalpha, a.dmu, a.dbeta,
                        a.deta, f.T, f.NT);
     return hipGetLastError();
 }

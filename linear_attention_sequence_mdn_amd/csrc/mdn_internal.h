@@ -58,7 +58,7 @@ struct BwdArgs {
     float *dalpha, *dmu, *dbeta, *deta;   // [BH][T]
     float *dS0, *dM0;     // [BH][D][D]
     void *Sst, *Mst, *dSst, *dMst;        // [BH*NT][D][D] elem: chunk-start states, chunk-end adjoints
-    float *dqp, *dkp;     // [BH*NT][C][D] fp32: state-product parts of dq, dk
+    void *dqp, *dkp;      // [BH*NT][C][D] elem: state-product parts of dq, dk
     float* vec;           // [BH*NT][MDN_BWD_VEC_ROWS][C] fp32: coefficient adjoints from the state products
 };
 constexpr int MDN_BWD_VEC_ROWS = 8;   // Dabar, Db, Dab, DgS, DgM, then <S,dS'>, <M,dS'>, <M,dM'> in row 5

@@ -286,10 +286,10 @@ def bwd_call(L, B=1, H=2, T=64, d=32, C=32, dt=1, ptrs=None, ws_bytes=None):
 
 def test_bwd_workspace_bytes(L):
     # T^T, Aqk^T (bf16 C x C per chunk), 8 coefficient rows, four d x d states
-    # (bf16), two C x d fp32 partial gradients and 8 rows of coefficient adjoints
+    # and two C x d partial gradients (bf16), and 8 rows of coefficient adjoints
     B, H, T, d, C = 8, 8, 4096, 128, 64
     tiles = B * H * (T // C)
-    expect = (2 * tiles * C * C * 2 + tiles * 8 * C * 4 + 4 * tiles * d * d * 2 + 2 * tiles * C * d * 4
+    expect = (2 * tiles * C * C * 2 + tiles * 8 * C * 4 + 4 * tiles * d * d * 2 + 2 * tiles * C * d * 2
               + tiles * 8 * C * 4)
     assert mdn.chunk_bwd_workspace_bytes(B, H, T, d, d, C, mdn.MDN_BF16) == expect
     bad = ctypes.c_size_t(-1).value
