@@ -520,8 +520,8 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
 // one column tile the four states' operands are held while the chunk's
 // row tiles run; each 16 x 16 output tile is folded and stored as soon as
 // its six products are done.  Row dots with q and k give the coefficient
-// adjoints (rows past a ragged end are masked: their staged rows repeat the
-// last one); the state inner products <S, dS'>, <M, dS'>, <M, dM'> come from
+// adjoints (rows past a ragged end stage copies of the last row and meet
+// zero q and k); the state inner products <S, dS'>, <M, dS'>, <M, dM'> come from
 // the same operands.
 // ---------------------------------------------------------------------------
 template <typename Tr, int D, int C>
@@ -650,11 +650,10 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
             float pd[5][4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = r0 + e;
-                const bool in = r < vm;
-                const float m = in ? 1.f : 0.f;
-                const float os = m * oS[e], om = m * oM[e], ws = m * wS[e], wm = m * wM[e];
-                const float vs = m * vS[e], vmm = m * vM[e];
+                // rows past a ragged end: their q and k are zero, so they add
+                // nothing to the row dots, and their partial rows are never read
+                const float os = oS[e], om = oM[e], ws = wS[e], wm = wM[e];
+                const float vs = vS[e], vmm = vM[e];
                 qo[e * D] = Tr::from_f(ca[e] * os - cb[e] * om);
                 ko[e * D] = Tr::from_f(-ca[e] * ws + cab[e] * wm + cgs[e] * vs - cgm[e] * vmm);
                 const float qv = qcur[e], kv = kcur[e];
