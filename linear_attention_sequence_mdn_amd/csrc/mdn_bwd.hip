@@ -148,6 +148,35 @@ template <> struct FragScale<TraitsF32> {
     static __device__ __forceinline__ float apply(float v, const float (&s)[1]) { return v * s[0]; }
 };
 
+// Hand-off of a chain wave's 16-column slice of an R x D state (accumulator
+// tiles t, rows perm(16t + 4g + e), column nn) to the loader waves.  The chain
+// wave only writes the slice into an LDS tile of row stride SS = 20 elements:
+// the four rows a lane group writes per instruction (8 apart in the bf16 slot
+// order, 4 apart in the fp32 one) then start 16 banks apart, so the writes
+// are conflict-free.  After the next barrier the loader waves copy the tile
+// to the row-major destination in 8-byte pieces.
+template <typename Tr, int R>
+struct SliceTile {
+    using E = typename Tr::elem;
+    static constexpr int ES = sizeof(E);
+    static constexpr int SS = 20;
+    static constexpr int BYTES = R * SS * ES;
+    static constexpr int P8 = 16 * ES / 8;             // 8-byte pieces per row
+    static constexpr int NP = R * P8;
+    static __device__ __forceinline__ void write(const floatx4 (&X)[R / 16], E* __restrict__ lt, int lane) {
+        const int g = lane >> 4, nn = lane & 15;
+#pragma unroll
+        for (int t = 0; t < R / 16; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lt[Slots<Tr>::perm(16 * t + 4 * g + e) * SS + nn] = Tr::from_f(X[t][e]);
+    }
+    // piece p (< NP) of the tile to dst, a row-major array of row stride ld
+    static __device__ __forceinline__ void copy(const char* lt, E* __restrict__ dst, int p, int ld) {
+        const int r = p / P8, c = (p % P8) * (8 / ES);
+        *reinterpret_cast<uint2*>(dst + (size_t)r * ld + c) = *reinterpret_cast<const uint2*>(lt + (r * SS + c) * ES);
+    }
+};
+
 // ---------------------------------------------------------------------------
 // replay: chunk-start states from vtilde
 // ---------------------------------------------------------------------------
@@ -268,6 +297,15 @@ void mdn_bwd_replay_kernel(const typename Tr::elem* __restrict__ k, const typena
 
 // ---------------------------------------------------------------------------
 // carry: reverse pass of the state adjoints
+//
+// One workgroup per (head, slab of 16 NCOL state columns), backward over the
+// chunks: NCOL chain waves carry dS and dM of their 16 columns in registers,
+// four loader waves stage each chunk's K, Q, T^T, Aqk^T, dO slab and
+// coefficient rows.  Each chunk's dS', dM' slices and dV rows leave the chain
+// waves as LDS writes into hand-off tiles; two of the loader waves copy them
+// to HBM after the next barrier, and the other two stage (where the LDS
+// budget has no room for the hand-off tiles, the chain waves store them
+// through staging tiles themselves and all four loaders stage).
 // ---------------------------------------------------------------------------
 template <typename Tr, int D, int C, int NCOL, int NBUF>
 struct CarryLayout {
@@ -286,7 +324,13 @@ struct CarryLayout {
     static constexpr int BUF = CF0 + PC * 16;
     static constexpr int SR = D > C ? D : C;          // staging rows: adjoint slices and dV rows
     static constexpr int STG = NCOL * 2 * SR * 16 * ES;
-    static constexpr int TOTAL = NBUF * BUF + STG;
+    // with two stage buffers and room to spare, the adjoint slices and the dV
+    // rows go to the loaders instead: per parity and column tile a dS' and a
+    // dM' slice tile, then C x 16 dV rows
+    static constexpr int SLB = SliceTile<Tr, D>::BYTES, DVB = C * 16 * ES, CTB = 2 * SLB + DVB;
+    static constexpr int PAR = NCOL * CTB, HAND = 2 * PAR;
+    static constexpr bool OFF = NBUF == 2 && 2 * BUF + HAND <= 160 * 1024 - 1024;
+    static constexpr int TOTAL = NBUF * BUF + (OFF ? HAND : STG);
 };
 
 template <typename Tr, int D, int C>
@@ -315,7 +359,12 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
     constexpr int SLABS = D / (16 * NCOL), OW = 16 * NCOL;
     __shared__ __attribute__((aligned(16))) char stA[LT::BUF];
     __shared__ __attribute__((aligned(16))) char stB[NBUF == 2 ? LT::BUF : 16];
-    __shared__ __attribute__((aligned(16))) E stg[NCOL][2][LT::SR * 16];   // adjoint slices, dV rows on their way out
+    constexpr bool OFF = LT::OFF;
+    constexpr int NDMA = OFF ? 2 : 4;                  // staging loader waves
+    using ST = SliceTile<Tr, D>;
+    // adjoint slices and dV rows on their way out (hand-off tiles, or per
+    // column tile two staging tiles of the chain wave)
+    __shared__ __attribute__((aligned(16))) char stg[OFF ? LT::HAND : LT::STG];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, nn = lane & 15;
@@ -333,26 +382,68 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
             auto seq_row = [&](unsigned r) { return (r < vlast ? r : vlast) * (unsigned)(D * LT::ES); };
             auto t_row = [](unsigned r) { return r * (unsigned)(C * LT::ES); };
             auto cf_row = [](unsigned) { return 0u; };
-            // four loaders: K, Q, T^T and Aqk^T by rows; the dO slab; the coefficients
-            constexpr int RPL = C / 4;
+            // the staging loaders: K, Q, T^T and Aqk^T by rows; the dO slab; the
+            // coefficients
+            constexpr int RPL = C / NDMA;
             const int r0 = lw * RPL;
             dma_tile<RPL, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rb * D), seq_row, lane, r0);
             dma_tile<RPL, LT::PK>(buf + LT::Q0, reinterpret_cast<const char*>(q + rb * D), seq_row, lane, r0);
             dma_tile<RPL, LT::PT>(buf + LT::TT0, reinterpret_cast<const char*>(TT + tile * C * C), t_row, lane, r0);
             dma_tile<RPL, LT::PT>(buf + LT::AT0, reinterpret_cast<const char*>(AT + tile * C * C), t_row, lane, r0);
-            if (lw == 2)
+            if (lw == NDMA - 2)
                 dma_plain<C, LT::PV>(buf + LT::O0, reinterpret_cast<const char*>(dO + rb * D + col0), seq_row, lane);
-            else if (lw == 3)
+            else if (lw == NDMA - 1)
                 dma_plain<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
                                      cf_row, lane);
         };
+        // what the chain waves handed over in iteration j (chunk NT - 1 - j):
+        // the dS', dM' slices to dSst, dMst and the dV rows to dv
+        auto flush = [&](int64_t j) __attribute__((always_inline)) {
+            const int64_t m = NT - 1 - j;
+            const char* hb = stg + (j & 1) * LT::PAR;
+            const size_t off = ((size_t)bh * NT + m) * D * D + col0;
+            constexpr int NT64 = 64 * (4 - NDMA);
+            const int ft = (lw - NDMA) * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < (NCOL * 2 * ST::NP + NT64 - 1) / NT64; ++i) {
+                const int p = i * NT64 + ft;
+                if (p < NCOL * 2 * ST::NP) {
+                    const int sl = p / ST::NP, c = sl >> 1;
+                    ST::copy(hb + c * LT::CTB + (sl & 1) * LT::SLB, ((sl & 1) ? dMst : dSst) + off + 16 * c,
+                             p % ST::NP, D);
+                }
+            }
+            constexpr int PPR = 16 * LT::ES / 16, NPV = C * PPR;
+            const int vm = valid_of(m);
+            E* dst = dv + ((size_t)bh * T + m * C) * D + col0;
+#pragma unroll
+            for (int i = 0; i < (NCOL * NPV + NT64 - 1) / NT64; ++i) {
+                const int p = i * NT64 + ft;
+                const int c = p / NPV, r = (p % NPV) / PPR, e = (p % PPR) * (16 / LT::ES);
+                if (p < NCOL * NPV && r < vm)
+                    *reinterpret_cast<uint4*>(dst + (size_t)r * D + 16 * c + e) =
+                        *reinterpret_cast<const uint4*>(hb + c * LT::CTB + 2 * LT::SLB + (r * 16 + e) * LT::ES);
+            }
+        };
+        // with the hand-off, waves 0-1 stage and waves 2-3 copy out: the copying
+        // waves never wait for their stores, so store latency stays off the
+        // chunk barrier
         const uint32_t aA = lds_addr(stA), aB = lds_addr(stB);
+        const bool stager = lw < NDMA;
         if constexpr (NBUF == 2) {
-            if (NT > 0) issue(aA, NT - 1);
+            if (stager && NT > 0) issue(aA, NT - 1);
             for (int64_t it = 0; it < NT; ++it) {
-                __builtin_amdgcn_s_waitcnt(0);
+                if (stager) __builtin_amdgcn_s_waitcnt(0);
                 lds_barrier();
-                if (it + 1 < NT) issue((it & 1) ? aA : aB, NT - 2 - it);
+                if (stager) {
+                    if (it + 1 < NT) issue((it & 1) ? aA : aB, NT - 2 - it);
+                } else if constexpr (OFF) {
+                    if (it > 0) flush(it - 1);
+                }
+            }
+            if constexpr (OFF) {
+                lds_barrier();                          // the last chunk's hand-off
+                if (!stager && NT > 0) flush(NT - 1);
             }
         } else {
             for (int64_t it = 0; it < NT; ++it) {
@@ -395,10 +486,16 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
         const size_t tile = (size_t)bh * NT + n;
 
         // the chunk-end adjoints of chunk n
-        {
+        // OFF: this iteration's hand-off tiles; otherwise the wave's staging tiles
+        char* hand = OFF ? stg + (it & 1) * LT::PAR + ct * LT::CTB : stg;
+        E* sg = OFF ? reinterpret_cast<E*>(stg) : reinterpret_cast<E*>(stg) + ct * 2 * LT::SR * 16;
+        if constexpr (OFF) {
+            ST::write(XS, reinterpret_cast<E*>(hand), lane);
+            ST::write(XM, reinterpret_cast<E*>(hand + LT::SLB), lane);
+        } else {
             const size_t off = tile * D * D + col0 + 16 * ct;
-            store_slice<Tr, D>(XS, stg[ct][0], dSst + off, lane);
-            store_slice<Tr, D>(XM, stg[ct][1], dMst + off, lane);
+            store_slice<Tr, D>(XS, sg, dSst + off, lane);
+            store_slice<Tr, D>(XM, sg + LT::SR * 16, dMst + off, lane);
         }
         // dvt = Aqk^T dO + Diag(gS) K dS - Diag(gM) K dM
         floatx4 dV[NCT];
@@ -445,20 +542,23 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
             }
         }
         {
-            // dV rows of the chunk: C x 16 through the first staging tile
-            E* lt = stg[ct][0];
+            // dV rows of the chunk: C x 16 into the hand-off tile, or through
+            // the first staging tile
+            E* lt = OFF ? reinterpret_cast<E*>(hand + 2 * LT::SLB) : sg;
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) lt[SL::perm(16 * tc + 4 * g + e) * 16 + nn] = Tr::from_f(dW[tc][e]);
-            constexpr int EPV = 16 / sizeof(E), PPR = 16 / EPV, NP = C * PPR;
-            E* dst = dv + ((size_t)bh * T + n * C) * D + col0 + 16 * ct;
+            if constexpr (!OFF) {
+                constexpr int EPV = 16 / sizeof(E), PPR = 16 / EPV, NP = C * PPR;
+                E* dst = dv + ((size_t)bh * T + n * C) * D + col0 + 16 * ct;
 #pragma unroll
-            for (int i = 0; i < (NP + 63) / 64; ++i) {
-                const int p = i * 64 + lane;
-                const int r = p / PPR, c = (p % PPR) * EPV;
-                if ((NP % 64 == 0 || p < NP) && r < vm)
-                    *reinterpret_cast<uint4*>(dst + (size_t)r * D + c) = reinterpret_cast<const uint4*>(lt)[p];
+                for (int i = 0; i < (NP + 63) / 64; ++i) {
+                    const int p = i * 64 + lane;
+                    const int r = p / PPR, c = (p % PPR) * EPV;
+                    if ((NP % 64 == 0 || p < NP) && r < vm)
+                        *reinterpret_cast<uint4*>(dst + (size_t)r * D + c) = reinterpret_cast<const uint4*>(lt)[p];
+                }
             }
         }
         // chunk-start adjoints
@@ -500,6 +600,7 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
             }
         }
     }
+    if constexpr (OFF) lds_barrier();                   // the loaders copy the last chunk's hand-off
 #pragma unroll
     for (int t = 0; t < NDH; ++t)
 #pragma unroll
