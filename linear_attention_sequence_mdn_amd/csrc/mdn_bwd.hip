@@ -148,32 +148,69 @@ template <> struct FragScale<TraitsF32> {
     static __device__ __forceinline__ float apply(float v, const float (&s)[1]) { return v * s[0]; }
 };
 
-// Hand-off of a chain wave's 16-column slice of an R x D state (accumulator
-// tiles t, rows perm(16t + 4g + e), column nn) to the loader waves.  The chain
-// wave only writes the slice into an LDS tile of row stride SS = 20 elements:
-// the four rows a lane group writes per instruction (8 apart in the bf16 slot
-// order, 4 apart in the fp32 one) then start 16 banks apart, so the writes
-// are conflict-free.  After the next barrier the loader waves copy the tile
-// to the row-major destination in 8-byte pieces.
-template <typename Tr, int R>
-struct SliceTile {
-    using E = typename Tr::elem;
-    static constexpr int ES = sizeof(E);
+// Hand-off of a chain wave's 16-column slice of an R-row matrix (accumulator
+// tiles t, rows perm(16t + 4g + e), column nn) to the loader waves through an
+// LDS tile: the chain wave only writes it, and after the next barrier the
+// loader waves copy it to its row-major destination.
+//   bf16: the tile is column-major with column stride RS = R + 4, so a lane's
+//   four rows (consecutive in the slot order) are one 8-byte write.  The
+//   copy reads it back with the LDS transpose read: a lane group addresses a
+//   4-column x 16-row block and each lane receives one row's 4 columns,
+//   which is an 8-byte piece of the destination row.
+//   fp32: the tile is row-major with row stride 20, so the four rows a lane
+//   group writes per instruction (4 apart in the fp32 slot order) start 16
+//   banks apart; the copy moves 8-byte pieces.
+template <typename Tr, int R> struct HandTile;
+template <int R> struct HandTile<TraitsBf16, R> {
+    static constexpr int RS = R + 4;
+    static constexpr int BYTES = 16 * RS * 2;
+    static __device__ __forceinline__ void write(const floatx4 (&X)[R / 16], __bf16* __restrict__ lt, int lane) {
+        const int g = lane >> 4, nn = lane & 15;
+#pragma unroll
+        for (int t = 0; t < R / 16; ++t) {
+            const int r = Slots<TraitsBf16>::perm(16 * t + 4 * g);
+            union { __bf16 h[4]; uint2 u; } v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v.h[e] = (__bf16)X[t][e];
+            *reinterpret_cast<uint2*>(lt + nn * RS + r) = v.u;
+        }
+    }
+    // the whole tile to dst (row stride ld) by the NW waves of threads
+    // tid < 64 NW; rows >= nrows are not stored
+    template <int NW>
+    static __device__ __forceinline__ void copy(const char* lt, __bf16* __restrict__ dst, int ld, int nrows, int tid) {
+        const int lane = tid & 63, gq = lane >> 4, s = lane & 15;
+#pragma unroll
+        for (int i = 0; i < (R / 16 + NW - 1) / NW; ++i) {
+            const int rb = i * NW + (tid >> 6);
+            if (rb < R / 16) {
+                const int c = 4 * gq + (s >> 2), r = 16 * rb + 4 * (s & 3);
+                const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) shortx4*)(lt + (c * RS + r) * 2));
+                const int row = 16 * rb + s;
+                if (row < nrows) *reinterpret_cast<shortx4*>(dst + (size_t)row * ld + 4 * gq) = v;
+            }
+        }
+    }
+};
+template <int R> struct HandTile<TraitsF32, R> {
     static constexpr int SS = 20;
-    static constexpr int BYTES = R * SS * ES;
-    static constexpr int P8 = 16 * ES / 8;             // 8-byte pieces per row
-    static constexpr int NP = R * P8;
-    static __device__ __forceinline__ void write(const floatx4 (&X)[R / 16], E* __restrict__ lt, int lane) {
+    static constexpr int BYTES = R * SS * 4;
+    static __device__ __forceinline__ void write(const floatx4 (&X)[R / 16], float* __restrict__ lt, int lane) {
         const int g = lane >> 4, nn = lane & 15;
 #pragma unroll
         for (int t = 0; t < R / 16; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) lt[Slots<Tr>::perm(16 * t + 4 * g + e) * SS + nn] = Tr::from_f(X[t][e]);
+            for (int e = 0; e < 4; ++e) lt[Slots<TraitsF32>::perm(16 * t + 4 * g + e) * SS + nn] = X[t][e];
     }
-    // piece p (< NP) of the tile to dst, a row-major array of row stride ld
-    static __device__ __forceinline__ void copy(const char* lt, E* __restrict__ dst, int p, int ld) {
-        const int r = p / P8, c = (p % P8) * (8 / ES);
-        *reinterpret_cast<uint2*>(dst + (size_t)r * ld + c) = *reinterpret_cast<const uint2*>(lt + (r * SS + c) * ES);
+    template <int NW>
+    static __device__ __forceinline__ void copy(const char* lt, float* __restrict__ dst, int ld, int nrows, int tid) {
+        for (int p = tid; p < R * 8; p += 64 * NW) {
+            const int r = p >> 3, c = 2 * (p & 7);
+            if (r < nrows)
+                *reinterpret_cast<uint2*>(dst + (size_t)r * ld + c) =
+                    *reinterpret_cast<const uint2*>(lt + (r * SS + c) * 4);
+        }
     }
 };
 
@@ -327,7 +364,7 @@ struct CarryLayout {
     // with two stage buffers and room to spare, the adjoint slices and the dV
     // rows go to the loaders instead: per parity and column tile a dS' and a
     // dM' slice tile, then C x 16 dV rows
-    static constexpr int SLB = SliceTile<Tr, D>::BYTES, DVB = C * 16 * ES, CTB = 2 * SLB + DVB;
+    static constexpr int SLB = HandTile<Tr, D>::BYTES, DVB = HandTile<Tr, C>::BYTES, CTB = 2 * SLB + DVB;
     static constexpr int PAR = NCOL * CTB, HAND = 2 * PAR;
     static constexpr bool OFF = NBUF == 2 && 2 * BUF + HAND <= 160 * 1024 - 1024;
     static constexpr int TOTAL = NBUF * BUF + (OFF ? HAND : STG);
@@ -361,7 +398,6 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
     __shared__ __attribute__((aligned(16))) char stB[NBUF == 2 ? LT::BUF : 16];
     constexpr bool OFF = LT::OFF;
     constexpr int NDMA = OFF ? 2 : 4;                  // staging loader waves
-    using ST = SliceTile<Tr, D>;
     // adjoint slices and dV rows on their way out (hand-off tiles, or per
     // column tile two staging tiles of the chain wave)
     __shared__ __attribute__((aligned(16))) char stg[OFF ? LT::HAND : LT::STG];
@@ -402,27 +438,15 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
             const int64_t m = NT - 1 - j;
             const char* hb = stg + (j & 1) * LT::PAR;
             const size_t off = ((size_t)bh * NT + m) * D * D + col0;
-            constexpr int NT64 = 64 * (4 - NDMA);
-            const int ft = (lw - NDMA) * 64 + lane;
+            constexpr int NW = 4 - NDMA;
+            const int ft = (lw - NDMA) * 64 + lane, vm = valid_of(m);
+            E* dvd = dv + ((size_t)bh * T + m * C) * D + col0;
 #pragma unroll
-            for (int i = 0; i < (NCOL * 2 * ST::NP + NT64 - 1) / NT64; ++i) {
-                const int p = i * NT64 + ft;
-                if (p < NCOL * 2 * ST::NP) {
-                    const int sl = p / ST::NP, c = sl >> 1;
-                    ST::copy(hb + c * LT::CTB + (sl & 1) * LT::SLB, ((sl & 1) ? dMst : dSst) + off + 16 * c,
-                             p % ST::NP, D);
-                }
-            }
-            constexpr int PPR = 16 * LT::ES / 16, NPV = C * PPR;
-            const int vm = valid_of(m);
-            E* dst = dv + ((size_t)bh * T + m * C) * D + col0;
-#pragma unroll
-            for (int i = 0; i < (NCOL * NPV + NT64 - 1) / NT64; ++i) {
-                const int p = i * NT64 + ft;
-                const int c = p / NPV, r = (p % NPV) / PPR, e = (p % PPR) * (16 / LT::ES);
-                if (p < NCOL * NPV && r < vm)
-                    *reinterpret_cast<uint4*>(dst + (size_t)r * D + 16 * c + e) =
-                        *reinterpret_cast<const uint4*>(hb + c * LT::CTB + 2 * LT::SLB + (r * 16 + e) * LT::ES);
+            for (int c = 0; c < NCOL; ++c) {
+                const char* cb = hb + c * LT::CTB;
+                HandTile<Tr, D>::template copy<NW>(cb, dSst + off + 16 * c, D, D, ft);
+                HandTile<Tr, D>::template copy<NW>(cb + LT::SLB, dMst + off + 16 * c, D, D, ft);
+                HandTile<Tr, C>::template copy<NW>(cb + 2 * LT::SLB, dvd + 16 * c, D, vm, ft);
             }
         };
         // with the hand-off, waves 0-1 stage and waves 2-3 copy out: the copying
@@ -490,8 +514,8 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
         char* hand = OFF ? stg + (it & 1) * LT::PAR + ct * LT::CTB : stg;
         E* sg = OFF ? reinterpret_cast<E*>(stg) : reinterpret_cast<E*>(stg) + ct * 2 * LT::SR * 16;
         if constexpr (OFF) {
-            ST::write(XS, reinterpret_cast<E*>(hand), lane);
-            ST::write(XM, reinterpret_cast<E*>(hand + LT::SLB), lane);
+            HandTile<Tr, D>::write(XS, reinterpret_cast<E*>(hand), lane);
+            HandTile<Tr, D>::write(XM, reinterpret_cast<E*>(hand + LT::SLB), lane);
         } else {
             const size_t off = tile * D * D + col0 + 16 * ct;
             store_slice<Tr, D>(XS, sg, dSst + off, lane);
@@ -544,12 +568,14 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
         {
             // dV rows of the chunk: C x 16 into the hand-off tile, or through
             // the first staging tile
-            E* lt = OFF ? reinterpret_cast<E*>(hand + 2 * LT::SLB) : sg;
+            if constexpr (OFF) {
+                HandTile<Tr, C>::write(dW, reinterpret_cast<E*>(hand + 2 * LT::SLB), lane);
+            } else {
+                E* lt = sg;
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc)
+                for (int tc = 0; tc < NCT; ++tc)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lt[SL::perm(16 * tc + 4 * g + e) * 16 + nn] = Tr::from_f(dW[tc][e]);
-            if constexpr (!OFF) {
+                    for (int e = 0; e < 4; ++e) lt[SL::perm(16 * tc + 4 * g + e) * 16 + nn] = Tr::from_f(dW[tc][e]);
                 constexpr int EPV = 16 / sizeof(E), PPR = 16 / EPV, NP = C * PPR;
                 E* dst = dv + ((size_t)bh * T + n * C) * D + col0 + 16 * ct;
 #pragma unroll
