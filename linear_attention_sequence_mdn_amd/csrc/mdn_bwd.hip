@@ -641,8 +641,9 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
 // sgrad: the products with the states, one workgroup per chunk tile
 //
 // The A operands (the chunk's dO, dW and vtilde rows) are staged in LDS by
-// direct loads; wave w owns dk-column tiles [w*CPW, (w+1)*CPW) of the
-// outputs, so each state row (the B operand X^T: rows of X are contiguous
+// direct loads; wave w owns dk-column tiles w, w + 4, ... of the outputs
+// (in each pass the four waves read adjacent q and k columns, so a line of
+// q or k is fetched once), and each state row (the B operand X^T: rows of X are contiguous
 // in the contraction index) is read from memory once per workgroup.  For
 // one column tile the four states' operands are held while the chunk's
 // row tiles run; each 16 x 16 output tile is folded and stored as soon as
@@ -709,14 +710,14 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
             bdM[ks] = SlotRow<Tr>::load(dM + ro, ks, g);
         }
     };
-    if (wave * CPW < NDH) load_states(wave * CPW);
+    if (wave < NDH) load_states(wave);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     float ip0 = 0.f, ip1 = 0.f, ip2 = 0.f;
 #pragma unroll
     for (int cc = 0; cc < CPW; ++cc) {
-        const int ct = wave * CPW + cc;
+        const int ct = wave + 4 * cc;                 // interleaved: the four waves read one q, k line
         if (ct >= NDH) break;                         // uniform
         const int c = 16 * ct + nn;                   // dk column of this lane's outputs / state row
         if (cc > 0) load_states(ct);
