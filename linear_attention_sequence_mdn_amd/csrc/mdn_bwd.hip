@@ -833,9 +833,10 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
 //   dLM_m = beta_m Z_m - eta_m colsum(DGamma o Psi)_m - DgM_m gM_m (+ the L terms)
 //   deta_i = colsum(DGamma o Psi)_i + DgM_i F[L,i]
 //   dalpha = revcumsum(dLA) / alpha + rowdot(K, X2 K) + Dab b_prev,  dmu = revcumsum(dLM) / mu
-// (LA, LM the chunk's inclusive cumulative logs).  The C x C products over
-// chunk rows run on the fp32 matrix cores with E and F formed on the fly
-// from LA and LM (every exponent <= 0).
+// (LA, LM the chunk's inclusive cumulative logs).  Psi comes from its column
+// recurrence (products of alpha and mu only); the Z contraction over chunk
+// rows runs on the fp32 matrix cores with E formed on the fly from LA (every
+// exponent <= 0).
 // ---------------------------------------------------------------------------
 template <typename Tr, int D, int C>
 struct CgradLayout {
