@@ -341,7 +341,7 @@ int mdn_chunk_bwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dt
                 !dalpha || !dmu || !dbeta || !deta))
         return MDN_ERR_NULL_ARG;
     const BwdSections sec = bwd_sections(s, dk, C, dtype);
-    if (!workspace || workspace_bytes < sec.total) return MDN_ERR_WORKSPACE;
+    if (sec.total > 0 && (!workspace || workspace_bytes < sec.total)) return MDN_ERR_WORKSPACE;
     const void* all[] = {q, k, alpha, mu, beta, eta, S0, M0, Vtilde, dO, dS_T, dM_T,
                          dq, dk_out, dv_out, dalpha, dmu, dbeta, deta, dS0, dM0, workspace};
     for (const void* p : all)

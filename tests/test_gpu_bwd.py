@@ -97,3 +97,36 @@ def test_bwd_full_size_sampled():
     ref = oracle.bwd(*(sel(getattr(x, n)) for n in ("q", "k", "v", "alpha", "mu", "beta", "eta")),
                      sel(x.S0), sel(x.M0), dO=sel(dO), dST=sel(dST), dMT=sel(dMT))
     check({n: got[n][bi, hi] for n in GRADS}, ref, TOL["bf16"], f"bwd full size, heads {heads}")
+
+
+def test_bwd_empty_sequence_passes_state_gradients_through():
+    # T = 0: no tokens, so dS0 = dS_T and dM0 = dM_T exactly (and with no
+    # upstream state gradients, zero); nothing else is written
+    import linear_attention_sequence_mdn_amd as mdn
+    torch = torch_mod()
+    rng = np.random.default_rng(5)
+    z = torch.zeros((2, 2, 0, 32), dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros((2, 2, 0), dtype=torch.float32, device="cuda")
+    S0 = dev(rng.standard_normal((2, 2, 32, 32)).astype(np.float32))
+    M0 = dev(rng.standard_normal((2, 2, 32, 32)).astype(np.float32))
+    dST = dev(rng.standard_normal((2, 2, 32, 32)).astype(np.float32))
+    dMT = dev(rng.standard_normal((2, 2, 32, 32)).astype(np.float32))
+    note("bwd bf16 d32 C32 T0")
+    got = mdn.chunk_bwd(z, z.clone(), g, g.clone(), g.clone(), g.clone(), z.clone(), z.clone(), S0, M0, dST, dMT, C=32)
+    none = mdn.chunk_bwd(z, z.clone(), g, g.clone(), g.clone(), g.clone(), z.clone(), z.clone(), S0, M0, None, None,
+                         C=32)
+    torch.cuda.synchronize()
+    assert torch.equal(got["dS0"], dST) and torch.equal(got["dM0"], dMT)
+    assert not none["dS0"].any() and not none["dM0"].any()
+    for n in ("dq", "dk", "dv", "dalpha", "dmu", "dbeta", "deta"):
+        assert got[n].numel() == 0, n
+
+
+@pytest.mark.parametrize("dtype,d,C", [("f32", 16, 16), ("bf16", 32, 32), ("bf16", 128, 64)])
+def test_bwd_single_token(dtype, d, C):
+    # one token: a single chunk with one valid row (the rest of the tile is
+    # padding that must contribute nothing)
+    x = inputs.make_chunk_inputs(1, 2, 1, d, C=C, dtype=dtype, seed=60 + d, state_std=0.3)
+    dO, dST, dMT = upstream(x, 60 + d)
+    note(f"bwd {dtype} d={d} C={C} T=1")
+    check(run_bwd(x, dO, dST, dMT), ref_bwd(x, dO, dST, dMT), TOL[dtype], f"bwd {dtype} d{d} C{C} T1")
