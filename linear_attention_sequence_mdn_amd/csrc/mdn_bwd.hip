@@ -649,7 +649,8 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
 // row tiles run; each 16 x 16 output tile is folded and stored as soon as
 // its six products are done.  Row dots with q and k give the coefficient
 // adjoints (rows past a ragged end stage copies of the last row and meet
-// zero q and k); the state inner products <S, dS'>, <M, dS'>, <M, dM'> come from
+// zero q and k; q and k of all row tiles are loaded with the column tile's
+// state operands, so their latency is paid once per column tile); the state inner products <S, dS'>, <M, dS'>, <M, dM'> come from
 // the same operands.
 // ---------------------------------------------------------------------------
 template <typename Tr, int D, int C>
@@ -700,7 +701,20 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     // the first column tile's state operands are issued before the wait, so
     // that they travel with the staging copies
     frag bS[KSD], bM[KSD], bdS[KSD], bdM[KSD];
+    // q, k at this lane's output positions for all row tiles, two rows per
+    // vector (one register in the bf16 path), issued with the state operands
+    typedef E e2 __attribute__((ext_vector_type(2)));
+    e2 qa[NCT][2], ka[NCT][2];
     auto load_states = [&](int ct) __attribute__((always_inline)) {
+        const int c = 16 * ct + nn;
+#pragma unroll
+        for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + 4 * g + e;
+                qa[rt][e >> 1][e & 1] = r < vm ? q[(rowbase + r) * D + c] : Tr::from_f(0.f);
+                ka[rt][e >> 1][e & 1] = r < vm ? k[(rowbase + r) * D + c] : Tr::from_f(0.f);
+            }
         const size_t ro = (size_t)(16 * ct + nn) * D;
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
@@ -739,21 +753,14 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 ip2 = fmaf(bM[ks], bdM[ks], ip2);
             }
         }
-        // q and k at this lane's output positions, one row tile ahead
-        auto qk_load = [&](int rt, float (&qv)[4], float (&kv)[4]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rt + 4 * g + e;
-                qv[e] = r < vm ? Tr::to_f(q[(rowbase + r) * D + c]) : 0.f;
-                kv[e] = r < vm ? Tr::to_f(k[(rowbase + r) * D + c]) : 0.f;
-            }
-        };
-        float qcur[4], kcur[4];
-        qk_load(0, qcur, kcur);
 #pragma unroll
         for (int rt = 0; rt < NCT; ++rt) {
-            float qnx[4], knx[4];
-            if (rt + 1 < NCT) qk_load(rt + 1, qnx, knx);
+            float qcur[4], kcur[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qcur[e] = Tr::to_f(qa[rt][e >> 1][e & 1]);
+                kcur[e] = Tr::to_f(ka[rt][e >> 1][e & 1]);
+            }
             floatx4 oS = zero4(), wS = zero4(), oM = zero4(), wM = zero4(), vS = zero4(), vM = zero4();
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
@@ -800,10 +807,6 @@ void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 for (int a = 0; a < 5; ++a)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) atomicAdd(&rv[a][r0 + e], pd[a][e]);
-            }
-            if (rt + 1 < NCT) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { qcur[e] = qnx[e]; kcur[e] = knx[e]; }
             }
         }
     }
