@@ -1122,6 +1122,22 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     }
     __syncthreads();
 
+    // the state-product parts of dq and dk for step 4, all column tiles, two
+    // rows per vector: issued here so that their latency hides behind Z
+    typedef E e2 __attribute__((ext_vector_type(2)));
+    e2 pqa[NDH][2], pka[NDH][2];
+    if (wave < NCT) {
+        const E* qp = dqp + (tile * C + 16 * wave + 4 * g) * D + nn;
+        const E* kp = dkp + (tile * C + 16 * wave + 4 * g) * D + nn;
+#pragma unroll
+        for (int ct = 0; ct < NDH; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pqa[ct][e >> 1][e & 1] = qp[e * D + 16 * ct];
+                pka[ct][e >> 1][e & 1] = kp[e * D + 16 * ct];
+            }
+    }
+
     // ---- 3. Z: G = E^T (DGamma Diag(eta)) on the fp32 matrix cores, G o F row sums
     // (the E entries of a k-step are shared by the column tiles; DGamma is
     // read from the lower triangle only)
@@ -1195,20 +1211,13 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         }
         const char* Qc = reinterpret_cast<const char*>(Ql);
         const char* Kc = reinterpret_cast<const char*>(Kl);
-        const E* qp = dqp + (tile * C + r0) * D;
-        const E* kp = dkp + (tile * C + r0) * D;
-        float pq[4], pk[4];                            // state-product parts, one column tile ahead
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { pq[e] = Tr::to_f(qp[e * D + nn]); pk[e] = Tr::to_f(kp[e * D + nn]); }
 #pragma unroll
         for (int ct = 0; ct < NDH; ++ct) {
-            float nq[4], nk[4];
-            if (ct + 1 < NDH) {
+            float pq[4], pk[4];                        // the state-product parts (loaded before Z)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    nq[e] = Tr::to_f(qp[e * D + 16 * (ct + 1) + nn]);
-                    nk[e] = Tr::to_f(kp[e * D + 16 * (ct + 1) + nn]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                pq[e] = Tr::to_f(pqa[ct][e >> 1][e & 1]);
+                pk[e] = Tr::to_f(pka[ct][e >> 1][e & 1]);
             }
             floatx4 aq = zero4(), ak = zero4();
 #pragma unroll
@@ -1228,10 +1237,6 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
                     dq[(rowbase + r) * D + c] = Tr::from_f(aq[e] + pq[e]);
                     dk[(rowbase + r) * D + c] = Tr::from_f(ak[e] + pk[e]);
                 }
-            }
-            if (ct + 1 < NDH) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { pq[e] = nq[e]; pk[e] = nk[e]; }
             }
         }
     }
