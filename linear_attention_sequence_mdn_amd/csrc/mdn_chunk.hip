@@ -63,10 +63,11 @@ namespace mdn {
 // Four loader waves issue every global->LDS copy (K, Q, T, Aqk, the
 // coefficient rows and the V slab of the next chunk, 16 bytes per lane, into
 // one of two buffers) and every output store, and they compute the output:
-// after the barrier of chunk n each forms, for its token tile and column
-// tiles, R = Diag(abar) Q S - Diag(b) Q M from the chunk-start state
-// operands (all dk rows, so no partial sums are exchanged); after the next
-// chunk barrier it adds Aqk vtilde, and writes O and vtilde to LDS out tiles
+// after the mid-chunk barrier of chunk n each forms, for its token tile and
+// column tiles, R = Diag(abar) Q S - Diag(b) Q M from the chunk-start state
+// operands (all dk rows, so no partial sums are exchanged; the operands are
+// kept per chunk parity, so the chain waves can store the next chunk's
+// meanwhile); after the next chunk barrier it adds Aqk vtilde, and writes O and vtilde to LDS out tiles
 // that are copied out with 16-byte stores.  K, Q, T and Aqk rows are
 // XOR-swizzled by 16-byte piece so that the 16 rows an operand read touches
 // fall in different LDS banks.  K^T, the A operand of the state updates, and
@@ -100,7 +101,7 @@ struct InterLayout {
     // partial-product exchange (RS > 1): 4 fp32 values per lane and row tile
     static constexpr int XP = RS > 1 ? NCOL * RS * NCT * 64 * 16 : 0;
     // chain -> output waves: chunk-start S, M operands and vtilde operands
-    static constexpr int SM = NCOL * RS * 2 * KSH * 64 * FS;
+    static constexpr int SM = 2 * NCOL * RS * 2 * KSH * 64 * FS;   // two chunk parities
     static constexpr int VB = NCOL * KSC * 64 * FS;
     static constexpr int OUT = 2 * C * PV * 16;
     static constexpr int TOTAL = NBUF * BUF + XP + SM + VB + OUT;
@@ -280,7 +281,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     __shared__ __attribute__((aligned(16))) char stA[LT::BUF];
     __shared__ __attribute__((aligned(16))) char stB[NBUF == 2 ? LT::BUF : 16];
     __shared__ __attribute__((aligned(16))) floatx4 xp[RS > 1 ? NCOL * RS * NCT * 64 : 1];   // P_h
-    __shared__ __attribute__((aligned(16))) frag sm[NCOL * RS * 2 * KSH * 64];             // S_h, M_h operands
+    __shared__ __attribute__((aligned(16))) frag sm[2][NCOL * RS * 2 * KSH * 64];          // S_h, M_h operands, by chunk parity
     __shared__ __attribute__((aligned(16))) frag vb[NCOL * KSC * 64];                       // vtilde operands
     __shared__ __attribute__((aligned(16))) E ov[C * OW];                // vtilde out tile
     __shared__ __attribute__((aligned(16))) E oo[C * OW];                // O out tile
@@ -367,7 +368,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         };
         floatx4 R[NOC];
         // R = Diag(abar) Q S - Diag(b) Q M of the chunk staged in `cur`, over all dk rows
-        auto out_r = [&](const char* cur) __attribute__((always_inline)) {
+        auto out_r = [&](const char* cur, int64_t n) __attribute__((always_inline)) {
+            const frag* smp = sm[n & 1];
             const char* Ql = cur + LT::Q0;
             const float* cf = reinterpret_cast<const float*>(cur + LT::CF0);
             frag qa[KSD];
@@ -382,8 +384,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks) {
                     const int base = ((oct * RS + ks / KSH) * 2) * KSH * 64 + (ks % KSH) * 64 + lane;
-                    qs = Tr::mma(qa[ks], sm[base], qs);
-                    qm = Tr::mma(qa[ks], sm[base + KSH * 64], qm);
+                    qs = Tr::mma(qa[ks], smp[base], qs);
+                    qm = Tr::mma(qa[ks], smp[base + KSH * 64], qm);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) R[i][e] = ca[e] * qs[e] - cb[e] * qm[e];
@@ -425,9 +427,9 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 lds_barrier();                          // B0
                 if (more) issue(nxt, n + 1, 0);
                 if (n > 0) out_o(prev);                 // chunk n-1
-                out_r(cur);                             // chunk n
                 lds_barrier();                          // X
                 if (more) issue(nxt, n + 1, 1);
+                out_r(cur, n);                          // chunk n (its state operands stay until chunk n + 2)
                 if (n > 0) copy_outs(n - 1);
             };
             for (int64_t n = 0; n < NTu; n += 2) {
@@ -444,8 +446,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 if (n > 0) copy_outs(n - 1);
                 __builtin_amdgcn_s_waitcnt(0);
                 lds_barrier();                          // B0
-                out_r(stA);
                 lds_barrier();                          // X
+                out_r(stA, n);
             }
         }
         lds_barrier();                                  // E1: vtilde operands of the last chunk stored
@@ -484,12 +486,14 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             XS[t][e] = S0 ? S0[off] : 0.f;
             XM[t][e] = M0 ? M0[off] : 0.f;
         }
-    frag* const smS = sm + ((ct * RS + h) * 2) * KSH * 64 + lane;
-    frag* const smM = smS + KSH * 64;
+    int64_t spar = 0;                                 // parity of the chunk whose start state is stored next
+    const int smo = ((ct * RS + h) * 2) * KSH * 64 + lane;
     // chunk-start state operands, for P and for the output waves; stored
     // before the chunk barrier, at the end of the previous chunk
     frag Sb[KSH], Mb[KSH];
     auto state_operands = [&]() __attribute__((always_inline)) {
+        frag* const smS = sm[spar & 1] + smo;
+        frag* const smM = smS + KSH * 64;
 #pragma unroll
         for (int ks = 0; ks < KSH; ++ks) {
             Sb[ks] = SL::from_acc(XS, ks);
@@ -497,6 +501,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             smS[ks * 64] = Sb[ks];
             smM[ks * 64] = Mb[ks];
         }
+        ++spar;
     };
     state_operands();
 
