@@ -671,12 +671,28 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename Tr, int D, int C>
-static hipError_t launch_inter_nw(const ChunkArgs& a)
+// Compute units of the current device, queried once per device.
+static int device_cus()
+{
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+template <typename Tr, int D, int C, int NCOL, int RS>
+static hipError_t launch_inter_cols(const ChunkArgs& a)
 {
     using E = typename Tr::elem;
     using P = InterPick<Tr, D, C>;
-    constexpr int NCOL = P::NCOL, RS = P::RS, NBUF = P::NBUF, NLD = 4;
+    constexpr int NLD = 4;
+    constexpr int NBUF = InterLayout<Tr, D, C, NCOL, RS, 2>::TOTAL <= P::LIMIT ? 2 : 1;
+    static_assert(InterLayout<Tr, D, C, NCOL, RS, NBUF>::TOTAL <= P::LIMIT, "LDS");
     const int64_t units = a.cu ? a.BH * a.nseq : a.BH;   // (sequence, head) pairs of a packed batch
     const int64_t grid = units * (D / (16 * NCOL));
     hipLaunchKernelGGL((mdn_inter_kernel<Tr, D, C, NCOL, RS, NBUF, NLD>), dim3((unsigned)grid), dim3(64 * (NCOL * RS + NLD)),
@@ -684,6 +700,23 @@ static hipError_t launch_inter_nw(const ChunkArgs& a)
                        (const E*)a.Tmat, (const E*)a.Aqk, a.coef, a.S0, a.M0,
                        (E*)a.O, a.ST, a.MT, (E*)a.Vt, a.T, a.NT, (int)units, a.cu, a.perm, (int)a.BH);
     return hipGetLastError();
+}
+
+// When the grid of two-tile slabs would occupy at most half of the compute
+// units (few heads), the launch takes one-tile slabs, so that each chain
+// wave has a compute unit's loaders and LDS to itself, and at dk >= 64 it
+// splits each tile's rows over two chain waves, which shortens the per-chunk
+// chain that bounds such a launch.  The price is reading K, Q, T and Aqk
+// once more per head and the partial-product exchange of the row split.
+template <typename Tr, int D, int C>
+static hipError_t launch_inter_nw(const ChunkArgs& a)
+{
+    using P = InterPick<Tr, D, C>;
+    if constexpr (P::NCOL == 2 && P::RS == 1) {
+        const int64_t units = a.cu ? a.BH * a.nseq : a.BH;
+        if (2 * units * (D / 32) <= device_cus()) return launch_inter_cols<Tr, D, C, 1, (D >= 64 ? 2 : 1)>(a);
+    }
+    return launch_inter_cols<Tr, D, C, P::NCOL, P::RS>(a);
 }
 
 template <typename Tr>

@@ -49,6 +49,19 @@ def test_bf16_small_ragged(d, C, T):
     check_all(run_chunk(x), oracle_of(x), TOL["bf16"], f"bf16 d{d} C{C} T{T}")
 
 
+# Few heads launch slabs of one 16-column tile; enough heads to fill half of
+# the compute units launch slabs of two.  The cases above take the first
+# launch, these the second.
+@pytest.mark.parametrize("dtype,d,C,T,B,H", [("bf16", 32, 32, 70, 4, 36), ("bf16", 64, 64, 130, 2, 40),
+                                             ("bf16", 128, 32, 100, 2, 20), ("f32", 32, 32, 70, 4, 36),
+                                             ("f32", 128, 16, 50, 2, 20)])
+def test_two_tile_slabs(dtype, d, C, T, B, H):
+    x = inputs.make_chunk_inputs(B, H, T, d, C=C, dtype=dtype, seed=3 * d + C + T,
+                                 state_std=0.3 if dtype == "f32" else 0.02)
+    note(f"chunk {dtype} d={d} C={C} T={T} B={B} H={H} (two-tile slabs)")
+    check_all(run_chunk(x), oracle_of(x), TOL[dtype], f"{dtype} d{d} C{C} T{T} BH{B * H}")
+
+
 def test_bf16_strong_momentum_gates():
     x = inputs.make_chunk_inputs(1, 4, 512, 128, C=64, dtype="bf16", seed=4,
                                  mu_range=(-2.0, -1.5), a_range=(5.0, 10.0))
