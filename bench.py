@@ -13,16 +13,24 @@ kernel's average launch duration comes from K back-to-back launches of its
 stage entry point, timed the same way right after.
 
 The same run also reports, each measured live with HIP events:
+  * the median of the K per-call durations;
   * per-kernel average durations (K launches of each stage) and the roofline
-    of the dominant kernel;
+    of the dominant kernel: the path's algorithmic bytes (q, k, v, gates, O
+    and vtilde per token-head, the states per head) over that kernel's
+    average launch duration, against the HBM peak; the same over the whole
+    call; and how much more the kernels move (their own algorithmic bytes,
+    and the counted traffic from the committed counter summaries when they
+    match the sources);
   * the decode workload (B=256, H=16, d=128, 128 consecutive ``mdn_step``
-    calls, median of 5 repetitions) as GB/s of algorithmic HBM traffic;
+    calls, median of 5 repetitions) as GB/s of algorithmic HBM traffic,
+    beside an in-place read-write stream over the same bytes;
   * the gate pre-operation with the query correction (``mdn_gates``) on the
     400M-layer shape, as GB/s of algorithmic HBM traffic;
   * a packed prefill batch (``mdn_chunk_fwd_varlen``): 32768 tokens of 8
     heads in sequences of lengths ~U{1..4096}, as tokens/s;
   * the backward (``mdn_chunk_bwd``) on the 400M-layer workload, as tokens/s;
-  * the fp64 CPU oracle on a bounded sample of the chunk workload.
+  * the fp64 CPU oracle on a bounded sample of the chunk workload, with all of
+    the host's threads and with one.
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -64,7 +72,7 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=128)
     p.add_argument("--calibration-copy", action="store_true",
                    help="run one 1 GiB device copy first (HBM counter calibration)")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--cpu-seconds", type=float, default=8.0)
     p.add_argument("--cpu-threads", type=int, default=0,
                    help="threads of the CPU-baseline oracle (0 = all the host's OpenMP threads)")
     p.add_argument("--workload", type=int, default=1, choices=(1, 2, 4),
@@ -119,20 +127,27 @@ def chunk_bench(args, torch, mdn, inputs):
         call.run()
     torch.cuda.synchronize()
 
-    def timed(fn):
+    def timed(fn, per_call=False):
         """Average duration (ms) of K back-to-back launches of fn, HIP events
-        on the stream the kernels run on (torch's current stream)."""
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        on the stream the kernels run on (torch's current stream); with
+        per_call, also the median of the K per-call durations (an event
+        between consecutive calls)."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1 if per_call else 2)]
         torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
+        ev[0].record()
+        for i in range(args.steps):
             fn()
-        e1.record()
+            if per_call:
+                ev[i + 1].record()
+        ev[-1].record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        avg = ev[0].elapsed_time(ev[-1]) / args.steps
+        if not per_call:
+            return avg
+        return avg, float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]))
 
     # the timed region: K whole steps (plain mdn_chunk_fwd calls)
-    ms_step = timed(call.run)
+    ms_step, ms_call_median = timed(call.run, per_call=True)
     # each kernel's average launch duration: K launches of its stage alone
     # (repeating either stage recomputes the same result)
     ms_intra = timed(call.intra)
@@ -171,24 +186,38 @@ def chunk_bench(args, torch, mdn, inputs):
                          if args.workload == 1 else None)
     dom_name = max(kernels, key=lambda n: kernels[n]["ms"])
     dom = kernels[dom_name]
-    sha, traffic = dom["source_sha"], dom["traffic"]
-    if dom["bound"] == "hbm":
-        roof = {"bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": dom["GBps"] / PEAK_HBM_GBS}
-    else:
-        roof = {"bound": "mfma", "achieved": dom["TFLOPs"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": dom["TFLOPs"] / PEAK_BF16_TFLOPS}
-    roof.update({"traffic": traffic, "kernel": dom_name, "ms": dom["ms"],
-                 "alg_bytes_per_launch": dom["alg_bytes"], "alg_flop_per_launch": dom["alg_flop"],
-                 "source_sha": sha})
     tps = tokens / (ms_step / 1e3)
     mfma_frac = tps * H * F_TOKEN_HEAD / (PEAK_BF16_TFLOPS * 1e12)
-    # the whole call's ideal HBM traffic: q, k, v, the gates, O and vtilde per
-    # token-head, the final states (and the initial ones when given) per head
+    # The path's algorithmic HBM bytes: per token-head q, k, v, the four
+    # gates, O and vtilde (1,296 B at d = 128 in bf16), per head the final
+    # states (and the initial ones when given).  Intermediates that one
+    # kernel hands to the next through HBM are not algorithmic: they are
+    # reported as the workspace overhead below.
     call_bytes = tok_head * (3 * d * es + 16 + 2 * d * es) + B * H * nstate * d * d * 4
+    call_flop = tok_head * F_TOKEN_HEAD
     hbm_cap = tokens / (call_bytes / (PEAK_HBM_GBS * 1e9))
-    return dict(ms_step=ms_step, tokens_per_s=tps, mfma_frac=mfma_frac, kernels=kernels,
-                roofline=roof, finite=finite, x=x, cfg=cfg, call=call, call_bytes=call_bytes, hbm_cap=hbm_cap)
+    # The roofline of the dominant kernel: the path's algorithmic bytes over
+    # that kernel's average launch duration.  Its intensity (FLOP per byte)
+    # is below the chip's ridge, so HBM bounds it.
+    bound = "hbm" if call_flop / call_bytes < PEAK_BF16_TFLOPS / PEAK_HBM_GBS else "mfma"
+    achieved = call_bytes / (dom["ms"] / 1e3) / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": dom["traffic"], "kernel": dom_name, "ms": dom["ms"],
+            "alg_bytes_per_launch": call_bytes, "intensity_flop_per_byte": call_flop / call_bytes,
+            "intensity_bound": bound, "source_sha": dom["source_sha"],
+            "call": {"ms": ms_step, "GBps": call_bytes / (ms_step / 1e3) / 1e9,
+                     "frac": call_bytes / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS}}
+    # what the kernels move beyond the path's bytes: their own algorithmic
+    # bytes (each input read once per kernel, the workspace they hand on)
+    # and, when the committed counter summaries match the sources, the
+    # counted traffic
+    kern_bytes = sum(kd["alg_bytes"] for kd in kernels.values())
+    roof["workspace_overhead"] = kern_bytes / call_bytes
+    trs = [kd["traffic"] for kd in kernels.values()]
+    roof["counted_traffic_over_alg"] = (sum(trs) / call_bytes) if all(t is not None for t in trs) else None
+    return dict(ms_step=ms_step, ms_call_median=ms_call_median, tokens_per_s=tps, mfma_frac=mfma_frac,
+                kernels=kernels, roofline=roof, finite=finite, x=x, cfg=cfg, call=call, call_bytes=call_bytes,
+                hbm_cap=hbm_cap)
 
 
 def decode_bench(args, torch, mdn, inputs):
@@ -231,26 +260,29 @@ def decode_bench(args, torch, mdn, inputs):
     ms = float(np.median(times))
     bytes_step = B * H * (16 * d * d + 2 * (2 * d + d) + 16 + 2 * d)
     gbs = n * bytes_step / (ms / 1e3) / 1e9
-    # a device-to-device copy of the state's size, the same way, as the
-    # attainable bandwidth next to the peak
-    src = torch.empty(2 * B * H * d * d, dtype=torch.float32, device="cuda").fill_(1.0)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
+    # The attainable-bandwidth reference: the library's in-place stream over
+    # a buffer of the states' size (read, scale by 1, write back, with the
+    # step's non-temporal 16-byte accesses), 128 passes timed the same way.
+    buf = torch.ones(2 * B * H * d * d, dtype=torch.float32, device="cuda")
+    mdn.stream_rw(buf, 1.0)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 10 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
-    del src, dst
+    rw_times = []
+    for _ in range(args.decode_reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            mdn.stream_rw(buf, 1.0)
+        e1.record()
+        torch.cuda.synchronize()
+        rw_times.append(e0.elapsed_time(e1))
+    rw_gbs = n * 2 * buf.numel() * 4 / (float(np.median(rw_times)) / 1e3) / 1e9
+    del buf
     sha = kernel_sources_sha(["mdn_step.hip", "mdn_device.h"])
     traffic = load_traffic("traffic_mdn_step_kernel_decode.md", sha)
     return {"metric": "decode GB/s", "value": gbs, "unit": "GB/s",
             "workload": f"decode B{B} H{H} d{d} bf16, {n} consecutive mdn_step calls",
             "ms_per_decode_step": ms / n, "reps": args.decode_reps,
-            "alg_bytes_per_step": bytes_step, "copy_GBps": copy_gbs, "frac_of_copy": gbs / copy_gbs,
+            "alg_bytes_per_step": bytes_step, "stream_rw_GBps": rw_gbs, "frac_of_stream_rw": gbs / rw_gbs,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "kernel": "mdn_step_kernel",
                          "source_sha": sha}}
@@ -358,12 +390,21 @@ def gates_bench(args, torch, mdn, inputs):
 
 
 def cpu_baseline(args, x):
-    """The fp64 oracle, untuned, on the chunk workload: the whole workload
-    when it takes less than ``--cpu-seconds`` (repeated to fill that time,
-    median reported), else a prefix of the sequence on all heads."""
+    """The fp64 oracle, untuned, on the chunk workload, with all of the
+    host's threads (or ``--cpu-threads``) and with one thread: each on the
+    whole workload when that takes less than ``--cpu-seconds`` (repeated to
+    fill that time, median reported), else on a prefix of the sequence on
+    all heads."""
     import oracle
-    if args.cpu_threads > 0:
-        oracle.set_threads(args.cpu_threads)
+    full = oracle.threads()
+    res = _cpu_baseline_at(args, x, oracle, args.cpu_threads if args.cpu_threads > 0 else full)
+    res["one_core"] = _cpu_baseline_at(args, x, oracle, 1)
+    oracle.set_threads(full)
+    return res
+
+
+def _cpu_baseline_at(args, x, oracle, threads):
+    oracle.set_threads(threads)
 
     def run(Ts):
         sl = lambda a: np.ascontiguousarray(a[:, :, :Ts])
@@ -381,7 +422,7 @@ def cpu_baseline(args, x):
     return {"value": x.B * Ts / wall, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"fp64 oracle on all B{x.B} x H{x.H} heads, tokens 0..{Ts} of {x.T}; "
                       f"median of {len(walls)} runs of {wall:.2f} s",
-            "cpu": _cpu_model()}
+            "cpu": _cpu_model(), "host_threads": os.cpu_count()}
 
 
 def _cpu_model():
@@ -426,6 +467,7 @@ def main():
         ch = chunk_bench(args, torch, mdn, inputs)
         x = ch["x"]
         out.update({"value": ch["tokens_per_s"], "ms_per_step": ch["ms_step"],
+                    "ms_per_call_median": ch["ms_call_median"],
                     "config": {"workload": WORKLOAD_NAMES[args.workload], "B": x.B, "H": x.H, "T": x.T,
                                "dk": x.dk, "dv": x.dv, "C": x.C, "tokens_per_step": x.B * x.T},
                     "mfma_frac_of_bf16_peak": ch["mfma_frac"], "flop_per_token_head": F_TOKEN_HEAD,

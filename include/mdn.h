@@ -239,6 +239,18 @@ int mdn_step(int64_t B, int64_t H, int dk, int dv, int dtype,
              const float* alpha, const float* mu, const float* beta, const float* eta,
              float* S, float* M, void* o, void* stream);
 
+/* Measurement reference for mdn_step (not part of the method): reads every
+ * fp32 of `buf` and writes it back multiplied by `scale`, in place, with the
+ * decode step's access pattern (16-byte non-temporal loads, then stores,
+ * 64 KiB per workgroup).  Over a buffer the size of the decode states it
+ * gives the HBM bandwidth an in-place read-write stream attains, the
+ * ceiling the decode step is compared with.
+ *   buf     device buffer, 16-byte aligned; bytes a multiple of 16 (>= 0).
+ *   scale   factor applied to every element (1 leaves the buffer unchanged).
+ * Errors: MDN_ERR_BAD_SHAPE (bytes negative, not a multiple of 16, or beyond
+ * 2^47), MDN_ERR_NULL_ARG, MDN_ERR_ALIGN, MDN_ERR_HIP. */
+int mdn_stream_rw(void* buf, int64_t bytes, float scale, void* stream);
+
 /* Diagnostic: the log-domain coefficient stage alone (summary, step 5), as
  * used inside mdn_chunk_fwd.
  *   alpha, mu, beta, eta   [B][H][T] fp32;  C in {16, 32, 64}.

@@ -75,6 +75,8 @@ def lib():
         L.mdn_chunk_coef.restype = i32
         L.mdn_gates.argtypes = [i64, i64, i64, i32, i32, ctypes.c_float, ctypes.c_float] + [vp] * 12 + [vp]
         L.mdn_gates.restype = i32
+        L.mdn_stream_rw.argtypes = [vp, i64, ctypes.c_float, vp]
+        L.mdn_stream_rw.restype = i32
         L.mdn_status_string.argtypes = [i32]
         L.mdn_status_string.restype = ctypes.c_char_p
         L.mdn_abi_version.argtypes = []
@@ -101,10 +103,22 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _stream(stream, owned=()):
+    """The hipStream_t handle of `stream` (None = torch's current stream).
+
+    `owned` are the tensors this binding allocated for the call (outputs,
+    workspace).  They come from the caching allocator on the current stream;
+    when the kernels run on another stream, each is recorded on that stream so
+    that its memory is not handed out again before the kernels have finished
+    with it, even if the caller drops it at once."""
     torch = _torch()
+    cur = torch.cuda.current_stream()
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = cur
+    elif stream != cur:
+        for t in owned:
+            if t is not None:
+                t.record_stream(stream)
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -156,18 +170,24 @@ class ChunkCall:
         for name, s in (("S0", S0), ("M0", M0)):
             if s is not None:
                 _need(s, name, torch.float32, (B, H, dk, dv), dev)
+        owned = []
         if out is None:
             O = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
             Vt = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+            owned += [O, Vt]
         else:
             O, Vt = out
         if S_T is None:
             S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+            owned.append(S_T)
         if M_T is None:
             M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+            owned.append(M_T)
         nws = chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, self.dt)
         if workspace is None and nws > 0:
             workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+            owned.append(workspace)
+        self._owned = owned
         self.sizes = (B, H, T, dk, dv, C, self.dt)
         self.tensors = (q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vt)
         self.workspace = workspace
@@ -177,16 +197,18 @@ class ChunkCall:
                     workspace.numel() if workspace is not None else 0)
 
     def run(self, stream=None):
-        _check(lib().mdn_chunk_fwd(*self.sizes, *self._ptrs, *self._ws, _stream(stream)), "mdn_chunk_fwd")
+        _check(lib().mdn_chunk_fwd(*self.sizes, *self._ptrs, *self._ws, _stream(stream, self._owned)),
+               "mdn_chunk_fwd")
         return self.outputs
 
     def intra(self, stream=None):
         p = self._ptrs
         _check(lib().mdn_chunk_intra(*self.sizes, p[0], p[1], p[3], p[4], p[5], p[6], *self._ws,
-                                     _stream(stream)), "mdn_chunk_intra")
+                                     _stream(stream, self._owned)), "mdn_chunk_intra")
 
     def inter(self, stream=None):
-        _check(lib().mdn_chunk_inter(*self.sizes, *self._ptrs, *self._ws, _stream(stream)), "mdn_chunk_inter")
+        _check(lib().mdn_chunk_inter(*self.sizes, *self._ptrs, *self._ws, _stream(stream, self._owned)),
+               "mdn_chunk_inter")
         return self.outputs
 
 
@@ -244,9 +266,11 @@ class BwdCall:
             deta=torch.empty((B, H, T), dtype=torch.float32, device=dev),
             dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev),
             dM0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
+        self._owned = list(self.grads.values())
         nws = chunk_bwd_workspace_bytes(B, H, T, dk, dv, C, self.dt)
         if workspace is None:
             workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+            self._owned.append(workspace)
         self.workspace = workspace
         self.sizes = (B, H, T, dk, dv, C, self.dt)
         self.inputs = (q, k, alpha, mu, beta, eta, S0, M0, Vtilde, dO, dS_T, dM_T)
@@ -254,7 +278,8 @@ class BwdCall:
         self._ws = (_ptr(workspace), workspace.numel())
 
     def run(self, stream=None):
-        _check(lib().mdn_chunk_bwd(*self.sizes, *self._ptrs, *self._ws, _stream(stream)), "mdn_chunk_bwd")
+        _check(lib().mdn_chunk_bwd(*self.sizes, *self._ptrs, *self._ws, _stream(stream, self._owned)),
+               "mdn_chunk_bwd")
         return self.grads
 
 
@@ -298,18 +323,24 @@ class VarlenCall:
         for name, s in (("S0", S0), ("M0", M0)):
             if s is not None:
                 _need(s, name, torch.float32, (nseq, H, dk, dv), dev)
+        owned = []
         if out is None:
             O = torch.empty((H, T, dv), dtype=q.dtype, device=dev)
             Vt = torch.empty((H, T, dv), dtype=q.dtype, device=dev)
+            owned += [O, Vt]
         else:
             O, Vt = out
         if S_T is None:
             S_T = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
+            owned.append(S_T)
         if M_T is None:
             M_T = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
+            owned.append(M_T)
         nws = chunk_fwd_varlen_workspace_bytes(H, T, nseq, dk, dv, C, self.dt)
         if workspace is None and nws > 0:
             workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+            owned.append(workspace)
+        self._owned = owned
         self.sizes = (H, T, nseq)
         self.dims = (dk, dv, C, self.dt)
         self.cu = cu_seqlens
@@ -322,7 +353,7 @@ class VarlenCall:
 
     def run(self, stream=None):
         _check(lib().mdn_chunk_fwd_varlen(*self.sizes, _ptr(self.cu), *self.dims, *self._ptrs, *self._ws,
-                                          _stream(stream)), "mdn_chunk_fwd_varlen")
+                                          _stream(stream, self._owned)), "mdn_chunk_fwd_varlen")
         return self.outputs
 
 
@@ -355,12 +386,25 @@ def step(q, k, v, alpha, mu, beta, eta, S, M, *, o=None, stream=None):
         _need(g, name, torch.float32, (B, H), dev)
     _need(S, "S", torch.float32, (B, H, dk, dv), dev)
     _need(M, "M", torch.float32, (B, H, dk, dv), dev)
+    owned = ()
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+        owned = (o,)
     st = lib().mdn_step(B, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu),
-                        _ptr(beta), _ptr(eta), _ptr(S), _ptr(M), _ptr(o), _stream(stream))
+                        _ptr(beta), _ptr(eta), _ptr(S), _ptr(M), _ptr(o), _stream(stream, owned))
     _check(st, "mdn_step")
     return o
+
+
+def stream_rw(buf, scale=1.0, *, stream=None):
+    """Measurement reference for the decode step: every fp32 of the
+    contiguous device tensor ``buf`` is read and written back times
+    ``scale``, in place, with the step's access pattern (``mdn_stream_rw``)."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    _check(lib().mdn_stream_rw(_ptr(buf), buf.numel() * buf.element_size(), float(scale), _stream(stream)),
+           "mdn_stream_rw")
+    return buf
 
 
 def chunk_coef(alpha, mu, beta, eta, C, *, with_gamma=True, stream=None):
@@ -377,7 +421,7 @@ def chunk_coef(alpha, mu, beta, eta, C, *, with_gamma=True, stream=None):
     coef = torch.empty((B, H, NT, COEF_ROWS, C), dtype=torch.float32, device=dev)
     gamma = torch.empty((B, H, NT, C, C), dtype=torch.float32, device=dev) if with_gamma else None
     st = lib().mdn_chunk_coef(B, H, T, C, _ptr(alpha), _ptr(mu), _ptr(beta), _ptr(eta),
-                              _ptr(coef), _ptr(gamma), _stream(stream))
+                              _ptr(coef), _ptr(gamma), _stream(stream, (coef, gamma)))
     _check(st, "mdn_chunk_coef")
     return coef, gamma
 
@@ -395,6 +439,7 @@ def gates(x, a, b, mu_log, *, s=1.0, mu_log_min=-2.0, q=None, k=None, d=None, q_
     for name, t in (("x", x), ("a", a), ("b", b), ("mu_log", mu_log)):
         _need(t, name, torch.float32, (B, H, T), dev)
     corr = q is not None or k is not None or d is not None
+    owned = []
     dk, dt = 16, MDN_F32
     if corr:
         if q is None or k is None or d is None:
@@ -406,12 +451,14 @@ def gates(x, a, b, mu_log, *, s=1.0, mu_log_min=-2.0, q=None, k=None, d=None, q_
         _need(d, "d", torch.float32, (H,), dev)
         if q_out is None:
             q_out = torch.empty_like(q)
+            owned.append(q_out)
         _need(q_out, "q_out", q.dtype, (B, H, T, dk), dev)
     if out is None:
         out = tuple(torch.empty((B, H, T), dtype=torch.float32, device=dev) for _ in range(4))
+        owned += list(out)
     for name, t in zip(("alpha", "mu", "beta", "eta"), out):
         _need(t, name, torch.float32, (B, H, T), dev)
     _check(lib().mdn_gates(B, H, T, dk, dt, float(s), float(mu_log_min),
                            _ptr(x), _ptr(a), _ptr(b), _ptr(mu_log), *[_ptr(t) for t in out],
-                           _ptr(q), _ptr(k), _ptr(d), _ptr(q_out), _stream(stream)), "mdn_gates")
+                           _ptr(q), _ptr(k), _ptr(d), _ptr(q_out), _stream(stream, owned)), "mdn_gates")
     return (*out, q_out) if corr else tuple(out)

@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -19,8 +20,12 @@ SOURCES = ["mdn_api.cpp", "mdn_step.hip", "mdn_intra.hip", "mdn_chunk.hip", "mdn
 HEADERS = ["mdn_device.h", "mdn_internal.h", "mdn_lds.h"]
 ARCH = os.environ.get("MDN_OFFLOAD_ARCH", "gfx950")
 
-# Packed fp32 vector ops are disabled: the compiler may otherwise form
-# v_pk_* fp32 instructions from ordinary float code.
+# Packed fp32 vector ops are disabled for the device code: without the
+# feature switch the compiler forms v_pk_fma/mul/add_f32 from ordinary float
+# (and float2) code.  hipcc also hands the switch to the host pass, which
+# warns that it does not know the feature; that warning is harmless.  After
+# compiling, every object's gfx950 code is disassembled and the build fails
+# if any packed fp32 instruction is present (check_no_packed_fp32).
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(HERE, "..", "include")]
@@ -33,10 +38,42 @@ def _hipcc():
     return "hipcc"
 
 
+def _llvm_tool(name):
+    return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", name)
+
+
+PACKED_FP32 = re.compile(r"\bv_pk_(fma|mul|add)_f32\b")
+
+
+def check_no_packed_fp32(obj: str) -> None:
+    """Disassemble the gfx950 code object bundled in `obj` (built here) and
+    raise if it holds a packed fp32 instruction."""
+    folder, base = os.path.split(os.path.abspath(obj))
+    # extracts the bundled code objects next to `obj`, as <obj>.<n>.<target>
+    subprocess.run([_llvm_tool("llvm-objdump"), "--offloading", base], check=True, cwd=folder,
+                   stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    parts = [f for f in os.listdir(folder) if f.startswith(base + ".")]
+    try:
+        dev = [f for f in parts if f"amdgcn-amd-amdhsa--{ARCH}" in f]
+        if not dev:
+            raise RuntimeError(f"{obj}: no {ARCH} code object found to check")
+        for f in dev:
+            asm = subprocess.run([_llvm_tool("llvm-objdump"), "-d", os.path.join(folder, f)], check=True,
+                                 capture_output=True, text=True).stdout
+            hits = sorted({m.group(0) for m in PACKED_FP32.finditer(asm)})
+            if hits:
+                raise RuntimeError(f"{obj}: packed fp32 instructions in the device code: {hits}")
+    finally:
+        for f in parts:
+            os.remove(os.path.join(folder, f))
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [_hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     subprocess.run(cmd, check=True)
+    if src.endswith(".hip"):
+        check_no_packed_fp32(obj)
     return obj
 
 

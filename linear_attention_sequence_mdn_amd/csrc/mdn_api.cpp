@@ -11,6 +11,7 @@
 #include <stdint.h>
 #include <string.h>
 
+
 #include "../../include/mdn.h"
 #include "mdn_internal.h"
 
@@ -448,6 +449,15 @@ int mdn_step(int64_t B, int64_t H, int dk, int dv, int dtype,
     a.alpha = alpha; a.mu = mu; a.beta = beta; a.eta = eta;
     a.S = S; a.M = M; a.o = o; a.stream = stream;
     return hip_status(mdn::launch_step(a));
+}
+
+int mdn_stream_rw(void* buf, int64_t bytes, float scale, void* stream)
+{
+    if (bytes < 0 || bytes % 16 != 0 || bytes / 16 > (int64_t)INT32_MAX * 4096) return MDN_ERR_BAD_SHAPE;
+    if (bytes == 0) return MDN_OK;
+    if (!buf) return MDN_ERR_NULL_ARG;
+    if (!aligned16(buf)) return MDN_ERR_ALIGN;
+    return hip_status(mdn::launch_stream_rw(buf, bytes / 16, scale, stream));
 }
 
 int mdn_gates(int64_t B, int64_t H, int64_t T, int dk, int dtype, float s, float mu_log_min,

@@ -671,18 +671,14 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// Compute units of the current device, queried once per device.
+// Compute units of the current device.  Queried on every call (a lookup in
+// the runtime's device properties), so the library keeps no mutable state.
 static int device_cus()
 {
-    static int cache[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    return n;
 }
 
 template <typename Tr, int D, int C, int NCOL, int RS>

@@ -77,6 +77,8 @@ struct GateArgs {
 };
 
 hipError_t launch_step(const StepArgs& a);
+// in-place read, scale and write of n16 16-byte pieces (decode bandwidth reference)
+hipError_t launch_stream_rw(void* buf, int64_t n16, float scale, void* stream);
 // gate pre-operation and query correction
 hipError_t launch_gates(const GateArgs& g);
 // coefficient + intra-chunk stage (T, (QK^T) o Gamma, coefficients)

@@ -163,4 +163,43 @@ hipError_t launch_step(const StepArgs& a)
     return a.dtype == 1 ? launch_step_d<TraitsBf16>(a) : launch_step_d<TraitsF32>(a);
 }
 
+// Bandwidth reference for the decode step: every fp32 of a buffer is read,
+// multiplied by `scale` and written back in place, with the step's access
+// pattern and none of its arithmetic: 256 threads per workgroup, each
+// loading RPT 16-byte pieces (non-temporal) before storing them back, so a
+// workgroup streams 64 KiB, as a decode workgroup does with its half of a
+// head's S and M.  A scale of 1 leaves the buffer as it was.
+template <int RPT>
+__global__ __launch_bounds__(256)
+void mdn_stream_rw_kernel(floatx4* __restrict__ buf, int64_t n16, float scale)
+{
+    const int64_t base = (int64_t)blockIdx.x * 256 * RPT + threadIdx.x;
+    floatx4 x[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int64_t j = base + (int64_t)i * 256;
+        if (j < n16) x[i] = __builtin_nontemporal_load(buf + j);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int64_t j = base + (int64_t)i * 256;
+        if (j < n16) {
+            floatx4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = x[i][e] * scale;
+            __builtin_nontemporal_store(y, buf + j);
+        }
+    }
+}
+
+hipError_t launch_stream_rw(void* buf, int64_t n16, float scale, void* stream)
+{
+    constexpr int RPT = 16;
+    if (n16 == 0) return hipSuccess;
+    const int64_t blocks = (n16 + 256 * RPT - 1) / (256 * RPT);
+    hipLaunchKernelGGL((mdn_stream_rw_kernel<RPT>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<floatx4*>(buf), n16, scale);
+    return hipGetLastError();
+}
+
 }  // namespace mdn

@@ -204,11 +204,14 @@ def fwd_varlen(q, k, v, alpha, mu, beta, eta, cu, S0=None, M0=None):
     return O, ST, MT, Vt
 
 
-def step(q, k, v, alpha, mu, beta, eta, S, M):
+def step(q, k, v, alpha, mu, beta, eta, S, M, inplace=False):
     """One decode step of the recurrence for every head, fp64.
 
     q, k ``[..., dk]``; v ``[..., dv]``; gates ``[...]``; S, M ``[..., dk, dv]``.
-    Returns ``(o, S_new, M_new, vtilde)``; the inputs S and M are not modified.
+    Returns ``(o, S_new, M_new, vtilde)``.  The inputs S and M are not
+    modified, unless ``inplace`` is set: then they must be C-contiguous fp64
+    arrays of the full shape, are updated in place and returned as S_new,
+    M_new (which saves two copies of the states per step on large batches).
     Same equations as :func:`fwd` (one token): the recurrent form the MDN
     article (ijyty.com, section 6) says generation uses.
     """
@@ -218,8 +221,16 @@ def step(q, k, v, alpha, mu, beta, eta, S, M):
     lead = q.shape[:-1]
     dk, dv = q.shape[-1], v.shape[-1]
     BH = int(np.prod(lead)) if lead else 1
-    S2 = np.array(np.broadcast_to(S, lead + (dk, dv)), dtype=np.float64, order="C", copy=True)
-    M2 = np.array(np.broadcast_to(M, lead + (dk, dv)), dtype=np.float64, order="C", copy=True)
+    if inplace:
+        for name, a in (("S", S), ("M", M)):
+            if not (isinstance(a, np.ndarray) and a.dtype == np.float64 and a.flags.c_contiguous
+                    and a.shape == lead + (dk, dv)):
+                raise ValueError(f"inplace step: {name} must be a C-contiguous float64 array of shape "
+                                 f"{lead + (dk, dv)}")
+        S2, M2 = S, M
+    else:
+        S2 = np.array(np.broadcast_to(S, lead + (dk, dv)), dtype=np.float64, order="C", copy=True)
+        M2 = np.array(np.broadcast_to(M, lead + (dk, dv)), dtype=np.float64, order="C", copy=True)
     o = np.zeros(lead + (dv,))
     vt = np.zeros(lead + (dv,))
     lib.mdn_oracle_step(BH, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu),

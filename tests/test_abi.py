@@ -178,6 +178,16 @@ def test_step_validation(L):
     assert step_call(L, ptrs=q) == ALIGN
 
 
+def test_stream_rw_validation(L):
+    p = addrs(1)[0]
+    assert L.mdn_stream_rw(p, -16, 1.0, None) == BAD_SHAPE
+    assert L.mdn_stream_rw(p, 24, 1.0, None) == BAD_SHAPE
+    assert L.mdn_stream_rw(p, 1 << 48, 1.0, None) == BAD_SHAPE
+    assert L.mdn_stream_rw(None, 0, 1.0, None) == OK
+    assert L.mdn_stream_rw(None, 64, 1.0, None) == NULL_ARG
+    assert L.mdn_stream_rw(ctypes.c_void_p(p.value + 4), 64, 1.0, None) == ALIGN
+
+
 def test_coef_validation(L):
     p = addrs(6)
     assert L.mdn_chunk_coef(1, 1, 64, 48, *p, None) == UNSUPPORTED

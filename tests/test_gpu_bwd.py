@@ -81,22 +81,15 @@ def test_bwd_strong_momentum():
     check(run_bwd(x, dO, dST, dMT), ref_bwd(x, dO, dST, dMT), TOL["bf16"], "bwd strong momentum")
 
 
-def test_bwd_full_size_sampled():
+def test_bwd_full_size():
     # the 400M-layer workload (B8 H8 T4096 d128 C64 bf16) in the launch
-    # configuration the benchmark times; three heads against the oracle
+    # configuration the benchmark times; every gradient of every head
+    # against the oracle's reverse mode, as whole tensors
     x = inputs.config_inputs(1)
     dO, dST, dMT = upstream(x, 1)
-    note("bwd 400M-layer B8 H8 T4096 d128 C64 bf16")
+    note("bwd 400M-layer B8 H8 T4096 d128 C64 bf16, all heads")
     got = run_bwd(x, dO, dST, dMT)
-    for n in GRADS:
-        assert np.all(np.isfinite(got[n])), n
-    heads = [(0, 0), (7, 7), (3, 5)]
-    bi = np.array([p[0] for p in heads])
-    hi = np.array([p[1] for p in heads])
-    sel = lambda a: None if a is None else a[bi, hi]
-    ref = oracle.bwd(*(sel(getattr(x, n)) for n in ("q", "k", "v", "alpha", "mu", "beta", "eta")),
-                     sel(x.S0), sel(x.M0), dO=sel(dO), dST=sel(dST), dMT=sel(dMT))
-    check({n: got[n][bi, hi] for n in GRADS}, ref, TOL["bf16"], f"bwd full size, heads {heads}")
+    check(got, ref_bwd(x, dO, dST, dMT), TOL["bf16"], "bwd full size, all 64 heads")
 
 
 def test_bwd_empty_sequence_passes_state_gradients_through():

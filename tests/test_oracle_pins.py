@@ -65,6 +65,22 @@ def test_step_matches_fwd():
     assert pins.check_step_matches_fwd(oracle.fwd, oracle.step) < 1e-13
 
 
+def test_inplace_step_equals_copying_step():
+    rng = np.random.default_rng(8)
+    B, H, d = 3, 2, 8
+    S = rng.standard_normal((B, H, d, d))
+    M = rng.standard_normal((B, H, d, d))
+    args = [rng.standard_normal((B, H, d)) for _ in range(3)] + [rng.uniform(0.2, 1.0, (B, H)) for _ in range(4)]
+    o, S1, M1, vt = oracle.step(*args, S, M)
+    S2, M2 = S.copy(), M.copy()
+    o2, S3, M3, vt2 = oracle.step(*args, S2, M2, inplace=True)
+    assert S3 is S2 and M3 is M2
+    assert np.array_equal(o, o2) and np.array_equal(vt, vt2)
+    assert np.array_equal(S1, S2) and np.array_equal(M1, M2)
+    with pytest.raises(ValueError):
+        oracle.step(*args, S.astype(np.float32), M, inplace=True)
+
+
 def test_hand_worked_example():
     with open(os.path.join(GOLDEN, "hand_worked_d1.json")) as f:
         g = json.load(f)
