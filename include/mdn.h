@@ -58,7 +58,8 @@ typedef enum mdn_status {
     MDN_ERR_ALIAS = 4,       /* an output overlaps an input (other than the allowed aliases) */
     MDN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
     MDN_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
-    MDN_ERR_HIP = 7          /* a HIP launch or runtime call failed */
+    MDN_ERR_HIP = 7,         /* a HIP launch or runtime call failed */
+    MDN_ERR_TOO_LARGE = 8    /* mdn_chunk_fwd_noalloc: workspace need above MDN_NOALLOC_SCRATCH_BYTES */
 } mdn_status;
 
 typedef enum mdn_dtype {
@@ -124,6 +125,30 @@ int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dt
                   const float* S0, const float* M0,
                   void* O, float* S_T, float* M_T, void* Vtilde,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* mdn_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, semantics and errors as mdn_chunk_fwd, without the
+ * workspace: it uses a static device array of MDN_NOALLOC_SCRATCH_BYTES
+ * instead, which every GPU the library runs on holds until the process
+ * ends.  The call itself allocates nothing (no hipMalloc, no hipFree).
+ *   - Problems whose mdn_chunk_fwd_workspace_bytes() exceeds
+ *     MDN_NOALLOC_SCRATCH_BYTES return MDN_ERR_TOO_LARGE and enqueue
+ *     nothing.  At dk = dv = 128, C = 64 in bf16 a chunk tile needs 18 KiB,
+ *     so 80 MiB holds 4551 tiles: e.g. B*H = 64 heads of 4096 tokens, or
+ *     16 heads of 16384 (4096 tiles each).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (two streams, two host threads) race and give
+ *     undefined results.  Calls ordered on one stream are safe.
+ *   - The first call on a device looks up the array's device address once
+ *     (hipGetSymbolAddress, with that device current) and keeps it: this
+ *     entry point is the one exception to "no mutable global state". */
+#define MDN_NOALLOC_SCRATCH_BYTES (80ll << 20)
+int mdn_chunk_fwd_noalloc(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                          const void* q, const void* k, const void* v,
+                          const float* alpha, const float* mu, const float* beta, const float* eta,
+                          const float* S0, const float* M0,
+                          void* O, float* S_T, float* M_T, void* Vtilde, void* stream);
 
 /* The two stages of mdn_chunk_fwd, exposed separately so that each kernel
  * can be timed or checked on its own.  mdn_chunk_fwd(args) is exactly
@@ -296,7 +321,7 @@ const char* mdn_status_string(int status);
 /* ABI revision of this header (incremented on any signature change). */
 int mdn_abi_version(void);
 
-#define MDN_ABI_VERSION 5
+#define MDN_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

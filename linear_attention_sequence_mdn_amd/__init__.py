@@ -9,6 +9,8 @@ PyTorch fallback: if the library is missing, every call raises.
 Entry points (same names as the C ABI):
     chunk_fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64)
         -> (O, S_T, M_T, Vtilde)
+    chunk_fwd_noalloc(q, k, v, alpha, mu, beta, eta, S0, M0, C, out=(O, Vt), S_T=, M_T=)
+        -> (O, S_T, M_T, Vtilde)   workspace in the library's static scratch
     chunk_fwd_varlen(q, k, v, alpha, mu, beta, eta, cu_seqlens, S0=None, M0=None, C=64)
         -> (O, S_T, M_T, Vtilde)   packed variable-length batch
     step(q, k, v, alpha, mu, beta, eta, S, M) -> o   (S, M updated in place)
@@ -65,6 +67,8 @@ def lib():
         L.mdn_chunk_fwd_varlen_workspace_bytes.restype = sz
         L.mdn_chunk_fwd_varlen.argtypes = [i64, i64, i64, vp, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
         L.mdn_chunk_fwd_varlen.restype = i32
+        L.mdn_chunk_fwd_noalloc.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp]
+        L.mdn_chunk_fwd_noalloc.restype = i32
         L.mdn_chunk_intra.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 6 + [vp, sz, vp]
         L.mdn_chunk_intra.restype = i32
         L.mdn_chunk_inter.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
@@ -148,6 +152,9 @@ def chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype) -> int:
     return int(n)
 
 
+_NO_WORKSPACE = object()      # ChunkCall(workspace=_NO_WORKSPACE): allocate none
+
+
 class ChunkCall:
     """Validated, preallocated arguments of one chunk forward.
 
@@ -183,10 +190,13 @@ class ChunkCall:
         if M_T is None:
             M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
             owned.append(M_T)
-        nws = chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, self.dt)
-        if workspace is None and nws > 0:
-            workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
-            owned.append(workspace)
+        if workspace is _NO_WORKSPACE:
+            workspace = None
+        else:
+            nws = chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, self.dt)
+            if workspace is None and nws > 0:
+                workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+                owned.append(workspace)
         self._owned = owned
         self.sizes = (B, H, T, dk, dv, C, self.dt)
         self.tensors = (q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vt)
@@ -225,6 +235,21 @@ def chunk_fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, *,
     call = ChunkCall(q, k, v, alpha, mu, beta, eta, S0, M0, C, out=out, S_T=S_T, M_T=M_T,
                      workspace=workspace)
     return call.run(stream)
+
+
+NOALLOC_SCRATCH_BYTES = 80 << 20
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, *, out, S_T, M_T, stream=None):
+    """``mdn_chunk_fwd_noalloc``: the chunk forward with its workspace in the
+    library's static device scratch, for callers that cannot allocate.  The
+    caller passes every output: ``out`` = (O, Vtilde), ``S_T``, ``M_T``
+    (shapes as in :func:`chunk_fwd`).  Calls that overlap in time on one GPU
+    share the scratch and race."""
+    call = ChunkCall(q, k, v, alpha, mu, beta, eta, S0, M0, C, out=out, S_T=S_T, M_T=M_T,
+                     workspace=_NO_WORKSPACE)
+    _check(lib().mdn_chunk_fwd_noalloc(*call.sizes, *call._ptrs, _stream(stream)), "mdn_chunk_fwd_noalloc")
+    return call.outputs
 
 
 def chunk_bwd_workspace_bytes(B, H, T, dk, dv, C, dtype) -> int:

@@ -11,6 +11,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "../../include/mdn.h"
 #include "mdn_internal.h"
@@ -133,6 +134,8 @@ const char* mdn_status_string(int status)
     case MDN_ERR_WORKSPACE: return "MDN_ERR_WORKSPACE: workspace missing or too small";
     case MDN_ERR_ALIGN: return "MDN_ERR_ALIGN: a pointer is not 16-byte aligned";
     case MDN_ERR_HIP: return "MDN_ERR_HIP: a HIP launch or runtime call failed";
+    case MDN_ERR_TOO_LARGE:
+        return "MDN_ERR_TOO_LARGE: the problem needs more than the allocation-free entry point's static scratch";
     default: return "unknown mdn status";
     }
 }
@@ -273,6 +276,63 @@ int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dt
         if (st != MDN_OK) return st;
     }
     return hip_status(mdn::launch_chunk_inter(a));
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward.  The chunk forward's workspace (T, Aqk and the
+// coefficient rows of every chunk tile) lives in a file-scope device array
+// instead of a caller buffer.  Each GPU holds its own copy of the array, at
+// its own address, for the life of the process.  In host code `scratch`
+// names a host-side stand-in, never the device memory: the device address
+// is taken once per device with hipGetSymbolAddress (with that device
+// current) and only that address is handed to the kernels.
+// ---------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) unsigned char scratch[MDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void* scratch_dev[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// Device address of this device's `scratch` (looked up on the first call
+// on the device, then kept).
+int scratch_of_current_device(void** p) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MDN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MDN_ERR_UNSUPPORTED;
+    std::call_once(scratch_once[dev], [dev]() {
+        void* ptr = nullptr;
+        scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        scratch_dev[dev] = scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    if (scratch_err[dev] != hipSuccess || !scratch_dev[dev]) return MDN_ERR_HIP;
+    *p = scratch_dev[dev];
+    return MDN_OK;
+}
+}  // namespace
+
+int mdn_chunk_fwd_noalloc(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                          const void* q, const void* k, const void* v,
+                          const float* alpha, const float* mu, const float* beta, const float* eta,
+                          const float* S0, const float* M0,
+                          void* O, float* S_T, float* M_T, void* Vtilde, void* stream)
+{
+    ChunkSizes s;
+    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
+    if (st != MDN_OK) return st;
+    if (!dims_supported_chunk(dtype, dk, dv, C)) return MDN_ERR_UNSUPPORTED;
+    const size_t need = workspace_of(s, C, dtype);
+    if (need > (size_t)MDN_NOALLOC_SCRATCH_BYTES) return MDN_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    if (need > 0) {
+        st = scratch_of_current_device(&ws);
+        if (st != MDN_OK) return st;
+    }
+    // the kernels write every byte of the workspace they read, so nothing
+    // left by an earlier call needs clearing
+    return mdn_chunk_fwd(B, H, T, dk, dv, C, dtype, q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde,
+                         ws, ws ? (size_t)MDN_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int mdn_chunk_intra(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,

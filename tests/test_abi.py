@@ -13,7 +13,7 @@ import linear_attention_sequence_mdn_amd as mdn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mdn.h")
 
-OK, NULL_ARG, BAD_SHAPE, UNSUPPORTED, ALIAS, WORKSPACE, ALIGN = 0, 1, 2, 3, 4, 5, 6
+OK, NULL_ARG, BAD_SHAPE, UNSUPPORTED, ALIAS, WORKSPACE, ALIGN, TOO_LARGE = 0, 1, 2, 3, 4, 5, 6, 8
 
 
 @pytest.fixture(scope="module")
@@ -49,11 +49,11 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.mdn_abi_version() == 5
+    assert L.mdn_abi_version() == 6
 
 
 def test_status_strings(L):
-    for s in range(8):
+    for s in range(9):
         assert L.mdn_status_string(s).startswith(b"MDN_")
     assert L.mdn_status_string(99) == b"unknown mdn status"
 
@@ -176,6 +176,16 @@ def test_step_validation(L):
     q = list(p)
     q[7] = ctypes.c_void_p(p[7].value + 8)
     assert step_call(L, ptrs=q) == ALIGN
+
+
+def test_noalloc_validation(L):
+    # host-side checks, made before the scratch is looked up (no device needed)
+    p = addrs(13)
+    f = lambda B, H, T, d, C, dt, ptrs=p: L.mdn_chunk_fwd_noalloc(B, H, T, d, d, C, dt, *ptrs, None)
+    assert f(8, 8, 4672, 128, 64, 1) == TOO_LARGE       # 4672 tiles of 18 KiB: beyond the 80 MiB scratch
+    assert f(8, 8, 4096, 48, 64, 1) == UNSUPPORTED
+    assert f(-1, 8, 4096, 128, 64, 1) == BAD_SHAPE
+    assert f(0, 8, 4096, 128, 64, 1) == OK               # empty: no workspace, nothing to do
 
 
 def test_stream_rw_validation(L):
