@@ -124,71 +124,14 @@ struct InterPick {
     static_assert(InterLayout<Tr, D, C, NCOL, RS, NBUF>::TOTAL <= LIMIT, "LDS");
 };
 
-// K^T operand of the state update for d-tile td, contraction step ks.
-template <typename Tr, int P> struct KtOperand;
-template <int P> struct KtOperand<TraitsBf16, P> {
-    static __device__ __forceinline__ bf16x8 load(const char* Kt, int td, int ks, int lane) {
-        // Transpose read: in each 16-lane group, result lane i takes element
-        // i%4 of source lane 4j + i/4.  Source lane s of group g points at
-        // row 32ks + 8g + s/4 (+4 for the second half) and columns
-        // perm(16td) + 8(s%4) .. +3, so lane i receives
-        // K[32ks + 8g + j][perm(16td + i)] for j = 0..3: the contraction
-        // slots j (and 4 + j) of lane group g, for state row 16td + i.
-        const int g = lane >> 4, s = lane & 15;
-        const int r0 = 32 * ks + 8 * g + (s >> 2);
-        const int b = 2 * (Slots<TraitsBf16>::perm(16 * td) + 8 * (s & 3));
-        union { shortx4 h[2]; bf16x8 v; } f;
-        f.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)(Kt + swz<P>(r0, b)));
-        f.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)(Kt + swz<P>(r0 + 4, b)));
-        return f.v;
-    }
-};
-template <int P> struct KtOperand<TraitsF32, P> {
-    static __device__ __forceinline__ float load(const char* Kt, int td, int ks, int lane) {
-        const int g = lane >> 4, m = lane & 15;
-        const int r = 16 * (ks >> 2) + 4 * g + (ks & 3);
-        return *reinterpret_cast<const float*>(Kt + swz<P>(r, 4 * (16 * td + m)));
-    }
-};
-
-// V slab (plain rows of OW elements) as the B operand of T V for column tile
-// ct, contraction step ks.
-template <typename Tr, int OW> struct VOperand;
-template <int OW> struct VOperand<TraitsBf16, OW> {
-    static __device__ __forceinline__ bf16x8 load(const char* Vs, int ct, int ks, int lane) {
-        // Transpose read: source lane s of group g points at row
-        // 32ks + 8g + s/4 (+4 for the second half) and columns
-        // 16ct + 4(s%4) .. +3, so lane i receives V[32ks + 8g + j][16ct + i]
-        // for j = 0..3 (4..7): the contraction slots of lane group g.
-        const int g = lane >> 4, s = lane & 15;
-        const int r0 = 32 * ks + 8 * g + (s >> 2);
-        const int b = 2 * (16 * ct + 4 * (s & 3));
-        union { shortx4 h[2]; bf16x8 v; } f;
-        f.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)(Vs + r0 * OW * 2 + b));
-        f.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)(Vs + (r0 + 4) * OW * 2 + b));
-        return f.v;
-    }
-};
-template <int OW> struct VOperand<TraitsF32, OW> {
-    static __device__ __forceinline__ float load(const char* Vs, int ct, int ks, int lane) {
-        const int g = lane >> 4, m = lane & 15;
-        const int r = 16 * (ks >> 2) + 4 * g + (ks & 3);
-        return *reinterpret_cast<const float*>(Vs + 4 * (r * OW + 16 * ct + m));
-    }
-};
-
 // Issue one loader wave's share of the direct global->LDS copies of one
-// chunk into the buffer at LDS byte address `buf`.  HALF 0 (needed first):
+// chunk into the stage buffer `buf`.  HALF 0 (needed first):
 // the K and Q rows, split by rows over the NLD loaders; HALF 1: T, Aqk, the
 // V slab and the coefficient rows.  A single wave sustains only a fraction
 // of a CU's L2 bandwidth, so the copies are spread over all loaders.  Rows
 // past `valid` (ragged last chunk) repeat the last valid row.
 template <typename LT, typename E, int D, int C, int NLD, int HALF>
-__device__ __forceinline__ void stage_chunk(int lw, uint32_t buf, const E* __restrict__ k, const E* __restrict__ q,
+__device__ __forceinline__ void stage_chunk(int lw, lds_char* buf, const E* __restrict__ k, const E* __restrict__ q,
                                             const E* __restrict__ v, const E* __restrict__ Tm,
                                             const E* __restrict__ Aqk, const float* __restrict__ coef,
                                             size_t rowbase, int valid, size_t tile, int col0, int lane)
@@ -204,19 +147,21 @@ __device__ __forceinline__ void stage_chunk(int lw, uint32_t buf, const E* __res
         const bool isq = lw >= NH;
         const int part = lw % NH;
         if (isq)      // Q is read only by the loader waves: swizzle key 1
-            dma_tile<RPL, LT::PK, 1>(buf + LT::Q0, reinterpret_cast<const char*>(q + rowbase * D), seq_row, lane, part * RPL);
+            dma_tile_p<RPL, LT::PK, 1>(buf + LT::Q0, reinterpret_cast<const char*>(q + rowbase * D), seq_row, lane,
+                                       part * RPL);
         else
-            dma_tile<RPL, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rowbase * D), seq_row, lane, part * RPL);
+            dma_tile_p<RPL, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rowbase * D), seq_row, lane,
+                                    part * RPL);
     } else {
         if (lw == 0)
-            dma_tile<C, LT::PT>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
+            dma_tile_p<C, LT::PT>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
         else if (lw == 1)
-            dma_tile<C, LT::PT, 1>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
+            dma_tile_p<C, LT::PT, 1>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
         else if (lw == 2)
-            dma_plain<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), seq_row, lane);
+            dma_plain_p<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), seq_row, lane);
         else
-            dma_plain<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
-                                 cf_row, lane);
+            dma_plain_p<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
+                                   cf_row, lane);
     }
 }
 
@@ -288,43 +233,9 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, nn = lane & 15;
-    // the sequence this workgroup carries: its state index bh, column slab,
-    // first row, first tile slot and length
-    int bh, slab;
-    int64_t row0, tile0, len;
-    if (!cu) {
-        xcd_head_map(blockIdx.x, SLABS, BH, bh, slab);
-        row0 = (int64_t)bh * T;
-        tile0 = (int64_t)bh * NT;
-        len = T;
-    } else {
-        // Packed batch of BH = nseq * H units (sequence, head); states are
-        // [nseq, H, D, D].  Units are taken longest sequence first (perm):
-        // unit rank r = (sequence rank) * H + head.  Workgroups go to the
-        // XCDs round robin in launch order, so rank r runs on XCD r % 8, all
-        // its slabs there, and each XCD meets its units longest first.
-        int r;
-        if ((BH & 7) == 0) {
-            const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
-            r = (l / SLABS) * 8 + x;
-            slab = l % SLABS;
-        } else {
-            r = blockIdx.x / SLABS;
-            slab = blockIdx.x % SLABS;
-        }
-        const int64_t nseq = BH / H, h = r % H;
-        int64_t i = perm[r / H];
-        i = i < 0 ? 0 : (i >= nseq ? nseq - 1 : i);
-        bh = (int)(i * H + h);
-        // The bounds are clamped into [0, T] and ordered, which keeps every
-        // row and tile slot in range whatever the table holds.
-        int64_t c0 = cu[i], c1 = cu[i + 1];
-        c0 = c0 < 0 ? 0 : (c0 > T ? T : c0);
-        c1 = c1 < c0 ? c0 : (c1 > T ? T : c1);
-        row0 = h * T + c0;
-        tile0 = h * NT + c0 / C + i;
-        len = c1 - c0;
-    }
+    const InterUnit unit = inter_unit(blockIdx.x, SLABS, BH, T, NT, C, cu, perm, H);
+    const int bh = unit.bh, slab = unit.slab;
+    const int64_t row0 = unit.row0, tile0 = unit.tile0, len = unit.len;
     const int col0 = slab * OW;
     const int64_t NTu = (len + C - 1) / C;
     auto valid_of = [&](int64_t n) { return (int)((len - n * C) < C ? (len - n * C) : C); };
@@ -353,7 +264,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         constexpr int OCS = NLD / NCT;                 // output waves per token tile
         constexpr int NOC = (NCOL + OCS - 1) / OCS;    // column tiles per output wave
         constexpr int tc = lw % NCT, oc0 = lw / NCT;
-        auto issue = [&](uint32_t buf, int64_t m, int half) __attribute__((always_inline)) {
+        auto issue = [&](lds_char* buf, int64_t m, int half) __attribute__((always_inline)) {
             const size_t tile = (size_t)(tile0 + m);
             const size_t rb = (size_t)(row0 + m * C);
             const int vm = valid_of(m);
@@ -415,18 +326,22 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 }
             }
         };
-        const uint32_t aA = lds_addr(stA), aB = lds_addr(stB);
+        lds_char* const aA = lds_ptr(stA);
+        lds_char* const aB = lds_ptr(stB);
         if constexpr (NBUF == 2) {
             if (NTu > 0) {
                 issue(aA, 0, 0);
                 issue(aA, 0, 1);
             }
-            auto step = [&](uint32_t nxt, const char* cur, const char* prev, int64_t n) __attribute__((always_inline)) {
+            auto step = [&](lds_char* nxt, const char* cur, const char* prev, int64_t n) __attribute__((always_inline)) {
                 const bool more = n + 1 < NTu;
                 __builtin_amdgcn_s_waitcnt(0);          // chunk n has landed (and earlier stores left)
                 lds_barrier();                          // B0
+                // chunk n-1 (its Aqk rows are in the buffer refilled next):
+                // read before the copies into that buffer are issued, which
+                // later reads of the buffer would have to wait for
+                if (n > 0) out_o(prev);
                 if (more) issue(nxt, n + 1, 0);
-                if (n > 0) out_o(prev);                 // chunk n-1
                 lds_barrier();                          // X
                 if (more) issue(nxt, n + 1, 1);
                 out_r(cur, n);                          // chunk n (its state operands stay until chunk n + 2)

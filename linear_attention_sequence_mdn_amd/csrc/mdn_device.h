@@ -216,4 +216,52 @@ __device__ __forceinline__ void xcd_head_map(int id, int slabs, int BH, int& bh,
     }
 }
 
+// The sequence a workgroup of the inter-chunk stage carries: state index
+// bh, column slab, first row, first tile slot and length.  Without cu the
+// batch is [BH, T] and workgroup id covers head bh (xcd_head_map).  With cu
+// it is a packed batch of BH = nseq * H units (sequence, head); states are
+// [nseq, H, D, D].  Units are taken longest sequence first (perm): unit rank
+// r = (sequence rank) * H + head.  Workgroups go to the XCDs round robin in
+// launch order, so rank r runs on XCD r % 8, all its slabs there, and each
+// XCD meets its units longest first.  The bounds read from cu are clamped
+// into [0, T] and ordered, which keeps every row and tile slot in range
+// whatever the table holds.
+struct InterUnit {
+    int bh, slab;
+    int64_t row0, tile0, len;
+};
+__device__ __forceinline__ InterUnit inter_unit(int id, int slabs, int BH, int64_t T, int64_t NT, int C,
+                                                const int32_t* __restrict__ cu, const int32_t* __restrict__ perm,
+                                                int H)
+{
+    InterUnit u;
+    if (!cu) {
+        xcd_head_map(id, slabs, BH, u.bh, u.slab);
+        u.row0 = (int64_t)u.bh * T;
+        u.tile0 = (int64_t)u.bh * NT;
+        u.len = T;
+        return u;
+    }
+    int r;
+    if ((BH & 7) == 0) {
+        const int x = id & 7, l = id >> 3;
+        r = (l / slabs) * 8 + x;
+        u.slab = l % slabs;
+    } else {
+        r = id / slabs;
+        u.slab = id % slabs;
+    }
+    const int64_t nseq = BH / H, h = r % H;
+    int64_t i = perm[r / H];
+    i = i < 0 ? 0 : (i >= nseq ? nseq - 1 : i);
+    u.bh = (int)(i * H + h);
+    int64_t c0 = cu[i], c1 = cu[i + 1];
+    c0 = c0 < 0 ? 0 : (c0 > T ? T : c0);
+    c1 = c1 < c0 ? c0 : (c1 > T ? T : c1);
+    u.row0 = h * T + c0;
+    u.tile0 = h * NT + c0 / C + i;
+    u.len = c1 - c0;
+    return u;
+}
+
 }  // namespace mdn

@@ -89,6 +89,46 @@ __device__ __forceinline__ void dma_tile(uint32_t dst, const char* __restrict__ 
     }
 }
 
+// The same copies with the destination given as a pointer into a named LDS
+// array (not as an integer address), so that the compiler can tell which
+// array a copy writes and need not wait for it before LDS accesses to other
+// arrays.
+typedef __attribute__((address_space(3))) char lds_char;
+template <typename T>
+__device__ __forceinline__ lds_char* lds_ptr(T* p) { return (lds_char*)(__attribute__((address_space(3))) void*)p; }
+
+template <int R, int P, int KEY = 0, typename RowOff>
+__device__ __forceinline__ void dma_tile_p(lds_char* dst, const char* __restrict__ base, RowOff rowoff, int lane,
+                                           int r0 = 0)
+{
+    static_assert(P <= 64 && 64 % P == 0, "rows of at most 64 pieces");
+    constexpr int RPI = 64 / P;
+    constexpr int NI = (R * P + 63) / 64;
+    const unsigned lr = (unsigned)lane / P, lp = (unsigned)lane % P;
+    lds_char* d0 = dst + r0 * P * 16;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const unsigned rl = i * RPI + lr;
+        const unsigned r = (unsigned)r0 + rl;
+        const unsigned p = lp ^ (unsigned)swz_key<P, KEY>((int)r);
+        if (R * P % 64 == 0 || rl < (unsigned)R)
+            __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(d0 + i * 1024), 16, 0, 0);
+    }
+}
+
+template <int R, int P, typename RowOff>
+__device__ __forceinline__ void dma_plain_p(lds_char* dst, const char* __restrict__ base, RowOff rowoff, int lane)
+{
+    constexpr int NI = (R * P + 63) / 64;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const unsigned s = i * 64 + (unsigned)lane;
+        const unsigned r = s / P, p = s % P;
+        if (R * P % 64 == 0 || r < (unsigned)R)
+            __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(dst + i * 1024), 16, 0, 0);
+    }
+}
+
 // Copy R rows of P plain 16-byte pieces (no swizzle).
 template <int R, int P, typename RowOff>
 __device__ __forceinline__ void dma_plain(uint32_t dst, const char* __restrict__ base, RowOff rowoff, int lane)
@@ -103,5 +143,62 @@ __device__ __forceinline__ void dma_plain(uint32_t dst, const char* __restrict__
     }
 }
 
+
+// K^T operand of the state update for d-tile td, contraction step ks.
+template <typename Tr, int P> struct KtOperand;
+template <int P> struct KtOperand<TraitsBf16, P> {
+    static __device__ __forceinline__ bf16x8 load(const char* Kt, int td, int ks, int lane) {
+        // Transpose read: in each 16-lane group, result lane i takes element
+        // i%4 of source lane 4j + i/4.  Source lane s of group g points at
+        // row 32ks + 8g + s/4 (+4 for the second half) and columns
+        // perm(16td) + 8(s%4) .. +3, so lane i receives
+        // K[32ks + 8g + j][perm(16td + i)] for j = 0..3: the contraction
+        // slots j (and 4 + j) of lane group g, for state row 16td + i.
+        const int g = lane >> 4, s = lane & 15;
+        const int r0 = 32 * ks + 8 * g + (s >> 2);
+        const int b = 2 * (Slots<TraitsBf16>::perm(16 * td) + 8 * (s & 3));
+        union { shortx4 h[2]; bf16x8 v; } f;
+        f.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(Kt + swz<P>(r0, b)));
+        f.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(Kt + swz<P>(r0 + 4, b)));
+        return f.v;
+    }
+};
+template <int P> struct KtOperand<TraitsF32, P> {
+    static __device__ __forceinline__ float load(const char* Kt, int td, int ks, int lane) {
+        const int g = lane >> 4, m = lane & 15;
+        const int r = 16 * (ks >> 2) + 4 * g + (ks & 3);
+        return *reinterpret_cast<const float*>(Kt + swz<P>(r, 4 * (16 * td + m)));
+    }
+};
+
+// V slab (plain rows of OW elements) as the B operand of T V for column tile
+// ct, contraction step ks.
+template <typename Tr, int OW> struct VOperand;
+template <int OW> struct VOperand<TraitsBf16, OW> {
+    static __device__ __forceinline__ bf16x8 load(const char* Vs, int ct, int ks, int lane) {
+        // Transpose read: source lane s of group g points at row
+        // 32ks + 8g + s/4 (+4 for the second half) and columns
+        // 16ct + 4(s%4) .. +3, so lane i receives V[32ks + 8g + j][16ct + i]
+        // for j = 0..3 (4..7): the contraction slots of lane group g.
+        const int g = lane >> 4, s = lane & 15;
+        const int r0 = 32 * ks + 8 * g + (s >> 2);
+        const int b = 2 * (16 * ct + 4 * (s & 3));
+        union { shortx4 h[2]; bf16x8 v; } f;
+        f.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(Vs + r0 * OW * 2 + b));
+        f.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)(Vs + (r0 + 4) * OW * 2 + b));
+        return f.v;
+    }
+};
+template <int OW> struct VOperand<TraitsF32, OW> {
+    static __device__ __forceinline__ float load(const char* Vs, int ct, int ks, int lane) {
+        const int g = lane >> 4, m = lane & 15;
+        const int r = 16 * (ks >> 2) + 4 * g + (ks & 3);
+        return *reinterpret_cast<const float*>(Vs + 4 * (r * OW + 16 * ct + m));
+    }
+};
 
 }  // namespace mdn
