@@ -653,8 +653,18 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
 // state operands, so their latency is paid once per column tile); the state inner products <S, dS'>, <M, dS'>, <M, dM'> come from
 // the same operands.
 // ---------------------------------------------------------------------------
+// Workgroups of the sgrad kernel that fit one compute unit's LDS (at most
+// three): the occupancy its register allocation targets (one wave per SIMD
+// each).
 template <typename Tr, int D, int C>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+struct SgradOcc {
+    static constexpr int LDS = 3 * C * D * (int)sizeof(typename Tr::elem) + MDN_COEF_ROWS * C * 4 + 5 * C * 4 + 48;
+    static constexpr int FIT = (160 * 1024) / LDS;
+    static constexpr int W = FIT < 1 ? 1 : (FIT > 3 ? 3 : FIT);
+};
+
+template <typename Tr, int D, int C>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SgradOcc<Tr, D, C>::W)))
 void mdn_bwd_sgrad_kernel(const typename Tr::elem* __restrict__ q, const typename Tr::elem* __restrict__ k,
                           const typename Tr::elem* __restrict__ Vt, const typename Tr::elem* __restrict__ dO,
                           const typename Tr::elem* __restrict__ dW, const float* __restrict__ coef,
