@@ -93,7 +93,9 @@ enum {
  *   [B*H*NT][C][C]  T matrices   (dtype)
  *   [B*H*NT][C][C]  (Q K^T) o Gamma, zero above the diagonal (dtype)
  *   [B*H*NT][MDN_COEF_ROWS][C]  coefficients (fp32)
- * each section starting on a 256-byte boundary. */
+ * each section starting on a 256-byte boundary.  For a widened bf16 call
+ * (dk = 16 or C = 16, see mdn_chunk_fwd) the layout is that of the fp32 call,
+ * followed by fp32 copies of q, k, v, O and Vtilde. */
 size_t mdn_chunk_fwd_workspace_bytes(int64_t B, int64_t H, int64_t T,
                                      int dk, int dv, int C, int dtype);
 
@@ -102,9 +104,13 @@ size_t mdn_chunk_fwd_workspace_bytes(int64_t B, int64_t H, int64_t T,
  *               shorter than C is handled by neutral padding; B*H == 0 or
  *               T == 0 is valid: with T == 0 only S_T, M_T are written,
  *               as copies of S0, M0).
- *   dk, dv      head dims: dk == dv, in {16, 32, 64, 128} for MDN_F32 and
- *               {32, 64, 128} for MDN_BF16.
- *   C           chunk size: {16, 32, 64} for MDN_F32, {32, 64} for MDN_BF16.
+ *   dk, dv      head dims: dk == dv, in {16, 32, 64, 128}.
+ *   C           chunk size: {16, 32, 64}.
+ *               The bf16 kernels contract in steps of 32 (the bf16 matrix
+ *               op), so a bf16 call with dk = 16 or C = 16 is widened: q, k,
+ *               v are copied to fp32 in the workspace (exactly), the fp32
+ *               kernels run, and O, Vtilde are rounded to bf16 (nearest
+ *               even).  Its arithmetic is the fp32 path's.
  *   q, k        [B][H][T][dk]  (dtype); every k_t is used as given.
  *   v           [B][H][T][dv]  (dtype)
  *   alpha, mu, beta, eta   [B][H][T] fp32, linear (not log) gates.
@@ -161,7 +167,9 @@ int mdn_chunk_fwd_noalloc(int64_t B, int64_t H, int64_t T, int dk, int dv, int C
  * mdn_chunk_inter: the sequential inter-chunk stage: vtilde = T W, O and the
  *   S/M carry (step 4 and the closed form of step 2).  Takes the arguments of
  *   mdn_chunk_fwd and reads the workspace mdn_chunk_intra left for the same
- *   q, k and gates; the gates themselves are validated but not read. */
+ *   q, k and gates; the gates themselves are validated but not read.
+ * Both take the natively compiled shapes only: a bf16 call with dk = 16 or
+ * C = 16 (widened inside mdn_chunk_fwd) returns MDN_ERR_UNSUPPORTED. */
 int mdn_chunk_intra(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
                     const void* q, const void* k,
                     const float* alpha, const float* mu, const float* beta, const float* eta,
@@ -182,7 +190,9 @@ int mdn_chunk_inter(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int 
  * forward's materialised vtilde (the reason the forward stores it: summary,
  * step 7; article, section 6 and the Q&A), so v itself is not needed.
  *   B, H, T, dk, dv, C, dtype   as for mdn_chunk_fwd, with the same
- *               supported sizes.
+ *               supported sizes (bf16 at dk = 16 or C = 16 widened to fp32
+ *               in the workspace the same way: q, k, Vtilde, dO copied in,
+ *               dq, dk_out, dv_out rounded back).
  *   q, k, alpha, mu, beta, eta, S0, M0   the forward's inputs (S0/M0 NULL
  *               for zero).
  *   Vtilde      [B][H][T][dv] (dtype): the forward's vtilde for these inputs.

@@ -45,7 +45,10 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 int64_t elem_size(int dtype) { return dtype == MDN_BF16 ? 2 : 4; }
 
-bool dims_supported_chunk(int dtype, int dk, int dv, int C) {
+// Shapes the chunk kernels are compiled for in the given element type.  The
+// bf16 kernels tile every contraction in steps of 32 (the bf16 matrix-core
+// op), so they need dk and C of at least 32.
+bool dims_native_chunk(int dtype, int dk, int dv, int C) {
     if (dk != dv) return false;
     if (dtype == MDN_F32)
         return (dk == 16 || dk == 32 || dk == 64 || dk == 128) && (C == 16 || C == 32 || C == 64);
@@ -54,9 +57,15 @@ bool dims_supported_chunk(int dtype, int dk, int dv, int C) {
     return false;
 }
 
-bool dims_supported_bwd(int dtype, int dk, int dv, int C) {
-    if (dk != dv) return false;
-    return dims_supported_chunk(dtype, dk, dv, C);
+// bf16 calls at dk = 16 or C = 16: the fp32 kernels run on fp32 copies of
+// the bf16 inputs (exact), and the outputs are rounded back to bf16.  The
+// copies live in the workspace, after the fp32 call's own sections.
+bool dims_widened_chunk(int dtype, int dk, int dv, int C) {
+    return dtype == MDN_BF16 && !dims_native_chunk(dtype, dk, dv, C) && dims_native_chunk(MDN_F32, dk, dv, C);
+}
+
+bool dims_supported_chunk(int dtype, int dk, int dv, int C) {
+    return dims_native_chunk(dtype, dk, dv, C) || dims_widened_chunk(dtype, dk, dv, C);
 }
 
 bool dims_supported_step(int dtype, int dk, int dv) {
@@ -119,6 +128,28 @@ size_t workspace_of(const ChunkSizes& s, int C, int dtype) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MDN_OK : MDN_ERR_HIP; }
 
+// Widened forward (dims_widened_chunk): the fp32 call's workspace, then fp32
+// q, k, v, O and vtilde (byte offsets).
+struct WideFwd {
+    size_t base, q, k, v, O, Vt, total;
+};
+WideFwd wide_fwd_sections(const ChunkSizes& s, int C) {
+    WideFwd w;
+    const size_t qk = align256((size_t)s.qk_elems * 4), vv = align256((size_t)s.v_elems * 4);
+    w.base = workspace_of(s, C, MDN_F32);
+    w.q = w.base;
+    w.k = w.q + qk;
+    w.v = w.k + qk;
+    w.O = w.v + vv;
+    w.Vt = w.O + vv;
+    w.total = w.Vt + vv;
+    return w;
+}
+
+size_t fwd_workspace(const ChunkSizes& s, int dk, int dv, int C, int dtype) {
+    return dims_widened_chunk(dtype, dk, dv, C) ? wide_fwd_sections(s, C).total : workspace_of(s, C, dtype);
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,7 +178,7 @@ size_t mdn_chunk_fwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int dk, in
     ChunkSizes s;
     if (chunk_sizes(B, H, T, dk, dv, C, &s) != MDN_OK) return (size_t)-1;
     if (!dims_supported_chunk(dtype, dk, dv, C)) return (size_t)-1;
-    return workspace_of(s, C, dtype);
+    return fwd_workspace(s, dk, dv, C, dtype);
 }
 
 size_t mdn_chunk_fwd_varlen_workspace_bytes(int64_t H, int64_t T, int64_t nseq, int dk, int dv, int C, int dtype)
@@ -155,7 +186,7 @@ size_t mdn_chunk_fwd_varlen_workspace_bytes(int64_t H, int64_t T, int64_t nseq, 
     ChunkSizes s;
     if (varlen_sizes(H, T, nseq, dk, dv, C, &s) != MDN_OK) return (size_t)-1;
     if (!dims_supported_chunk(dtype, dk, dv, C)) return (size_t)-1;
-    return workspace_of(s, C, dtype);
+    return fwd_workspace(s, dk, dv, C, dtype);
 }
 
 // Backward workspace: the forward's sections (T^T and Aqk^T in place of T and
@@ -165,6 +196,28 @@ size_t mdn_chunk_fwd_varlen_workspace_bytes(int64_t H, int64_t T, int64_t nseq, 
 struct BwdSections {
     size_t mat, cf, st, part, vec, total;
 };
+
+BwdSections bwd_sections(const ChunkSizes& s, int dk, int C, int dtype);
+
+// Widened backward (dims_widened_chunk): the fp32 call's workspace, then fp32
+// q, k, vtilde, dO (inputs) and dq, dk, dv (outputs), as byte offsets.
+struct WideBwd {
+    size_t base, q, k, Vt, dO, dq, dk, dv, total;
+};
+WideBwd wide_bwd_sections(const ChunkSizes& s, int dk, int C) {
+    WideBwd w;
+    const size_t qk = align256((size_t)s.qk_elems * 4), vv = align256((size_t)s.v_elems * 4);
+    w.base = bwd_sections(s, dk, C, MDN_F32).total;
+    w.q = w.base;
+    w.k = w.q + qk;
+    w.Vt = w.k + qk;
+    w.dO = w.Vt + vv;
+    w.dq = w.dO + vv;
+    w.dk = w.dq + qk;
+    w.dv = w.dk + qk;
+    w.total = w.dv + vv;
+    return w;
+}
 
 BwdSections bwd_sections(const ChunkSizes& s, int dk, int C, int dtype) {
     BwdSections b;
@@ -181,7 +234,9 @@ BwdSections bwd_sections(const ChunkSizes& s, int dk, int C, int dtype) {
 // Validation shared by mdn_chunk_fwd, its two stages and the packed-batch
 // forward (s.nseq >= 0, sequence bounds cu).  `stage` is 3 (both), 1 (intra
 // only) or 2 (inter only); only the pointers a stage reads or writes are
-// required.
+// required.  With `wide` the call is a widened bf16 forward: it is checked
+// against the widened workspace size, and the kernel arguments are not used
+// (the fp32 call is prepared from the workspace copies).
 static int chunk_prepare(int stage, const ChunkSizes& s, int64_t T, int dk, int dv, int C, int dtype,
                          const int32_t* cu,
                          const void* q, const void* k, const void* v,
@@ -189,9 +244,10 @@ static int chunk_prepare(int stage, const ChunkSizes& s, int64_t T, int dk, int 
                          const float* S0, const float* M0,
                          void* O, float* S_T, float* M_T, void* Vtilde,
                          void* workspace, size_t workspace_bytes, void* stream,
-                         mdn::ChunkArgs* a, bool* empty)
+                         mdn::ChunkArgs* a, bool* empty, bool wide = false)
 {
-    if (!dims_supported_chunk(dtype, dk, dv, C)) return MDN_ERR_UNSUPPORTED;
+    if (wide ? !dims_widened_chunk(dtype, dk, dv, C) : !dims_native_chunk(dtype, dk, dv, C))
+        return MDN_ERR_UNSUPPORTED;
     const bool packed = s.nseq >= 0;
     *empty = s.BH == 0 || s.nseq == 0;
     if (*empty) return MDN_OK;
@@ -204,7 +260,7 @@ static int chunk_prepare(int stage, const ChunkSizes& s, int64_t T, int dk, int 
     if (inter && (!S_T || !M_T)) return MDN_ERR_NULL_ARG;
     if (seq && (!q || !k || !alpha || !mu || !beta || !eta)) return MDN_ERR_NULL_ARG;
     if (seq && inter && (!v || !O || !Vtilde)) return MDN_ERR_NULL_ARG;
-    const size_t need = workspace_of(s, C, dtype);
+    const size_t need = wide ? wide_fwd_sections(s, C).total : workspace_of(s, C, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return MDN_ERR_WORKSPACE;
 
     const void* all[] = {q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde, workspace};
@@ -256,6 +312,61 @@ static int chunk_prepare(int stage, const ChunkSizes& s, int64_t T, int dk, int 
     return MDN_OK;
 }
 
+// The launches of a prepared forward (plain or packed batch).
+static int fwd_launch(const mdn::ChunkArgs& a, int64_t T)
+{
+    int st;
+    if (a.cu) {
+        st = hip_status(mdn::launch_varlen_prep(a));
+        if (st != MDN_OK) return st;
+    }
+    if (T > 0) {
+        st = hip_status(mdn::launch_chunk_intra(a));
+        if (st != MDN_OK) return st;
+    }
+    return hip_status(mdn::launch_chunk_inter(a));
+}
+
+// Widened bf16 forward: the caller's arguments are checked as a bf16 call,
+// q, k and v are widened into the workspace, the fp32 forward runs on them
+// (its own workspace sections first), and O and vtilde are rounded back.
+static int fwd_widened(const ChunkSizes& s, int64_t T, int dk, int dv, int C, const int32_t* cu,
+                       const void* q, const void* k, const void* v,
+                       const float* alpha, const float* mu, const float* beta, const float* eta,
+                       const float* S0, const float* M0,
+                       void* O, float* S_T, float* M_T, void* Vtilde,
+                       void* workspace, size_t workspace_bytes, void* stream)
+{
+    mdn::ChunkArgs a;
+    bool empty = false;
+    int st = chunk_prepare(3, s, T, dk, dv, C, MDN_BF16, cu, q, k, v, alpha, mu, beta, eta, S0, M0,
+                           O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty, true);
+    if (st != MDN_OK || empty) return st;
+    const WideFwd w = wide_fwd_sections(s, C);
+    char* ws = (char*)workspace;
+    const bool seq = s.tok > 0;
+    float* q32 = seq ? (float*)(ws + w.q) : nullptr;
+    float* k32 = seq ? (float*)(ws + w.k) : nullptr;
+    float* v32 = seq ? (float*)(ws + w.v) : nullptr;
+    float* O32 = seq ? (float*)(ws + w.O) : nullptr;
+    float* Vt32 = seq ? (float*)(ws + w.Vt) : nullptr;
+    if (seq) {
+        st = hip_status(mdn::launch_convert(q, MDN_BF16, q32, s.qk_elems, stream));
+        if (st == MDN_OK) st = hip_status(mdn::launch_convert(k, MDN_BF16, k32, s.qk_elems, stream));
+        if (st == MDN_OK) st = hip_status(mdn::launch_convert(v, MDN_BF16, v32, s.v_elems, stream));
+        if (st != MDN_OK) return st;
+    }
+    mdn::ChunkArgs b;
+    st = chunk_prepare(3, s, T, dk, dv, C, MDN_F32, cu, q32, k32, v32, alpha, mu, beta, eta, S0, M0,
+                       O32, S_T, M_T, Vt32, w.base ? ws : nullptr, w.base, stream, &b, &empty);
+    if (st != MDN_OK || empty) return st;
+    st = fwd_launch(b, T);
+    if (st != MDN_OK || !seq) return st;
+    st = hip_status(mdn::launch_convert(O32, MDN_F32, O, s.v_elems, stream));
+    if (st != MDN_OK) return st;
+    return hip_status(mdn::launch_convert(Vt32, MDN_F32, Vtilde, s.v_elems, stream));
+}
+
 int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
                   const void* q, const void* k, const void* v,
                   const float* alpha, const float* mu, const float* beta, const float* eta,
@@ -268,14 +379,13 @@ int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dt
     ChunkSizes s;
     int st = chunk_sizes(B, H, T, dk, dv, C, &s);
     if (st != MDN_OK) return st;
+    if (dims_widened_chunk(dtype, dk, dv, C))
+        return fwd_widened(s, T, dk, dv, C, nullptr, q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde,
+                           workspace, workspace_bytes, stream);
     st = chunk_prepare(3, s, T, dk, dv, C, dtype, nullptr, q, k, v, alpha, mu, beta, eta, S0, M0,
                        O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
     if (st != MDN_OK || empty) return st;
-    if (T > 0) {
-        st = hip_status(mdn::launch_chunk_intra(a));
-        if (st != MDN_OK) return st;
-    }
-    return hip_status(mdn::launch_chunk_inter(a));
+    return fwd_launch(a, T);
 }
 
 // ---------------------------------------------------------------------------
@@ -322,7 +432,7 @@ int mdn_chunk_fwd_noalloc(int64_t B, int64_t H, int64_t T, int dk, int dv, int C
     int st = chunk_sizes(B, H, T, dk, dv, C, &s);
     if (st != MDN_OK) return st;
     if (!dims_supported_chunk(dtype, dk, dv, C)) return MDN_ERR_UNSUPPORTED;
-    const size_t need = workspace_of(s, C, dtype);
+    const size_t need = fwd_workspace(s, dk, dv, C, dtype);
     if (need > (size_t)MDN_NOALLOC_SCRATCH_BYTES) return MDN_ERR_TOO_LARGE;
     void* ws = nullptr;
     if (need > 0) {
@@ -374,59 +484,24 @@ size_t mdn_chunk_bwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int dk, in
 {
     ChunkSizes s;
     if (chunk_sizes(B, H, T, dk, dv, C, &s) != MDN_OK) return (size_t)-1;
-    if (!dims_supported_bwd(dtype, dk, dv, C)) return (size_t)-1;
+    if (!dims_supported_chunk(dtype, dk, dv, C)) return (size_t)-1;
     int64_t x;
     if (!mul_ok(s.tiles, (int64_t)dk * dk, &x)) return (size_t)-1;
-    return bwd_sections(s, dk, C, dtype).total;
+    return dims_widened_chunk(dtype, dk, dv, C) ? wide_bwd_sections(s, dk, C).total : bwd_sections(s, dk, C, dtype).total;
 }
 
-int mdn_chunk_bwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
-                  const void* q, const void* k,
-                  const float* alpha, const float* mu, const float* beta, const float* eta,
-                  const float* S0, const float* M0, const void* Vtilde,
-                  const void* dO, const float* dS_T, const float* dM_T,
-                  void* dq, void* dk_out, void* dv_out,
-                  float* dalpha, float* dmu, float* dbeta, float* deta, float* dS0, float* dM0,
-                  void* workspace, size_t workspace_bytes, void* stream)
+// The launches of a checked backward call (element type dtype, natively
+// compiled shape); `workspace` holds bwd_sections(s, dk, C, dtype).
+static int bwd_launch(const ChunkSizes& s, int64_t T, int dk, int dv, int C, int dtype,
+                      const void* q, const void* k,
+                      const float* alpha, const float* mu, const float* beta, const float* eta,
+                      const float* S0, const float* M0, const void* Vtilde,
+                      const void* dO, const float* dS_T, const float* dM_T,
+                      void* dq, void* dk_out, void* dv_out,
+                      float* dalpha, float* dmu, float* dbeta, float* deta, float* dS0, float* dM0,
+                      void* workspace, void* stream)
 {
-    ChunkSizes s;
-    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
-    if (st != MDN_OK) return st;
-    if (!dims_supported_bwd(dtype, dk, dv, C)) return MDN_ERR_UNSUPPORTED;
-    int64_t x;
-    if (!mul_ok(s.tiles, (int64_t)dk * dk, &x)) return MDN_ERR_BAD_SHAPE;
-    if (s.BH == 0) return MDN_OK;
-    const bool seq = s.tok > 0;
-    if (!dS0 || !dM0) return MDN_ERR_NULL_ARG;
-    if (seq && (!q || !k || !alpha || !mu || !beta || !eta || !Vtilde || !dO || !dq || !dk_out || !dv_out ||
-                !dalpha || !dmu || !dbeta || !deta))
-        return MDN_ERR_NULL_ARG;
     const BwdSections sec = bwd_sections(s, dk, C, dtype);
-    if (sec.total > 0 && (!workspace || workspace_bytes < sec.total)) return MDN_ERR_WORKSPACE;
-    const void* all[] = {q, k, alpha, mu, beta, eta, S0, M0, Vtilde, dO, dS_T, dM_T,
-                         dq, dk_out, dv_out, dalpha, dmu, dbeta, deta, dS0, dM0, workspace};
-    for (const void* p : all)
-        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
-    const int64_t es = elem_size(dtype);
-    const Range ins[] = {range_of(q, s.qk_elems * es), range_of(k, s.qk_elems * es),
-                         range_of(alpha, s.g_elems * 4), range_of(mu, s.g_elems * 4),
-                         range_of(beta, s.g_elems * 4), range_of(eta, s.g_elems * 4),
-                         range_of(S0, S0 ? s.st_elems * 4 : 0), range_of(M0, M0 ? s.st_elems * 4 : 0),
-                         range_of(Vtilde, s.v_elems * es), range_of(dO, s.v_elems * es),
-                         range_of(dS_T, dS_T ? s.st_elems * 4 : 0), range_of(dM_T, dM_T ? s.st_elems * 4 : 0)};
-    const Range outs[] = {range_of(dq, s.qk_elems * es), range_of(dk_out, s.qk_elems * es),
-                          range_of(dv_out, s.v_elems * es), range_of(dalpha, s.g_elems * 4),
-                          range_of(dmu, s.g_elems * 4), range_of(dbeta, s.g_elems * 4),
-                          range_of(deta, s.g_elems * 4), range_of(dS0, s.st_elems * 4),
-                          range_of(dM0, s.st_elems * 4), range_of(workspace, (int64_t)sec.total)};
-    constexpr int NI = sizeof(ins) / sizeof(ins[0]), NO = sizeof(outs) / sizeof(outs[0]);
-    for (int i = 0; i < NO; ++i) {
-        for (int j = 0; j < NI; ++j)
-            if (overlap(outs[i], ins[j])) return MDN_ERR_ALIAS;
-        for (int j = i + 1; j < NO; ++j)
-            if (overlap(outs[i], outs[j])) return MDN_ERR_ALIAS;
-    }
-
     mdn::BwdArgs a;
     memset(&a, 0, sizeof(a));
     mdn::ChunkArgs& f = a.f;
@@ -453,6 +528,85 @@ int mdn_chunk_bwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dt
     return hip_status(mdn::launch_bwd(a));
 }
 
+int mdn_chunk_bwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                  const void* q, const void* k,
+                  const float* alpha, const float* mu, const float* beta, const float* eta,
+                  const float* S0, const float* M0, const void* Vtilde,
+                  const void* dO, const float* dS_T, const float* dM_T,
+                  void* dq, void* dk_out, void* dv_out,
+                  float* dalpha, float* dmu, float* dbeta, float* deta, float* dS0, float* dM0,
+                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    ChunkSizes s;
+    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
+    if (st != MDN_OK) return st;
+    const bool wide = dims_widened_chunk(dtype, dk, dv, C);
+    if (!wide && !dims_native_chunk(dtype, dk, dv, C)) return MDN_ERR_UNSUPPORTED;
+    int64_t x;
+    if (!mul_ok(s.tiles, (int64_t)dk * dk, &x)) return MDN_ERR_BAD_SHAPE;
+    if (s.BH == 0) return MDN_OK;
+    const bool seq = s.tok > 0;
+    if (!dS0 || !dM0) return MDN_ERR_NULL_ARG;
+    if (seq && (!q || !k || !alpha || !mu || !beta || !eta || !Vtilde || !dO || !dq || !dk_out || !dv_out ||
+                !dalpha || !dmu || !dbeta || !deta))
+        return MDN_ERR_NULL_ARG;
+    const size_t need = wide ? wide_bwd_sections(s, dk, C).total : bwd_sections(s, dk, C, dtype).total;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return MDN_ERR_WORKSPACE;
+    const void* all[] = {q, k, alpha, mu, beta, eta, S0, M0, Vtilde, dO, dS_T, dM_T,
+                         dq, dk_out, dv_out, dalpha, dmu, dbeta, deta, dS0, dM0, workspace};
+    for (const void* p : all)
+        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
+    const int64_t es = elem_size(dtype);
+    const Range ins[] = {range_of(q, s.qk_elems * es), range_of(k, s.qk_elems * es),
+                         range_of(alpha, s.g_elems * 4), range_of(mu, s.g_elems * 4),
+                         range_of(beta, s.g_elems * 4), range_of(eta, s.g_elems * 4),
+                         range_of(S0, S0 ? s.st_elems * 4 : 0), range_of(M0, M0 ? s.st_elems * 4 : 0),
+                         range_of(Vtilde, s.v_elems * es), range_of(dO, s.v_elems * es),
+                         range_of(dS_T, dS_T ? s.st_elems * 4 : 0), range_of(dM_T, dM_T ? s.st_elems * 4 : 0)};
+    const Range outs[] = {range_of(dq, s.qk_elems * es), range_of(dk_out, s.qk_elems * es),
+                          range_of(dv_out, s.v_elems * es), range_of(dalpha, s.g_elems * 4),
+                          range_of(dmu, s.g_elems * 4), range_of(dbeta, s.g_elems * 4),
+                          range_of(deta, s.g_elems * 4), range_of(dS0, s.st_elems * 4),
+                          range_of(dM0, s.st_elems * 4), range_of(workspace, (int64_t)need)};
+    constexpr int NI = sizeof(ins) / sizeof(ins[0]), NO = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < NO; ++i) {
+        for (int j = 0; j < NI; ++j)
+            if (overlap(outs[i], ins[j])) return MDN_ERR_ALIAS;
+        for (int j = i + 1; j < NO; ++j)
+            if (overlap(outs[i], outs[j])) return MDN_ERR_ALIAS;
+    }
+
+    if (!wide)
+        return bwd_launch(s, T, dk, dv, C, dtype, q, k, alpha, mu, beta, eta, S0, M0, Vtilde, dO, dS_T, dM_T,
+                          dq, dk_out, dv_out, dalpha, dmu, dbeta, deta, dS0, dM0, workspace, stream);
+    // widened bf16 call: fp32 copies of q, k, vtilde and dO, the fp32
+    // backward on them, and dq, dk, dv rounded back
+    const WideBwd w = wide_bwd_sections(s, dk, C);
+    char* ws = (char*)workspace;
+    void* q32 = seq ? ws + w.q : nullptr;
+    void* k32 = seq ? ws + w.k : nullptr;
+    void* Vt32 = seq ? ws + w.Vt : nullptr;
+    void* dO32 = seq ? ws + w.dO : nullptr;
+    void* dq32 = seq ? ws + w.dq : nullptr;
+    void* dk32 = seq ? ws + w.dk : nullptr;
+    void* dv32 = seq ? ws + w.dv : nullptr;
+    int st2 = MDN_OK;
+    if (seq) {
+        st2 = hip_status(mdn::launch_convert(q, MDN_BF16, q32, s.qk_elems, stream));
+        if (st2 == MDN_OK) st2 = hip_status(mdn::launch_convert(k, MDN_BF16, k32, s.qk_elems, stream));
+        if (st2 == MDN_OK) st2 = hip_status(mdn::launch_convert(Vtilde, MDN_BF16, Vt32, s.v_elems, stream));
+        if (st2 == MDN_OK) st2 = hip_status(mdn::launch_convert(dO, MDN_BF16, dO32, s.v_elems, stream));
+        if (st2 != MDN_OK) return st2;
+    }
+    st2 = bwd_launch(s, T, dk, dv, C, MDN_F32, q32, k32, alpha, mu, beta, eta, S0, M0, Vt32, dO32, dS_T, dM_T,
+                     dq32, dk32, dv32, dalpha, dmu, dbeta, deta, dS0, dM0, w.base ? ws : nullptr, stream);
+    if (st2 != MDN_OK || !seq) return st2;
+    st2 = hip_status(mdn::launch_convert(dq32, MDN_F32, dq, s.qk_elems, stream));
+    if (st2 == MDN_OK) st2 = hip_status(mdn::launch_convert(dk32, MDN_F32, dk_out, s.qk_elems, stream));
+    if (st2 == MDN_OK) st2 = hip_status(mdn::launch_convert(dv32, MDN_F32, dv_out, s.v_elems, stream));
+    return st2;
+}
+
 int mdn_chunk_fwd_varlen(int64_t H, int64_t T, int64_t nseq, const int32_t* cu_seqlens,
                          int dk, int dv, int C, int dtype,
                          const void* q, const void* k, const void* v,
@@ -466,16 +620,13 @@ int mdn_chunk_fwd_varlen(int64_t H, int64_t T, int64_t nseq, const int32_t* cu_s
     ChunkSizes s;
     int st = varlen_sizes(H, T, nseq, dk, dv, C, &s);
     if (st != MDN_OK) return st;
+    if (dims_widened_chunk(dtype, dk, dv, C))
+        return fwd_widened(s, T, dk, dv, C, cu_seqlens, q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T,
+                           Vtilde, workspace, workspace_bytes, stream);
     st = chunk_prepare(3, s, T, dk, dv, C, dtype, cu_seqlens, q, k, v, alpha, mu, beta, eta, S0, M0,
                        O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
     if (st != MDN_OK || empty) return st;
-    st = hip_status(mdn::launch_varlen_prep(a));
-    if (st != MDN_OK) return st;
-    if (T > 0) {
-        st = hip_status(mdn::launch_chunk_intra(a));
-        if (st != MDN_OK) return st;
-    }
-    return hip_status(mdn::launch_chunk_inter(a));
+    return fwd_launch(a, T);
 }
 
 int mdn_step(int64_t B, int64_t H, int dk, int dv, int dtype,

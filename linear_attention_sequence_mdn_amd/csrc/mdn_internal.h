@@ -79,6 +79,9 @@ struct GateArgs {
 hipError_t launch_step(const StepArgs& a);
 // in-place read, scale and write of n16 16-byte pieces (decode bandwidth reference)
 hipError_t launch_stream_rw(void* buf, int64_t n16, float scale, void* stream);
+// n values (a multiple of 8) from src to dst: bf16 -> fp32 when src_dtype is
+// bf16, else fp32 -> bf16 (round to nearest even)
+hipError_t launch_convert(const void* src, int src_dtype, void* dst, int64_t n, void* stream);
 // gate pre-operation and query correction
 hipError_t launch_gates(const GateArgs& g);
 // coefficient + intra-chunk stage (T, (QK^T) o Gamma, coefficients)

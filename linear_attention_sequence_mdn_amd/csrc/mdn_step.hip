@@ -202,4 +202,46 @@ hipError_t launch_stream_rw(void* buf, int64_t n16, float scale, void* stream)
     return hipGetLastError();
 }
 
+// Element-type conversion of n values (n a multiple of 8): bf16 -> fp32
+// (exact) or fp32 -> bf16 (round to nearest even), 8 values per thread.
+__global__ __launch_bounds__(256)
+void mdn_widen_kernel(const uint4* __restrict__ src, floatx4* __restrict__ dst, int64_t n8)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    union { uint4 u; __bf16 h[8]; } x;
+    x.u = src[i];
+    dst[2 * i] = floatx4{(float)x.h[0], (float)x.h[1], (float)x.h[2], (float)x.h[3]};
+    dst[2 * i + 1] = floatx4{(float)x.h[4], (float)x.h[5], (float)x.h[6], (float)x.h[7]};
+}
+
+__global__ __launch_bounds__(256)
+void mdn_narrow_kernel(const floatx4* __restrict__ src, uint4* __restrict__ dst, int64_t n8)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const floatx4 a = src[2 * i], b = src[2 * i + 1];
+    union { uint4 u; __bf16 h[8]; } y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        y.h[e] = (__bf16)a[e];
+        y.h[4 + e] = (__bf16)b[e];
+    }
+    dst[i] = y.u;
+}
+
+hipError_t launch_convert(const void* src, int src_dtype, void* dst, int64_t n, void* stream)
+{
+    if (n == 0) return hipSuccess;
+    if (n % 8 != 0) return hipErrorInvalidValue;
+    const int64_t n8 = n / 8, blocks = (n8 + 255) / 256;
+    if (src_dtype == 1)
+        hipLaunchKernelGGL(mdn_widen_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                           reinterpret_cast<const uint4*>(src), reinterpret_cast<floatx4*>(dst), n8);
+    else
+        hipLaunchKernelGGL(mdn_narrow_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                           reinterpret_cast<const floatx4*>(src), reinterpret_cast<uint4*>(dst), n8);
+    return hipGetLastError();
+}
+
 }  // namespace mdn

@@ -67,7 +67,12 @@ def test_workspace_bytes(L):
     assert L.mdn_chunk_fwd_workspace_bytes(1, 1, 0, 16, 16, 16, 0) == 0
     bad = ctypes.c_size_t(-1).value
     assert L.mdn_chunk_fwd_workspace_bytes(1, 1, 64, 48, 48, 16, 0) == bad
-    assert L.mdn_chunk_fwd_workspace_bytes(1, 1, 64, 16, 16, 16, 1) == bad    # bf16 needs d >= 32
+    # bf16 at d = 16 or C = 16 runs the fp32 kernels on widened copies: the
+    # fp32 workspace, then fp32 q, k, v, O and vtilde
+    f32 = L.mdn_chunk_fwd_workspace_bytes(1, 1, 64, 16, 16, 16, 0)
+    assert L.mdn_chunk_fwd_workspace_bytes(1, 1, 64, 16, 16, 16, 1) == f32 + 5 * 64 * 16 * 4
+    f32 = L.mdn_chunk_fwd_workspace_bytes(2, 3, 100, 128, 128, 16, 0)
+    assert L.mdn_chunk_fwd_workspace_bytes(2, 3, 100, 128, 128, 16, 1) == f32 + 5 * 600 * 128 * 4
     assert L.mdn_chunk_fwd_workspace_bytes(-1, 1, 64, 16, 16, 16, 0) == bad
 
 
@@ -94,7 +99,9 @@ def chunk_call(L, B=1, H=1, T=64, d=16, C=16, dt=0, ptrs=None, ws_bytes=None, S0
 def test_chunk_unsupported(L):
     assert chunk_call(L, d=48) == UNSUPPORTED
     assert chunk_call(L, C=128) == UNSUPPORTED
-    assert chunk_call(L, d=16, dt=1) == UNSUPPORTED
+    assert chunk_call(L, d=16, C=128, dt=1) == UNSUPPORTED
+    # the widened bf16 shapes need the widened workspace
+    assert chunk_call(L, d=16, dt=1, ws_bytes=L.mdn_chunk_fwd_workspace_bytes(1, 1, 64, 16, 16, 16, 0)) == WORKSPACE
     assert chunk_call(L, dt=7) == UNSUPPORTED
     p = addrs(14)
     assert L.mdn_chunk_fwd(1, 1, 64, 32, 64, 32, 1, *p[:13], p[13], 1 << 20, None) == UNSUPPORTED
@@ -225,6 +232,9 @@ def test_stage_entry_points_validate(L):
     assert L.mdn_chunk_intra(1, 1, 64, 16, 16, 16, 0, q, k, a, m, b, e, ws, need - 1, None) == WORKSPACE
     assert L.mdn_chunk_intra(1, 1, 64, 16, 16, 16, 0, None, k, a, m, b, e, ws, need, None) == NULL_ARG
     assert L.mdn_chunk_intra(1, 1, 64, 48, 48, 16, 0, q, k, a, m, b, e, ws, need, None) == UNSUPPORTED
+    # the stage entry points expose the workspace in the element type: they
+    # take the natively compiled shapes only
+    assert L.mdn_chunk_intra(1, 1, 64, 16, 16, 16, 1, q, k, a, m, b, e, ws, need, None) == UNSUPPORTED
     assert L.mdn_chunk_intra(1, 1, 64, 16, 16, 16, 0, q, k, a, m, b, e, q, need, None) == ALIAS
     assert L.mdn_chunk_inter(1, 1, 64, 16, 16, 16, 0, q, k, v, a, m, b, e, s0, m0, O, ST, MT, None,
                              ws, need, None) == NULL_ARG
@@ -314,13 +324,16 @@ def test_bwd_workspace_bytes(L):
     assert mdn.chunk_bwd_workspace_bytes(B, H, T, d, d, C, mdn.MDN_BF16) == expect
     bad = ctypes.c_size_t(-1).value
     assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 48, 48, 16, 0) == bad
-    assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 16, 16, 32, 1) == bad       # bf16 needs d >= 32
-    assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, 128, 128, 16, 1) == bad     # and C >= 32
+    # widened bf16 shapes: the fp32 workspace, then fp32 q, k, vtilde, dO, dq, dk, dv
+    for d, C in ((16, 32), (128, 16)):
+        f32 = L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, d, d, C, 0)
+        assert L.mdn_chunk_bwd_workspace_bytes(1, 1, 64, d, d, C, 1) == f32 + 7 * 64 * d * 4
 
 
 def test_bwd_validation(L):
     assert bwd_call(L, d=48) == UNSUPPORTED
-    assert bwd_call(L, dt=1, d=16, C=32) == UNSUPPORTED
+    assert bwd_call(L, dt=1, d=16, C=128) == UNSUPPORTED
+    assert bwd_call(L, dt=1, d=16, C=32, ws_bytes=L.mdn_chunk_bwd_workspace_bytes(1, 2, 64, 16, 16, 32, 0)) == WORKSPACE
     assert bwd_call(L, T=-1) == BAD_SHAPE
     assert bwd_call(L, B=0, ptrs=[None] * 22) == OK
     p = addrs(22)

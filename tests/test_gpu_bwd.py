@@ -66,6 +66,15 @@ def test_bwd_bf16_small(d, C, T):
     check(run_bwd(x, dO, dST, dMT), ref_bwd(x, dO, dST, dMT), TOL["bf16"], f"bwd bf16 d{d} C{C} T{T}")
 
 
+# bf16 at d = 16 or C = 16: the fp32 backward on widened copies
+@pytest.mark.parametrize("d,C,T", [(16, 32, 70), (16, 16, 33), (64, 16, 50)])
+def test_bwd_bf16_widened(d, C, T):
+    x = inputs.make_chunk_inputs(2, 2, T, d, C=C, dtype="bf16", seed=11 * d + C + T, state_std=0.02)
+    dO, dST, dMT = upstream(x, d + T)
+    note(f"bwd bf16 (widened) d={d} C={C} T={T}")
+    check(run_bwd(x, dO, dST, dMT), ref_bwd(x, dO, dST, dMT), TOL["bf16"], f"bwd bf16 wide d{d} C{C} T{T}")
+
+
 def test_bwd_zero_state_no_state_gradients():
     x = inputs.make_chunk_inputs(1, 2, 150, 128, C=64, dtype="bf16", seed=40)
     dO, _, _ = upstream(x, 40, with_states=False)

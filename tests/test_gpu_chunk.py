@@ -49,6 +49,16 @@ def test_bf16_small_ragged(d, C, T):
     check_all(run_chunk(x), oracle_of(x), TOL["bf16"], f"bf16 d{d} C{C} T{T}")
 
 
+# bf16 at d = 16 or C = 16: the fp32 kernels on widened copies, outputs
+# rounded to bf16.
+@pytest.mark.parametrize("d,C,T", [(16, 16, 100), (16, 32, 70), (16, 64, 130), (32, 16, 50), (64, 16, 33),
+                                   (128, 16, 64)])
+def test_bf16_widened_shapes(d, C, T):
+    x = inputs.make_chunk_inputs(2, 2, T, d, C=C, dtype="bf16", seed=5 * d + C + T, state_std=0.02)
+    note(f"chunk bf16 (widened) d={d} C={C} T={T}")
+    check_all(run_chunk(x), oracle_of(x), TOL["bf16"], f"bf16 wide d{d} C{C} T{T}")
+
+
 # Few heads launch slabs of one 16-column tile; enough heads to fill more
 # than half of the compute units launch slabs of two (the launch compares
 # 2 * B * H * d / 32 with the device's compute-unit count).  The cases above

@@ -49,6 +49,8 @@ CASES = [
     ("f32", 16, 16, 2, [1, 15, 16, 17, 50, 0, 3]),
     ("f32", 32, 32, 2, [70, 0, 31]),
     ("f32", 128, 64, 2, [65, 130, 1]),
+    ("bf16", 16, 16, 2, [1, 15, 17, 0, 40]),       # widened to the fp32 kernels
+    ("bf16", 64, 16, 2, [33, 16, 2]),
 ]
 
 
