@@ -16,6 +16,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace mdn {
 
@@ -198,6 +199,40 @@ __device__ __forceinline__ void wave_scan_affine(float& A, float& B) {
     affine_step<DPP_ROW_SHR8>(A, B);
     affine_step<DPP_ROW_BCAST15, 0xa>(A, B);
     affine_step<DPP_ROW_BCAST31, 0xc>(A, B);
+}
+
+// ---------------------------------------------------------------------------
+// Inverse of a 16 x 16 unit lower-triangular matrix I + A by forward
+// substitution in registers, one wave: lane (r, g) (r = lane % 16, g =
+// lane / 16) holds row r of A in a[0..3] (columns 4q .. 4q+3 in a[q]) and
+// returns row r of (I + A)^{-1} at columns 4g .. 4g+3 in t.  Only A's
+// strictly lower part is used.  Step Q takes row Q, final after the steps
+// before it, to every row of the lane's 16-lane row group by a DPP row
+// broadcast (row_newbcast) and subtracts A[r][Q] times it from rows r > Q.
+// ---------------------------------------------------------------------------
+template <int Q>
+__device__ __forceinline__ void unit_lower_inv16_step(float (&t)[4], const floatx4 (&a)[4], int r)
+{
+    const float lq = Q < r ? a[Q / 4][Q % 4] : 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float tq = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(t[c]), 0x150 + Q, 0xf, 0xf,
+                                                                    false));
+        t[c] = fmaf(-lq, tq, t[c]);
+    }
+}
+template <int... Q>
+__device__ __forceinline__ void unit_lower_inv16_steps(float (&t)[4], const floatx4 (&a)[4], int r,
+                                                       std::integer_sequence<int, Q...>)
+{
+    (unit_lower_inv16_step<Q>(t, a, r), ...);
+}
+__device__ __forceinline__ void unit_lower_inv16(float (&t)[4], const floatx4 (&a)[4], int lane)
+{
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t[c] = (r == 4 * g + c) ? 1.f : 0.f;
+    unit_lower_inv16_steps(t, a, r, std::make_integer_sequence<int, 15>{});
 }
 
 // ---------------------------------------------------------------------------

@@ -391,37 +391,28 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
     }
     lds_barrier();
 
-    // ---- 4a. diagonal blocks of T (wave 0, lane = 16 * block + column) --------
-    // forward substitution T[r][j] = delta_rj - sum_{i<r} A[r][i] T[i][j]
-    if (wave == 0) {
-        const int a = g, j = nn;
-        if (a < NCT) {
-            const float* Ab = sA + 16 * a * L::AS + 16 * a;
-            float tcol[16];
+    // ---- 4a. diagonal blocks of T: wave a inverts block a -------------------
+    // T_aa = (I + A_aa)^{-1} by forward substitution in registers (lane (r, g)
+    // holds row r of A_aa and returns row r of T_aa at columns 4g .. 4g+3),
+    // written over A's diagonal block and to the T out tile
+    if (wave < NCT) {
+        const int a = wave, r = nn;
+        floatx4 arow[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = (r == j) ? 1.f : 0.f;
+        for (int q4 = 0; q4 < 4; ++q4)
+            arow[q4] = *reinterpret_cast<const floatx4*>(sA + (16 * a + r) * L::AS + 16 * a + 4 * q4);
+        float t[4];
+        unit_lower_inv16(t, arow, lane);
+        // the wave's reads of A_aa have returned (t depends on them)
+        *reinterpret_cast<floatx4*>(sA + (16 * a + r) * L::AS + 16 * a + 4 * g) = floatx4{t[0], t[1], t[2], t[3]};
 #pragma unroll
-                for (int m4 = 0; m4 < (r + 3) / 4; ++m4) {
-                    const floatx4 a4 = *reinterpret_cast<const floatx4*>(Ab + r * L::AS + 4 * m4);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (4 * m4 + u < r) s = fmaf(-a4[u], tcol[4 * m4 + u], s);
-                }
-                tcol[r] = s;
-            }
-            // every lane of the group has read all of A_aa: overwrite it with T_aa
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sA[(16 * a + r) * L::AS + 16 * a + j] = tcol[r];
-                oT[(16 * a + r) * C + 16 * a + j] = Tr::from_f(tcol[r]);
-            }
-        }
-    } else {
-        // strictly upper blocks (a < b) of T are zero: waves 1-3, 16-byte stores
+        for (int c = 0; c < 4; ++c) oT[(16 * a + r) * C + 16 * a + 4 * g + c] = Tr::from_f(t[c]);
+    }
+    {
+        // strictly upper blocks (a < b) of T are zero: 16-byte stores
         constexpr int PB = 16 * L::ES / 16;          // 16-byte pieces per block row
         constexpr int NU = NCT * (NCT - 1) / 2;
-        for (int idx = tid - 64; idx < NU * 16 * PB; idx += 192) {
+        for (int idx = tid; idx < NU * 16 * PB; idx += 256) {
             int blk = idx / (16 * PB), a = 0;
             while (blk >= NCT - 1 - a) { blk -= NCT - 1 - a; ++a; }
             const int b = a + 1 + blk, rem = idx % (16 * PB);
