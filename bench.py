@@ -215,9 +215,22 @@ def chunk_bench(args, torch, mdn, inputs):
     roof["workspace_overhead"] = kern_bytes / call_bytes
     trs = [kd["traffic"] for kd in kernels.values()]
     roof["counted_traffic_over_alg"] = (sum(trs) / call_bytes) if all(t is not None for t in trs) else None
+    # the optional single-kernel forward (mdn_chunk_fwd_fused) on the same
+    # inputs, where it applies: K launches, same events and stream
+    fused = None
+    if x.dtype == "bf16" and C == 64 and d in (64, 128) and x.dk == x.dv:
+        for _ in range(args.warmup):
+            call.fused()
+        ms_fused = timed(call.fused)
+        fused = {"kernel": "mdn_fwd_kernel", "ms": ms_fused, "tokens_per_s": tokens / (ms_fused / 1e3),
+                 "GBps": call_bytes / (ms_fused / 1e3) / 1e9,
+                 "frac": call_bytes / (ms_fused / 1e3) / 1e9 / PEAK_HBM_GBS,
+                 "source_sha": kernel_sources_sha(["mdn_fwd.hip", "mdn_lds.h", "mdn_device.h"]),
+                 "note": "mdn_chunk_fwd_fused: the whole forward in one kernel without a workspace; "
+                         "value and roofline above are for mdn_chunk_fwd"}
     return dict(ms_step=ms_step, ms_call_median=ms_call_median, tokens_per_s=tps, mfma_frac=mfma_frac,
                 kernels=kernels, roofline=roof, finite=finite, x=x, cfg=cfg, call=call, call_bytes=call_bytes,
-                hbm_cap=hbm_cap)
+                hbm_cap=hbm_cap, fused=fused)
 
 
 def decode_bench(args, torch, mdn, inputs):
@@ -475,6 +488,8 @@ def main():
                     "call_alg_bytes": ch["call_bytes"], "hbm_capped_tokens_per_s": ch["hbm_cap"],
                     "frac_of_hbm_cap": ch["tokens_per_s"] / ch["hbm_cap"],
                     "kernels": ch["kernels"], "roofline": ch["roofline"], "outputs_finite": ch["finite"]})
+        if ch["fused"] is not None:
+            out["fused_forward"] = ch["fused"]
     if not args.no_decode:
         out["decode"] = decode_bench(args, torch, mdn, inputs)
     if not args.no_gates:

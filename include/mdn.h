@@ -132,6 +132,24 @@ int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dt
                   void* O, float* S_T, float* M_T, void* Vtilde,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* The whole forward in one kernel, without a workspace: the same arguments,
+ * results and errors as mdn_chunk_fwd (up to rounding: it computes the
+ * off-diagonal blocks of T with bf16 operands, where the two-kernel forward
+ * keeps T in fp32), for
+ *   dtype == MDN_BF16, C == 64, dk == dv in {64, 128};
+ * any other size returns MDN_ERR_UNSUPPORTED.  The per-chunk quantities of
+ * the summary's steps 2-5 (coefficients, Gamma, T, (Q K^T) o Gamma) stay on
+ * chip, so HBM carries q, k, v, the gates, O, Vtilde and the states only.
+ * On MI355X it is slower than mdn_chunk_fwd at these sizes (0.26 against
+ * 0.21 ms on B8 H8 T4096 d128): each of a head's four workgroups computes
+ * the head's whole intra-chunk stage.  Use it where no workspace can be
+ * given or HBM bandwidth is shared. */
+int mdn_chunk_fwd_fused(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha, const float* mu, const float* beta, const float* eta,
+                        const float* S0, const float* M0,
+                        void* O, float* S_T, float* M_T, void* Vtilde, void* stream);
+
 /* mdn_chunk_fwd for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, semantics and errors as mdn_chunk_fwd, without the
@@ -331,7 +349,7 @@ const char* mdn_status_string(int status);
 /* ABI revision of this header (incremented on any signature change). */
 int mdn_abi_version(void);
 
-#define MDN_ABI_VERSION 6
+#define MDN_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,9 @@ Entry points (same names as the C ABI):
         -> (O, S_T, M_T, Vtilde)
     chunk_fwd_noalloc(q, k, v, alpha, mu, beta, eta, S0, M0, C, out=(O, Vt), S_T=, M_T=)
         -> (O, S_T, M_T, Vtilde)   workspace in the library's static scratch
+    chunk_fwd_fused(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64)
+        -> (O, S_T, M_T, Vtilde)   the forward in one kernel, no workspace
+                                   (bf16, C = 64, d in {64, 128})
     chunk_fwd_varlen(q, k, v, alpha, mu, beta, eta, cu_seqlens, S0=None, M0=None, C=64)
         -> (O, S_T, M_T, Vtilde)   packed variable-length batch
     step(q, k, v, alpha, mu, beta, eta, S, M) -> o   (S, M updated in place)
@@ -69,6 +72,8 @@ def lib():
         L.mdn_chunk_fwd_varlen.restype = i32
         L.mdn_chunk_fwd_noalloc.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp]
         L.mdn_chunk_fwd_noalloc.restype = i32
+        L.mdn_chunk_fwd_fused.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp]
+        L.mdn_chunk_fwd_fused.restype = i32
         L.mdn_chunk_intra.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 6 + [vp, sz, vp]
         L.mdn_chunk_intra.restype = i32
         L.mdn_chunk_inter.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
@@ -216,6 +221,13 @@ class ChunkCall:
         _check(lib().mdn_chunk_intra(*self.sizes, p[0], p[1], p[3], p[4], p[5], p[6], *self._ws,
                                      _stream(stream, self._owned)), "mdn_chunk_intra")
 
+    def fused(self, stream=None):
+        """``mdn_chunk_fwd_fused`` on the same arguments (the workspace is
+        not used)."""
+        _check(lib().mdn_chunk_fwd_fused(*self.sizes, *self._ptrs, _stream(stream, self._owned)),
+               "mdn_chunk_fwd_fused")
+        return self.outputs
+
     def inter(self, stream=None):
         _check(lib().mdn_chunk_inter(*self.sizes, *self._ptrs, *self._ws, _stream(stream, self._owned)),
                "mdn_chunk_inter")
@@ -250,6 +262,16 @@ def chunk_fwd_noalloc(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, *, 
                      workspace=_NO_WORKSPACE)
     _check(lib().mdn_chunk_fwd_noalloc(*call.sizes, *call._ptrs, _stream(stream)), "mdn_chunk_fwd_noalloc")
     return call.outputs
+
+
+def chunk_fwd_fused(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, *, out=None, S_T=None, M_T=None,
+                    stream=None):
+    """``mdn_chunk_fwd_fused``: the chunk forward in one kernel, without a
+    workspace (bf16, C = 64, dk = dv in {64, 128}); arguments and results as
+    :func:`chunk_fwd`."""
+    call = ChunkCall(q, k, v, alpha, mu, beta, eta, S0, M0, C, out=out, S_T=S_T, M_T=M_T,
+                     workspace=_NO_WORKSPACE)
+    return call.fused(stream)
 
 
 def chunk_bwd_workspace_bytes(B, H, T, dk, dv, C, dtype) -> int:

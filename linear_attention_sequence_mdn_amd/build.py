@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmdn.so")
-SOURCES = ["mdn_api.cpp", "mdn_step.hip", "mdn_intra.hip", "mdn_chunk.hip", "mdn_gates.hip", "mdn_bwd.hip"]
+SOURCES = ["mdn_api.cpp", "mdn_step.hip", "mdn_intra.hip", "mdn_chunk.hip", "mdn_fwd.hip", "mdn_gates.hip",
+           "mdn_bwd.hip"]
 HEADERS = ["mdn_device.h", "mdn_internal.h", "mdn_lds.h"]
 ARCH = os.environ.get("MDN_OFFLOAD_ARCH", "gfx950")
 

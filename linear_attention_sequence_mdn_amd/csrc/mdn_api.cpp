@@ -244,7 +244,7 @@ static int chunk_prepare(int stage, const ChunkSizes& s, int64_t T, int dk, int 
                          const float* S0, const float* M0,
                          void* O, float* S_T, float* M_T, void* Vtilde,
                          void* workspace, size_t workspace_bytes, void* stream,
-                         mdn::ChunkArgs* a, bool* empty, bool wide = false)
+                         mdn::ChunkArgs* a, bool* empty, bool wide = false, bool no_workspace = false)
 {
     if (wide ? !dims_widened_chunk(dtype, dk, dv, C) : !dims_native_chunk(dtype, dk, dv, C))
         return MDN_ERR_UNSUPPORTED;
@@ -260,7 +260,7 @@ static int chunk_prepare(int stage, const ChunkSizes& s, int64_t T, int dk, int 
     if (inter && (!S_T || !M_T)) return MDN_ERR_NULL_ARG;
     if (seq && (!q || !k || !alpha || !mu || !beta || !eta)) return MDN_ERR_NULL_ARG;
     if (seq && inter && (!v || !O || !Vtilde)) return MDN_ERR_NULL_ARG;
-    const size_t need = wide ? wide_fwd_sections(s, C).total : workspace_of(s, C, dtype);
+    const size_t need = no_workspace ? 0 : wide ? wide_fwd_sections(s, C).total : workspace_of(s, C, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return MDN_ERR_WORKSPACE;
 
     const void* all[] = {q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde, workspace};
@@ -386,6 +386,27 @@ int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dt
                        O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
     if (st != MDN_OK || empty) return st;
     return fwd_launch(a, T);
+}
+
+// The whole forward in one kernel (no workspace): bf16, C = 64, dk = dv in
+// {64, 128}.
+int mdn_chunk_fwd_fused(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha, const float* mu, const float* beta, const float* eta,
+                        const float* S0, const float* M0,
+                        void* O, float* S_T, float* M_T, void* Vtilde, void* stream)
+{
+    mdn::ChunkArgs a;
+    bool empty = false;
+    ChunkSizes s;
+    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
+    if (st != MDN_OK) return st;
+    if (!(dtype == MDN_BF16 && C == 64 && dk == dv && (dk == 64 || dk == 128))) return MDN_ERR_UNSUPPORTED;
+    st = chunk_prepare(3, s, T, dk, dv, C, dtype, nullptr, q, k, v, alpha, mu, beta, eta, S0, M0,
+                       O, S_T, M_T, Vtilde, nullptr, 0, stream, &a, &empty, false, true);
+    if (st != MDN_OK || empty) return st;
+    if (!mdn::fwd_fused_supported(a)) return MDN_ERR_UNSUPPORTED;
+    return hip_status(mdn::launch_chunk_fwd_fused(a));
 }
 
 // ---------------------------------------------------------------------------

@@ -90,6 +90,10 @@ hipError_t launch_chunk_intra(const ChunkArgs& a);
 hipError_t launch_chunk_coef(const ChunkArgs& a);
 // sequential inter-chunk stage (vtilde, O, state carry)
 hipError_t launch_chunk_inter(const ChunkArgs& a);
+// the whole forward in one kernel, without a workspace, for the shapes it
+// covers (bf16, C = 64, dk = dv in {64, 128}, [B, H, T] layout)
+bool fwd_fused_supported(const ChunkArgs& a);
+hipError_t launch_chunk_fwd_fused(const ChunkArgs& a);
 // slot table and dispatch order of a packed variable-length batch (a.cu set)
 hipError_t launch_varlen_prep(const ChunkArgs& a);
 

@@ -34,6 +34,7 @@ def test_header_declares_expected_entry_points():
     for n in ("mdn_chunk_fwd", "mdn_step", "mdn_chunk_fwd_workspace_bytes", "mdn_chunk_intra",
               "mdn_chunk_inter", "mdn_chunk_coef", "mdn_gates", "mdn_chunk_fwd_varlen",
               "mdn_chunk_fwd_varlen_workspace_bytes", "mdn_chunk_bwd", "mdn_chunk_bwd_workspace_bytes",
+              "mdn_chunk_fwd_fused", "mdn_chunk_fwd_noalloc", "mdn_stream_rw",
               "mdn_status_string", "mdn_abi_version"):
         assert n in names
 
@@ -49,7 +50,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.mdn_abi_version() == 6
+    assert L.mdn_abi_version() == 7
 
 
 def test_status_strings(L):
@@ -354,3 +355,24 @@ def test_bwd_validation(L):
     q = list(p)
     q[21] = q[8]                               # workspace on Vtilde
     assert bwd_call(L, ptrs=q) == ALIAS
+
+
+def test_fused_forward_validation(L):
+    p = addrs(13)
+    f = lambda B=1, H=2, T=64, d=128, C=64, dt=1, ptrs=p: L.mdn_chunk_fwd_fused(B, H, T, d, d, C, dt, *ptrs, None)
+    assert f(dt=0) == UNSUPPORTED                 # fp32
+    assert f(C=32) == UNSUPPORTED
+    assert f(d=32) == UNSUPPORTED
+    assert L.mdn_chunk_fwd_fused(1, 2, 64, 128, 64, 64, 1, *p, None) == UNSUPPORTED   # dk != dv
+    assert f(B=-1) == BAD_SHAPE
+    assert f(B=0, ptrs=[None] * 13) == OK
+    for i in (0, 1, 2, 3, 4, 5, 6, 9, 10, 11, 12):
+        q = list(p)
+        q[i] = None
+        assert f(ptrs=q) == NULL_ARG, i
+    q = list(p)
+    q[9] = q[0]                                   # O over q
+    assert f(ptrs=q) == ALIAS
+    q = list(p)
+    q[12] = ctypes.c_void_p(BASE + 8)             # misaligned vtilde
+    assert f(ptrs=q) == ALIGN
