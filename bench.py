@@ -8,7 +8,11 @@ the 400M-layer workload: B=8, H=8, T=4096, dk=dv=128, C=64, bf16 q/k/v,
 fp32 gates, zero initial state.  Inputs are synthetic (seeded generator) and
 resident in HBM before the timed region.  W untimed warm-up steps, then K
 steps timed with HIP events on the stream the kernels run on, bracketed by
-device synchronisation.  ``value`` = B*T / time per step (tokens/s).  Each
+device synchronisation.  Before the warm-up steps of each timed section the
+device is held for ``--settle-ms`` (200 ms) under a neutral load (a bf16
+matrix product from torch, not the measured path): from idle the clocks ramp
+up over tens of milliseconds, and a few warm-up steps alone would time the
+ramp.  ``value`` = B*T / time per step (tokens/s).  Each
 kernel's average launch duration comes from K back-to-back launches of its
 stage entry point, timed the same way right after.
 
@@ -68,6 +72,11 @@ def parse():
     p.add_argument("--no-varlen", action="store_true")
     p.add_argument("--no-bwd", action="store_true")
     p.add_argument("--no-chunk", action="store_true")
+    p.add_argument("--settle-ms", type=float, default=200.0,
+                   help="device settling before each section's warm-up: ms of in-place stream load (0 = none)")
+    p.add_argument("--settle-kind", choices=("gemm", "stream"), default="gemm")
+    p.add_argument("--sustained-ms", type=float, default=150.0,
+                   help="after the chunk section, ms of back-to-back calls before the sustained-load window")
     p.add_argument("--decode-reps", type=int, default=5)
     p.add_argument("--decode-steps", type=int, default=128)
     p.add_argument("--calibration-copy", action="store_true",
@@ -103,6 +112,34 @@ def load_traffic(summary, sha):
     return d.get("traffic_bytes_per_launch")
 
 
+def settle_device(args, torch, mdn):
+    """Hold the device under a neutral load, not the measured path, for
+    ``--settle-ms`` of wall time, so that the warm-up steps that follow start
+    from running clocks rather than from the idle state: a bf16 matrix
+    product of two 8192 x 8192 operands (``--settle-kind gemm``) or an
+    in-place read-write stream over 256 MiB (``stream``).  Returns what was
+    run."""
+    if args.settle_ms <= 0:
+        return None
+    if args.settle_kind == "gemm":
+        a = torch.ones((8192, 8192), dtype=torch.bfloat16, device="cuda")
+        b = torch.ones((8192, 8192), dtype=torch.bfloat16, device="cuda")
+        c = torch.empty((8192, 8192), dtype=torch.bfloat16, device="cuda")
+        work, kind = (lambda: torch.mm(a, b, out=c)), "torch.mm bf16 8192 x 8192 x 8192"
+    else:
+        buf = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        work, kind = (lambda: mdn.stream_rw(buf, 1.0)), "mdn_stream_rw, 256 MiB in place"
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        for _ in range(4):
+            work()
+        torch.cuda.synchronize()
+        n += 4
+    return {"kind": kind, "ms": round((time.perf_counter() - t0) * 1e3, 1), "launches": n}
+
+
 WORKLOAD_NAMES = {
     1: "400M-layer chunk forward B8 H8 T4096 dk=dv=128 C64 bf16, zero initial state",
     2: "1.3B-layer chunk forward B4 H16 T4096 dk=dv=128 C64 bf16, S0/M0 ~ N(0, 0.02^2)",
@@ -123,6 +160,7 @@ def chunk_bench(args, torch, mdn, inputs):
     call = mdn.ChunkCall(q, k, v, *gates, S0, M0, C)
     torch.cuda.synchronize()
 
+    settle = settle_device(args, torch, mdn)
     for _ in range(args.warmup):
         call.run()
     torch.cuda.synchronize()
@@ -228,9 +266,21 @@ def chunk_bench(args, torch, mdn, inputs):
                  "source_sha": kernel_sources_sha(["mdn_fwd.hip", "mdn_lds.h", "mdn_device.h"]),
                  "note": "mdn_chunk_fwd_fused: the whole forward in one kernel without a workspace; "
                          "value and roofline above are for mdn_chunk_fwd"}
+    # a side figure, not the value: K calls timed after --sustained-ms of
+    # back-to-back calls, where the clocks have settled under this load
+    sustained = None
+    if args.sustained_ms > 0:
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < args.sustained_ms:
+            for _ in range(8):
+                call.run()
+            torch.cuda.synchronize()
+        ms_sus = timed(call.run)
+        sustained = {"ms_per_call": ms_sus, "tokens_per_s": tokens / (ms_sus / 1e3),
+                     "after_ms_of_calls": args.sustained_ms}
     return dict(ms_step=ms_step, ms_call_median=ms_call_median, tokens_per_s=tps, mfma_frac=mfma_frac,
                 kernels=kernels, roofline=roof, finite=finite, x=x, cfg=cfg, call=call, call_bytes=call_bytes,
-                hbm_cap=hbm_cap, fused=fused)
+                hbm_cap=hbm_cap, fused=fused, settle=settle, sustained=sustained)
 
 
 def decode_bench(args, torch, mdn, inputs):
@@ -259,6 +309,7 @@ def decode_bench(args, torch, mdn, inputs):
             if st != 0:
                 raise mdn.MdnError(st, "mdn_step")
 
+    settle_device(args, torch, mdn)
     run_all()                                           # warm-up pass
     times = []
     for _ in range(args.decode_reps):
@@ -320,6 +371,7 @@ def bwd_bench(args, torch, mdn, inputs, ch):
     rng = np.random.default_rng(901)
     dO = torch.from_numpy(rng.standard_normal(O.shape).astype(np.float32)).cuda().to(torch.bfloat16)
     bc = mdn.BwdCall(q, k, alpha, mu, beta, eta, Vt, dO, S0, M0, None, None, x.C)
+    settle_device(args, torch, mdn)
     for _ in range(args.warmup):
         bc.run()
     torch.cuda.synchronize()
@@ -351,6 +403,7 @@ def varlen_bench(args, torch, mdn, inputs):
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q, k, v = to(x.q).to(torch.bfloat16), to(x.k).to(torch.bfloat16), to(x.v).to(torch.bfloat16)
     call = mdn.VarlenCall(q, k, v, to(x.alpha), to(x.mu), to(x.beta), to(x.eta), to(x.cu), None, None, C)
+    settle_device(args, torch, mdn)
     for _ in range(args.warmup):
         call.run()
     torch.cuda.synchronize()
@@ -379,6 +432,7 @@ def gates_bench(args, torch, mdn, inputs):
     outs = tuple(torch.empty((B, H, T), dtype=torch.float32, device="cuda") for _ in range(4))
     qo = torch.empty_like(q)
     run = lambda: mdn.gates(x, a, b, ml, q=q, k=k, d=dd, q_out=qo, out=outs)
+    settle_device(args, torch, mdn)
     for _ in range(3):
         run()
     torch.cuda.synchronize()
@@ -488,6 +542,9 @@ def main():
                     "call_alg_bytes": ch["call_bytes"], "hbm_capped_tokens_per_s": ch["hbm_cap"],
                     "frac_of_hbm_cap": ch["tokens_per_s"] / ch["hbm_cap"],
                     "kernels": ch["kernels"], "roofline": ch["roofline"], "outputs_finite": ch["finite"]})
+        out["settle"] = ch["settle"]
+        if ch["sustained"] is not None:
+            out["sustained_load"] = ch["sustained"]
         if ch["fused"] is not None:
             out["fused_forward"] = ch["fused"]
     if not args.no_decode:
