@@ -307,7 +307,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             const char* Al = cur + LT::A0;
             frag aa[KSC];
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) aa[ks] = LdsA<Tr, LT::PT, 1>::load(Al, SL::perm(16 * tc + nn), ks, g);
+            for (int ks = 0; ks < KSC; ++ks)
+                if (SL::lower_step(tc, ks)) aa[ks] = LdsA<Tr, LT::PT, 1>::load(Al, SL::perm(16 * tc + nn), ks, g);
 #pragma unroll
             for (int i = 0; i < NOC; ++i) {
                 const int oct = oc0 + i * OCS;
@@ -317,7 +318,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 for (int ks = 0; ks < KSC; ++ks) vf[ks] = vb[(oct * KSC + ks) * 64 + lane];
                 floatx4 o = R[i];
 #pragma unroll
-                for (int ks = 0; ks < KSC; ++ks) o = Tr::mma(aa[ks], vf[ks], o);
+                for (int ks = 0; ks < KSC; ++ks)
+                    if (SL::lower_step(tc, ks)) o = Tr::mma(aa[ks], vf[ks], o);
                 const int r0 = SL::perm(16 * tc + 4 * g), c = 16 * oct + nn;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -437,7 +439,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) tA[ks][tc] = LdsA<Tr, LT::PT>::load(Tl, SL::perm(16 * tc + nn), ks, g);
+            for (int tc = 0; tc < NCT; ++tc)
+                if (SL::lower_step(tc, ks)) tA[ks][tc] = LdsA<Tr, LT::PT>::load(Tl, SL::perm(16 * tc + nn), ks, g);
         floatx4 Vx[NCT];
 #pragma unroll
         for (int tc = 0; tc < NCT; ++tc) Vx[tc] = zero4();
@@ -465,7 +468,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             for (int ks = 0; ks < KSC; ++ks) {
                 const frag vB = VOperand<Tr, OW>::load(Vl, ct, ks, lane);
 #pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) Vx[tc] = Tr::mma(tA[ks][tc], vB, Vx[tc]);
+                for (int tc = 0; tc < NCT; ++tc)
+                    if (SL::lower_step(tc, ks)) Vx[tc] = Tr::mma(tA[ks][tc], vB, Vx[tc]);
             }
             // first half of the state updates, while the chunk-start M is at hand
             {
@@ -529,7 +533,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
-                for (int tc = 0; tc < NCT; ++tc) Vx[tc] = Tr::mma(tA[ks][tc], Wb[ks], Vx[tc]);
+                for (int tc = 0; tc < NCT; ++tc)
+                    if (SL::lower_step(tc, ks)) Vx[tc] = Tr::mma(tA[ks][tc], Wb[ks], Vx[tc]);
         }
         // S_h += K_h^T Diag(gS) vtilde;  M_h -= K_h^T Diag(gM) vtilde, one
         // contraction step at a time (with the operands read just before
