@@ -36,6 +36,17 @@
 
 namespace mdn {
 
+// Whether row tile t of a lower-triangular C x C matrix (T, Aqk), read as a
+// matrix-core A operand, can be nonzero in contraction step ks.  bf16: step
+// ks covers columns 32ks .. 32ks + 31 and the rows perm(16t + x) of tile t
+// all lie in the 32-row half t/2; fp32: step ks covers the columns
+// 16(ks/4) + ks%4 + 4g and tile t holds rows 16t .. 16t + 15.
+template <typename Tr>
+constexpr bool lower_step(int t, int ks)
+{
+    return std::is_same<Tr, TraitsBf16>::value ? ks <= (t >> 1) : (ks >> 2) <= t;
+}
+
 // ---------------------------------------------------------------------------
 // mdn_inter_kernel
 //
@@ -308,7 +319,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             frag aa[KSC];
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks)
-                if (SL::lower_step(tc, ks)) aa[ks] = LdsA<Tr, LT::PT, 1>::load(Al, SL::perm(16 * tc + nn), ks, g);
+                if (lower_step<Tr>(tc, ks)) aa[ks] = LdsA<Tr, LT::PT, 1>::load(Al, SL::perm(16 * tc + nn), ks, g);
 #pragma unroll
             for (int i = 0; i < NOC; ++i) {
                 const int oct = oc0 + i * OCS;
@@ -319,7 +330,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 floatx4 o = R[i];
 #pragma unroll
                 for (int ks = 0; ks < KSC; ++ks)
-                    if (SL::lower_step(tc, ks)) o = Tr::mma(aa[ks], vf[ks], o);
+                    if (lower_step<Tr>(tc, ks)) o = Tr::mma(aa[ks], vf[ks], o);
                 const int r0 = SL::perm(16 * tc + 4 * g), c = 16 * oct + nn;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -440,7 +451,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
             for (int tc = 0; tc < NCT; ++tc)
-                if (SL::lower_step(tc, ks)) tA[ks][tc] = LdsA<Tr, LT::PT>::load(Tl, SL::perm(16 * tc + nn), ks, g);
+                if (lower_step<Tr>(tc, ks)) tA[ks][tc] = LdsA<Tr, LT::PT>::load(Tl, SL::perm(16 * tc + nn), ks, g);
         floatx4 Vx[NCT];
 #pragma unroll
         for (int tc = 0; tc < NCT; ++tc) Vx[tc] = zero4();
@@ -469,7 +480,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                 const frag vB = VOperand<Tr, OW>::load(Vl, ct, ks, lane);
 #pragma unroll
                 for (int tc = 0; tc < NCT; ++tc)
-                    if (SL::lower_step(tc, ks)) Vx[tc] = Tr::mma(tA[ks][tc], vB, Vx[tc]);
+                    if (lower_step<Tr>(tc, ks)) Vx[tc] = Tr::mma(tA[ks][tc], vB, Vx[tc]);
             }
             // first half of the state updates, while the chunk-start M is at hand
             {
@@ -534,7 +545,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
                 for (int tc = 0; tc < NCT; ++tc)
-                    if (SL::lower_step(tc, ks)) Vx[tc] = Tr::mma(tA[ks][tc], Wb[ks], Vx[tc]);
+                    if (lower_step<Tr>(tc, ks)) Vx[tc] = Tr::mma(tA[ks][tc], Wb[ks], Vx[tc]);
         }
         // S_h += K_h^T Diag(gS) vtilde;  M_h -= K_h^T Diag(gM) vtilde, one
         // contraction step at a time (with the operands read just before

@@ -102,10 +102,6 @@ template <> struct Slots<TraitsBf16> {
         f.u = uint4{0u, 0u, 0u, 0u};
         return f.v;
     }
-    // whether row tile t (rows perm(16t + x), all in the 32-row half t/2) of
-    // a lower-triangular C x C matrix read as an A operand (LdsA: step ks
-    // covers columns 32ks .. 32ks + 31) can be nonzero in step ks
-    static constexpr bool lower_step(int t, int ks) { return ks <= (t >> 1); }
     // element e of accumulator tile t, read back from the B operands that
     // from_acc built from the whole column
     static __device__ __forceinline__ __bf16 acc_elem(const bf16x8* b, int t, int e) {
@@ -135,8 +131,6 @@ template <> struct Slots<TraitsF32> {
         return acc[ks >> 2][ks & 3] * s[0];
     }
     static __device__ __forceinline__ float zero() { return 0.f; }
-    // step ks covers columns 16(ks/4) + ks%4 + 4g; row tile t holds rows 16t .. 16t + 15
-    static constexpr bool lower_step(int t, int ks) { return (ks >> 2) <= t; }
     static __device__ __forceinline__ float acc_elem(const float* b, int t, int e) { return b[4 * t + e]; }
     static __device__ __forceinline__ void load_row(const float* p, int ks, int g, float (&out)[NSLOT]) {
         out[0] = p[row(ks, g, 0)];
