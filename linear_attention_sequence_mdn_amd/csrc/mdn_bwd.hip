@@ -893,11 +893,18 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     E* Ql = reinterpret_cast<E*>(lds + L::Q0);
     E* Kl = reinterpret_cast<E*>(lds + L::K0);
     float* vv = reinterpret_cast<float*>(lds + L::V0);
-    float* sLA = vv + 0 * C; float* sLM = vv + 1 * C; float* sAl = vv + 2 * C; float* sMu = vv + 3 * C;
+    float* sLM = vv + 1 * C; float* sAl = vv + 2 * C; float* sMu = vv + 3 * C;   // (slot 0 unused)
     float* sBe = vv + 4 * C; float* sEt = vv + 5 * C; float* sAb = vv + 6 * C; float* sB = vv + 7 * C;
     float* sGM = vv + 8 * C; float* sDa = vv + 9 * C; float* sDb = vv + 10 * C; float* sDab = vv + 11 * C;
     float* sDgM = vv + 12 * C; float* sDgS = vv + 13 * C; float* sZ = vv + 14 * C; float* sAd = vv + 15 * C;
     float* sRow = vv + 16 * C; float* sCol = vv + 17 * C; float* sZb = vv + 18 * C; float* sMisc = vv + 19 * C;
+    // LA, LM again in fp64, for the factors E[r,m] = exp(LA_r - LA_m) and
+    // F[m,i] = exp(LM_m - LM_i) formed from differences of the cumulative
+    // logs: in fp32 such a difference keeps only the absolute precision of
+    // the larger sum (about 1e-5 at |LA| ~ 100), while Psi comes from
+    // running products; the gate gradients subtract terms built from the two
+    // (rowsum(DPsi o Psi) against beta Z), which then disagree by that much
+    __shared__ double sLAd[C], sLMd[C];
 
     const int64_t tile = blockIdx.x;
     const int64_t bh = tile / NT, n = tile % NT;
@@ -925,7 +932,6 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         if (tid < C) {
             const int r = tid;
             const bool in = r < vm;
-            sLA[r] = cf[MDN_COEF_LA * C + r];
             sLM[r] = cf[MDN_COEF_LM * C + r];
             sAl[r] = in ? alpha[rowbase + r] : 1.f;
             sMu[r] = in ? mu[rowbase + r] : 1.f;
@@ -943,6 +949,22 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
             sCol[r] = 0.f;
         }
         if (tid < 3) sMisc[tid] = vt[5 * C + tid];    // <S,dS'>, <M,dS'>, <M,dM'>
+        if (wave == 0) {                              // inclusive fp64 scans of log alpha, log mu
+            double pa = lane < C ? log((double)sAl[lane]) : 0.0;
+            double pm = lane < C ? log((double)sMu[lane]) : 0.0;
+#pragma unroll
+            for (int s = 1; s < 64; s <<= 1) {
+                const double ya = __shfl_up(pa, s, 64), ym = __shfl_up(pm, s, 64);
+                if (lane >= s) {
+                    pa += ya;
+                    pm += ym;
+                }
+            }
+            if (lane < C) {
+                sLAd[lane] = pa;
+                sLMd[lane] = pm;
+            }
+        }
     }
     __syncthreads();
     if (tid < C) {
@@ -969,7 +991,7 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         const bool act = wave < NCT && i < C;
         float lv[16], dv[16];
         if (act) {
-            float w = (rb > i) ? expf(sLM[rb - 1] - sLM[i]) : 0.f;
+            float w = (rb > i) ? expf((float)(sLMd[rb - 1] - sLMd[i])) : 0.f;
             float loc = 0.f, d = 1.f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -1153,7 +1175,7 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
     // read from the lower triangle only)
     if (wave < NCT) {
         const int mA = 16 * wave + nn, m0 = 16 * wave + 4 * g;
-        const float laA = sLA[mA];
+        const double laA = sLAd[mA];
         floatx4 acc[NCT];
         float etc[NCT];
 #pragma unroll
@@ -1165,7 +1187,7 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         for (int ks = 0; ks < C / 4; ++ks) {
             if (ks < 4 * wave) continue;               // uniform: rows above the wave's block
             const int r = 4 * ks + g;
-            const float a = (r >= mA) ? expf(sLA[r] - laA) : 0.f;
+            const float a = (r >= mA) ? expf((float)(sLAd[r] - laA)) : 0.f;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 if (ct > wave) continue;
@@ -1179,11 +1201,11 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         for (int ct = 0; ct < NCT; ++ct) {
             if (ct > wave) continue;
             const int i = 16 * ct + nn;
-            const float lmi = sLM[i];
+            const double lmi = sLMd[i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = m0 + e;
-                zp[e] += (i <= m) ? acc[ct][e] * expf(sLM[m] - lmi) : 0.f;
+                zp[e] += (i <= m) ? acc[ct][e] * expf((float)(sLMd[m] - lmi)) : 0.f;
             }
         }
 #pragma unroll
@@ -1260,7 +1282,7 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
         if (in) {
             z = sZ[m] + sZb[m];
             const float cs = sCol[m];
-            de = cs + sDgM[m] * expf(sLM[LR] - sLM[m]);
+            de = cs + sDgM[m] * expf((float)(sLMd[LR] - sLMd[m]));
             dla = sRow[m] + sDb[m] * sB[m] - sBe[m] * z + sDa[m] * sAb[m];
             dlm = sBe[m] * z - sEt[m] * cs - sDgM[m] * sGM[m];
             tail = sDgM[m] * sGM[m];
@@ -1270,10 +1292,11 @@ void mdn_bwd_cgrad_kernel(const typename Tr::elem* __restrict__ q, const typenam
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1) tsum += __shfl_xor(tsum, s, 64);
         if (m == LR) dlm += tsum + sMisc[2] * expf(sLM[LR]);
-        // suffix sums over rows: total - inclusive prefix + own
-        const float pla = wave_scan_add(dla), plm = wave_scan_add(dlm);
-        const float tla = __shfl(pla, 63, 64), tlm = __shfl(plm, 63, 64);
-        const float sla = tla - pla + dla, slm = tlm - plm + dlm;
+        // suffix sums over rows, as inclusive scans over the reversed rows
+        // (forming them as the total minus a prefix cancels when the suffix is
+        // small against the total, and dalpha then divides by a small alpha)
+        const float sla = __shfl(wave_scan_add(__shfl(dla, 63 - m, 64)), 63 - m, 64);
+        const float slm = __shfl(wave_scan_add(__shfl(dlm, 63 - m, 64)), 63 - m, 64);
         if (in && m < vm) {
             const float bprev = m > 0 ? sB[m - 1] : 0.f;
             const size_t gi = rowbase + m;
