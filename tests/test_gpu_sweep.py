@@ -97,3 +97,20 @@ def test_sweep_decode_steps(dtype, d, B, H, steps, seed):
     es, em = rel_err(host(S), Sr), rel_err(host(M), Mr)
     note(f"  o={worst:.2e} S={es:.2e} M={em:.2e}")
     assert worst <= TOL[dtype] and es <= TOL[dtype] and em <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d,C,T,B,H", [("bf16", 128, 64, 130, 2, 80), ("bf16", 128, 32, 70, 3, 55),
+                                             ("f32", 128, 32, 40, 2, 37)])
+def test_grid_beyond_one_wave_of_workgroups(dtype, d, C, T, B, H):
+    """More heads than the device holds inter workgroups at once (each uses
+    most of a compute unit's LDS), so the workgroups run in several rounds;
+    B*H both a multiple of 8 (the XCD-aware head map) and not."""
+    x = inputs.make_chunk_inputs(B, H, T, d, C=C, dtype=dtype, seed=600 + d + H,
+                                 state_std=0.02 if dtype == "bf16" else 0.3)
+    note(f"chunk {dtype} d={d} C={C} T={T} B={B} H={H}: {B * H} heads")
+    got = run_chunk(x)
+    ref = oracle.fwd(x.q, x.k, x.v, x.alpha, x.mu, x.beta, x.eta, x.S0, x.M0)
+    errs = {n: rel_err(g, r) for n, g, r in zip(NAMES, got, ref)}
+    note("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL[dtype], (n, e)
