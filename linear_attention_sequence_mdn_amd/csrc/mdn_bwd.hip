@@ -35,6 +35,17 @@
 
 namespace mdn {
 
+// Whether row tile t of an upper-triangular C x C matrix (T^T, Aqk^T), read
+// as a matrix-core A operand, can be nonzero in contraction step ks.  bf16:
+// step ks covers columns 32ks .. 32ks + 31 and the rows perm(16t + x) of tile
+// t all lie in the 32-row half t/2; fp32: step ks covers the columns
+// 16(ks/4) + ks%4 + 4g and tile t holds rows 16t .. 16t + 15.
+template <typename Tr>
+constexpr bool upper_step(int t, int ks)
+{
+    return std::is_same<Tr, TraitsBf16>::value ? ks >= (t >> 1) : (ks >> 2) >= t;
+}
+
 // K^T (or Q^T) operand of a state-row product for d-tile td, contraction
 // step ks over chunk rows (natural order 32ks + 8g + j), from a swizzled
 // tile of P pieces per row.
@@ -164,11 +175,13 @@ template <typename Tr, int R> struct HandTile;
 template <int R> struct HandTile<TraitsBf16, R> {
     static constexpr int RS = R + 4;
     static constexpr int BYTES = 16 * RS * 2;
-    static __device__ __forceinline__ void write(const floatx4 (&X)[R / 16], __bf16* __restrict__ lt, int lane) {
+    // tiles t0 .. t0 + NX - 1 of the slice (all of it by default)
+    template <int NX>
+    static __device__ __forceinline__ void write(const floatx4 (&X)[NX], __bf16* __restrict__ lt, int lane, int t0 = 0) {
         const int g = lane >> 4, nn = lane & 15;
 #pragma unroll
-        for (int t = 0; t < R / 16; ++t) {
-            const int r = Slots<TraitsBf16>::perm(16 * t + 4 * g);
+        for (int t = 0; t < NX; ++t) {
+            const int r = Slots<TraitsBf16>::perm(16 * (t0 + t) + 4 * g);
             union { __bf16 h[4]; uint2 u; } v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v.h[e] = (__bf16)X[t][e];
@@ -196,12 +209,13 @@ template <int R> struct HandTile<TraitsBf16, R> {
 template <int R> struct HandTile<TraitsF32, R> {
     static constexpr int SS = 20;
     static constexpr int BYTES = R * SS * 4;
-    static __device__ __forceinline__ void write(const floatx4 (&X)[R / 16], float* __restrict__ lt, int lane) {
+    template <int NX>
+    static __device__ __forceinline__ void write(const floatx4 (&X)[NX], float* __restrict__ lt, int lane, int t0 = 0) {
         const int g = lane >> 4, nn = lane & 15;
 #pragma unroll
-        for (int t = 0; t < R / 16; ++t)
+        for (int t = 0; t < NX; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) lt[Slots<TraitsF32>::perm(16 * t + 4 * g + e) * SS + nn] = X[t][e];
+            for (int e = 0; e < 4; ++e) lt[Slots<TraitsF32>::perm(16 * (t0 + t) + 4 * g + e) * SS + nn] = X[t][e];
     }
     template <int NW>
     static __device__ __forceinline__ void copy(const char* lt, float* __restrict__ dst, int ld, int nrows, int tid) {
@@ -343,8 +357,37 @@ void mdn_bwd_replay_kernel(const typename Tr::elem* __restrict__ k, const typena
 // to HBM after the next barrier, and the other two stage (where the LDS
 // budget has no room for the hand-off tiles, the chain waves store them
 // through staging tiles themselves and all four loaders stage).
+//
+// Row split (RS = 2, where the LDS has room for it): each column tile has two
+// chain waves, h = 0 and 1, holding dk rows [h D/2, (h+1) D/2) of dS and dM.
+// Per chunk, wave h forms the part of K dS', K dM' over its own rows; wave 1
+// adds Aqk^T dO to its part and hands it to wave 0 through an LDS exchange
+// tile; wave 0 completes dvt and dW = T^T dvt and hands dW back through the
+// same tile.  Meanwhile both scale their rows to the chunk start and add the
+// products with dO, which need no dW; the products with dW follow.  Each
+// wave's in-order share per chunk drops from about 112 to about 60 matrix-core
+// products.  The two hand-offs are ordered by counters in LDS (release after
+// the tile is written, acquire before it is read), not by workgroup barriers,
+// so the loader waves and the other column tile never wait for them.
 // ---------------------------------------------------------------------------
-template <typename Tr, int D, int C, int NCOL, int NBUF>
+
+// Release and acquire of a per-chunk counter in LDS between two waves of one
+// workgroup.  The wait is bounded (about 2^22 polls, tens of milliseconds):
+// a handshake that never completes ends the kernel with wrong values instead
+// of hanging it.
+__device__ __forceinline__ void pair_release(int* f, int v)
+{
+    __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void pair_wait(int* f, int v)
+{
+    for (int i = 0; i < (1 << 22); ++i) {
+        if (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= v) return;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+template <typename Tr, int D, int C, int NCOL, int NBUF, int RS = 1>
 struct CarryLayout {
     using E = typename Tr::elem;
     static constexpr int ES = sizeof(E);
@@ -366,20 +409,33 @@ struct CarryLayout {
     // dM' slice tile, then C x 16 dV rows
     static constexpr int SLB = HandTile<Tr, D>::BYTES, DVB = HandTile<Tr, C>::BYTES, CTB = 2 * SLB + DVB;
     static constexpr int PAR = NCOL * CTB, HAND = 2 * PAR;
-    static constexpr bool OFF = NBUF == 2 && 2 * BUF + HAND <= 160 * 1024 - 1024;
-    static constexpr int TOTAL = NBUF * BUF + (OFF ? HAND : STG);
+    // row split: per column tile one C x 16 fp32 exchange tile (4 values per
+    // lane and row tile)
+    static constexpr int XB = RS > 1 ? NCOL * (C / 16) * 64 * 16 : 0;
+    static constexpr bool OFF = NBUF == 2 && 2 * BUF + HAND + XB <= 160 * 1024 - 1024;
+    static constexpr int TOTAL = NBUF * BUF + (OFF ? HAND : STG) + XB;
 };
 
 template <typename Tr, int D, int C>
 struct CarryPick {
     static constexpr int LIMIT = 160 * 1024 - 1024;
     static constexpr int NCOL = D >= 32 ? 2 : 1;
-    static constexpr int NBUF = CarryLayout<Tr, D, C, NCOL, 2>::TOTAL <= LIMIT ? 2 : 1;
-    static_assert(CarryLayout<Tr, D, C, NCOL, NBUF>::TOTAL <= LIMIT, "LDS");
+    // the row split only with double-buffered staging and the hand-off tiles
+    static constexpr int RS = (D >= 64 && CarryLayout<Tr, D, C, NCOL, 2, 2>::OFF) ? 2 : 1;
+    static constexpr int NBUF = CarryLayout<Tr, D, C, NCOL, 2, RS>::TOTAL <= LIMIT ? 2 : 1;
+    static_assert(CarryLayout<Tr, D, C, NCOL, NBUF, RS>::TOTAL <= LIMIT, "LDS");
+    static_assert(RS == 1 || (NBUF == 2 && CarryLayout<Tr, D, C, NCOL, NBUF, RS>::OFF), "row split layout");
+    // loader waves, of which NST stage (with the hand-off tiles) and the rest
+    // copy the hand-off tiles out.  The split chain is short enough that two
+    // staging waves (their copies in flight bound the bytes per chunk) and
+    // two copying waves would set the pace; with four of each, twelve waves,
+    // the chain does again.
+    static constexpr int NLD = RS > 1 ? 8 : 4;
+    static constexpr int NST = RS > 1 ? 4 : 2;
 };
 
-template <typename Tr, int D, int C, int NCOL, int NBUF>
-__global__ __launch_bounds__(64 * (NCOL + 4))
+template <typename Tr, int D, int C, int NCOL, int NBUF, int RS, int NLD, int NST>
+__global__ __launch_bounds__(64 * (NCOL * RS + NLD))
 void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typename Tr::elem* __restrict__ k,
                           const typename Tr::elem* __restrict__ TT, const typename Tr::elem* __restrict__ AT,
                           const float* __restrict__ coef, const typename Tr::elem* __restrict__ dO,
@@ -390,17 +446,24 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
 {
     using E = typename Tr::elem;
     using SL = Slots<Tr>;
-    using LT = CarryLayout<Tr, D, C, NCOL, NBUF>;
+    using LT = CarryLayout<Tr, D, C, NCOL, NBUF, RS>;
     using frag = typename Tr::frag;
     constexpr int NSL = SL::NSLOT, KSC = C / Tr::KW, KSD = D / Tr::KW, NCT = C / 16, NDH = D / 16;
     constexpr int SLABS = D / (16 * NCOL), OW = 16 * NCOL;
+    constexpr int NW = NCOL * RS;                      // chain waves
+    constexpr int NDL = NDH / RS, KSH = KSD / RS;      // a chain wave's d tiles and contraction steps over d
+    static_assert(NDH % RS == 0 && KSD % RS == 0, "row split");
     __shared__ __attribute__((aligned(16))) char stA[LT::BUF];
     __shared__ __attribute__((aligned(16))) char stB[NBUF == 2 ? LT::BUF : 16];
     constexpr bool OFF = LT::OFF;
-    constexpr int NDMA = OFF ? 2 : 4;                  // staging loader waves
+    constexpr int NDMA = OFF ? NST : NLD;              // staging loader waves
     // adjoint slices and dV rows on their way out (hand-off tiles, or per
     // column tile two staging tiles of the chain wave)
     __shared__ __attribute__((aligned(16))) char stg[OFF ? LT::HAND : LT::STG];
+    // row split: the exchange tiles and, per column tile, the counters of the
+    // two hand-offs (partial dvt to wave 0, dW to wave 1)
+    __shared__ __attribute__((aligned(16))) floatx4 xb[RS > 1 ? NCOL * NCT * 64 : 1];
+    __shared__ int xflag[RS > 1 ? 2 * NCOL : 1];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, nn = lane & 15;
@@ -409,8 +472,8 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
     const int col0 = slab * OW;
     auto valid_of = [&](int64_t n) { return (int)((T - n * C) < C ? (T - n * C) : C); };
 
-    if (wave >= NCOL) {
-        const int lw = wave - NCOL;
+    if (wave >= NW) {
+        const int lw = wave - NW;
         // iteration it handles chunk NT - 1 - it
         auto issue = [&](uint32_t buf, int64_t m) __attribute__((always_inline)) {
             const size_t rb = (size_t)bh * T + m * C, tile = (size_t)bh * NT + m;
@@ -438,15 +501,15 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
             const int64_t m = NT - 1 - j;
             const char* hb = stg + (j & 1) * LT::PAR;
             const size_t off = ((size_t)bh * NT + m) * D * D + col0;
-            constexpr int NW = 4 - NDMA;
+            constexpr int NCP = NLD - NDMA;             // copying waves
             const int ft = (lw - NDMA) * 64 + lane, vm = valid_of(m);
             E* dvd = dv + ((size_t)bh * T + m * C) * D + col0;
 #pragma unroll
             for (int c = 0; c < NCOL; ++c) {
                 const char* cb = hb + c * LT::CTB;
-                HandTile<Tr, D>::template copy<NW>(cb, dSst + off + 16 * c, D, D, ft);
-                HandTile<Tr, D>::template copy<NW>(cb + LT::SLB, dMst + off + 16 * c, D, D, ft);
-                HandTile<Tr, C>::template copy<NW>(cb + 2 * LT::SLB, dvd + 16 * c, D, vm, ft);
+                HandTile<Tr, D>::template copy<NCP>(cb, dSst + off + 16 * c, D, D, ft);
+                HandTile<Tr, D>::template copy<NCP>(cb + LT::SLB, dMst + off + 16 * c, D, D, ft);
+                HandTile<Tr, C>::template copy<NCP>(cb + 2 * LT::SLB, dvd + 16 * c, D, vm, ft);
             }
         };
         // with the hand-off, waves 0-1 stage and waves 2-3 copy out: the copying
@@ -480,18 +543,21 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
         return;
     }
 
-    const int ct = wave;
+    const int ct = wave / RS, h = wave % RS;          // column tile; part of the dk rows
     const int col = col0 + 16 * ct + nn;
     const size_t sbase = (size_t)bh * D * D;
-    floatx4 XS[NDH], XM[NDH];                          // dS, dM (rows perm(16t + 4g + e))
+    floatx4 XS[NDL], XM[NDL];                          // dS, dM (rows perm(16 (t + h NDL) + 4g + e))
 #pragma unroll
-    for (int t = 0; t < NDH; ++t)
+    for (int t = 0; t < NDL; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const size_t off = sbase + (size_t)SL::perm(16 * t + 4 * g + e) * D + col;
+            const size_t off = sbase + (size_t)SL::perm(16 * (t + h * NDL) + 4 * g + e) * D + col;
             XS[t][e] = dST ? dST[off] : 0.f;
             XM[t][e] = dMT ? dMT[off] : 0.f;
         }
+    if constexpr (RS > 1) {
+        if (h == 0 && lane < 2) xflag[2 * ct + lane] = 0;   // the first barrier orders it before any use
+    }
     auto crow = [&](const float* cf, int which, int tc) __attribute__((always_inline)) {
         return *reinterpret_cast<const floatx4*>(cf + which * C + SL::perm(16 * tc + 4 * g));
     };
@@ -514,124 +580,245 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
         char* hand = OFF ? stg + (it & 1) * LT::PAR + ct * LT::CTB : stg;
         E* sg = OFF ? reinterpret_cast<E*>(stg) : reinterpret_cast<E*>(stg) + ct * 2 * LT::SR * 16;
         if constexpr (OFF) {
-            HandTile<Tr, D>::write(XS, reinterpret_cast<E*>(hand), lane);
-            HandTile<Tr, D>::write(XM, reinterpret_cast<E*>(hand + LT::SLB), lane);
+            HandTile<Tr, D>::write(XS, reinterpret_cast<E*>(hand), lane, h * NDL);
+            HandTile<Tr, D>::write(XM, reinterpret_cast<E*>(hand + LT::SLB), lane, h * NDL);
         } else {
+            static_assert(RS == 1, "row split needs the hand-off tiles");
             const size_t off = tile * D * D + col0 + 16 * ct;
             store_slice<Tr, D>(XS, sg, dSst + off, lane);
             store_slice<Tr, D>(XM, sg + LT::SR * 16, dMst + off, lane);
         }
-        // dvt = Aqk^T dO + Diag(gS) K dS - Diag(gM) K dM
-        floatx4 dV[NCT];
-        {
-            floatx4 KS[NCT], KM[NCT];
+        if constexpr (RS == 1) {
+            // dvt = Aqk^T dO + Diag(gS) K dS - Diag(gM) K dM
+            floatx4 dV[NCT];
+            {
+                floatx4 KS[NCT], KM[NCT];
 #pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) { KS[tc] = zero4(); KM[tc] = zero4(); dV[tc] = zero4(); }
+                for (int tc = 0; tc < NCT; ++tc) { KS[tc] = zero4(); KM[tc] = zero4(); dV[tc] = zero4(); }
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                const frag sb = SL::from_acc(XS, ks), mb = SL::from_acc(XM, ks);
+                for (int ks = 0; ks < KSD; ++ks) {
+                    const frag sb = SL::from_acc(XS, ks), mb = SL::from_acc(XM, ks);
+#pragma unroll
+                    for (int tc = 0; tc < NCT; ++tc) {
+                        const frag a = LdsA<Tr, LT::PK>::load(Kl, SL::perm(16 * tc + nn), ks, g);
+                        KS[tc] = Tr::mma(a, sb, KS[tc]);
+                        KM[tc] = Tr::mma(a, mb, KM[tc]);
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) {
+                    const frag ob = ColOperand<Tr, OW>::load(Ol, ct, ks, lane);
+#pragma unroll
+                    for (int tc = 0; tc < NCT; ++tc)
+                        if (upper_step<Tr>(tc, ks))
+                            dV[tc] = Tr::mma(LdsA<Tr, LT::PT>::load(ATl, SL::perm(16 * tc + nn), ks, g), ob, dV[tc]);
+                }
 #pragma unroll
                 for (int tc = 0; tc < NCT; ++tc) {
-                    const frag a = LdsA<Tr, LT::PK>::load(Kl, SL::perm(16 * tc + nn), ks, g);
-                    KS[tc] = Tr::mma(a, sb, KS[tc]);
-                    KM[tc] = Tr::mma(a, mb, KM[tc]);
+                    const floatx4 gs = crow(cf, MDN_COEF_GS, tc), gm = crow(cf, MDN_COEF_GM, tc);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dV[tc][e] += gs[e] * KS[tc][e] - gm[e] * KM[tc][e];
                 }
             }
+            // dW = T^T dvt, which is dV of the chunk
+            floatx4 dW[NCT];
+            {
+                frag vb[KSC];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) vb[ks] = SL::from_acc(dV, ks);
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) {
+                    dW[tc] = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < KSC; ++ks)
+                        if (upper_step<Tr>(tc, ks))
+                            dW[tc] = Tr::mma(LdsA<Tr, LT::PT>::load(TTl, SL::perm(16 * tc + nn), ks, g), vb[ks], dW[tc]);
+                }
+            }
+            {
+                // dV rows of the chunk: C x 16 into the hand-off tile, or through
+                // the first staging tile
+                if constexpr (OFF) {
+                    HandTile<Tr, C>::write(dW, reinterpret_cast<E*>(hand + 2 * LT::SLB), lane);
+                } else {
+                    E* lt = sg;
+#pragma unroll
+                    for (int tc = 0; tc < NCT; ++tc)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) lt[SL::perm(16 * tc + 4 * g + e) * 16 + nn] = Tr::from_f(dW[tc][e]);
+                    constexpr int EPV = 16 / sizeof(E), PPR = 16 / EPV, NP = C * PPR;
+                    E* dst = dv + ((size_t)bh * T + n * C) * D + col0 + 16 * ct;
+#pragma unroll
+                    for (int i = 0; i < (NP + 63) / 64; ++i) {
+                        const int p = i * 64 + lane;
+                        const int r = p / PPR, c = (p % PPR) * EPV;
+                        if ((NP % 64 == 0 || p < NP) && r < vm)
+                            *reinterpret_cast<uint4*>(dst + (size_t)r * D + c) = reinterpret_cast<const uint4*>(lt)[p];
+                    }
+                }
+            }
+            // chunk-start adjoints
+            const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
+            const float bC = cf[MDN_COEF_B * C + C - 1];
+            const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
+#pragma unroll
+            for (int t = 0; t < NDH; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    XM[t][e] = mubarC * XM[t][e] - bC * XS[t][e];
+                    XS[t][e] = abarC * XS[t][e];
+                }
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
+                float sa[NSL], sb[NSL], sab[NSL], nsa[NSL];
+                SL::load_row(cf + MDN_COEF_ABAR * C, ks, g, sa);
+                SL::load_row(cf + MDN_COEF_B * C, ks, g, sb);
+                SL::load_row(cf + MDN_COEF_ABP * C, ks, g, sab);
+#pragma unroll
+                for (int j = 0; j < NSL; ++j) {
+                    nsa[j] = -sa[j];
+                    // the staged dO rows past the end repeat the last row: weight 0
+                    const bool in = SL::row(ks, g, j) < vm;
+                    sa[j] = in ? sa[j] : 0.f;
+                    sb[j] = in ? -sb[j] : 0.f;
+                }
                 const frag ob = ColOperand<Tr, OW>::load(Ol, ct, ks, lane);
+                const frag dOa = FragScale<Tr>::apply(ob, sa), dOb = FragScale<Tr>::apply(ob, sb);
+                const frag dWa = SL::from_acc_scaled(dW, ks, nsa), dWab = SL::from_acc_scaled(dW, ks, sab);
 #pragma unroll
-                for (int tc = 0; tc < NCT; ++tc)
-                    dV[tc] = Tr::mma(LdsA<Tr, LT::PT>::load(ATl, SL::perm(16 * tc + nn), ks, g), ob, dV[tc]);
-            }
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) {
-                const floatx4 gs = crow(cf, MDN_COEF_GS, tc), gm = crow(cf, MDN_COEF_GM, tc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dV[tc][e] += gs[e] * KS[tc][e] - gm[e] * KM[tc][e];
-            }
-        }
-        // dW = T^T dvt, which is dV of the chunk
-        floatx4 dW[NCT];
-        {
-            frag vb[KSC];
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) vb[ks] = SL::from_acc(dV, ks);
-#pragma unroll
-            for (int tc = 0; tc < NCT; ++tc) {
-                dW[tc] = zero4();
-#pragma unroll
-                for (int ks = 0; ks < KSC; ++ks)
-                    dW[tc] = Tr::mma(LdsA<Tr, LT::PT>::load(TTl, SL::perm(16 * tc + nn), ks, g), vb[ks], dW[tc]);
-            }
-        }
-        {
-            // dV rows of the chunk: C x 16 into the hand-off tile, or through
-            // the first staging tile
-            if constexpr (OFF) {
-                HandTile<Tr, C>::write(dW, reinterpret_cast<E*>(hand + 2 * LT::SLB), lane);
-            } else {
-                E* lt = sg;
-#pragma unroll
-                for (int tc = 0; tc < NCT; ++tc)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) lt[SL::perm(16 * tc + 4 * g + e) * 16 + nn] = Tr::from_f(dW[tc][e]);
-                constexpr int EPV = 16 / sizeof(E), PPR = 16 / EPV, NP = C * PPR;
-                E* dst = dv + ((size_t)bh * T + n * C) * D + col0 + 16 * ct;
-#pragma unroll
-                for (int i = 0; i < (NP + 63) / 64; ++i) {
-                    const int p = i * 64 + lane;
-                    const int r = p / PPR, c = (p % PPR) * EPV;
-                    if ((NP % 64 == 0 || p < NP) && r < vm)
-                        *reinterpret_cast<uint4*>(dst + (size_t)r * D + c) = reinterpret_cast<const uint4*>(lt)[p];
+                for (int t = 0; t < NDH; ++t) {
+                    const frag qT = TrOperand<Tr, LT::PK>::load(Ql, t, ks, lane);
+                    const frag kT = TrOperand<Tr, LT::PK>::load(Kl, t, ks, lane);
+                    XS[t] = Tr::mma(qT, dOa, XS[t]);
+                    XS[t] = Tr::mma(kT, dWa, XS[t]);
+                    XM[t] = Tr::mma(qT, dOb, XM[t]);
+                    XM[t] = Tr::mma(kT, dWab, XM[t]);
                 }
             }
-        }
-        // chunk-start adjoints
-        const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
-        const float bC = cf[MDN_COEF_B * C + C - 1];
-        const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
+        } else {
+            // this wave's part of K dS', K dM' (its dk rows), weighted by the
+            // gates: P = Diag(gS) K dS - Diag(gM) K dM over those rows
+            floatx4 P[NCT];
+            {
+                floatx4 KS[NCT], KM[NCT];
 #pragma unroll
-        for (int t = 0; t < NDH; ++t)
+                for (int tc = 0; tc < NCT; ++tc) { KS[tc] = zero4(); KM[tc] = zero4(); }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                XM[t][e] = mubarC * XM[t][e] - bC * XS[t][e];
-                XS[t][e] = abarC * XS[t][e];
+                for (int kl = 0; kl < KSH; ++kl) {
+                    const frag sb = SL::from_acc(XS, kl), mb = SL::from_acc(XM, kl);
+#pragma unroll
+                    for (int tc = 0; tc < NCT; ++tc) {
+                        const frag a = LdsA<Tr, LT::PK>::load(Kl, SL::perm(16 * tc + nn), kl + h * KSH, g);
+                        KS[tc] = Tr::mma(a, sb, KS[tc]);
+                        KM[tc] = Tr::mma(a, mb, KM[tc]);
+                    }
+                }
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) {
+                    const floatx4 gs = crow(cf, MDN_COEF_GS, tc), gm = crow(cf, MDN_COEF_GM, tc);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) P[tc][e] = gs[e] * KS[tc][e] - gm[e] * KM[tc][e];
+                }
             }
+            frag ob[KSC];
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) {
-            float sa[NSL], sb[NSL], sab[NSL], nsa[NSL];
-            SL::load_row(cf + MDN_COEF_ABAR * C, ks, g, sa);
-            SL::load_row(cf + MDN_COEF_B * C, ks, g, sb);
-            SL::load_row(cf + MDN_COEF_ABP * C, ks, g, sab);
+            for (int ks = 0; ks < KSC; ++ks) ob[ks] = ColOperand<Tr, OW>::load(Ol, ct, ks, lane);
+            floatx4* xt = xb + ct * NCT * 64 + lane;
+            if (h == 1) {
+                // Aqk^T dO joins this part, which goes to wave 0
 #pragma unroll
-            for (int j = 0; j < NSL; ++j) {
-                nsa[j] = -sa[j];
-                // the staged dO rows past the end repeat the last row: weight 0
-                const bool in = SL::row(ks, g, j) < vm;
-                sa[j] = in ? sa[j] : 0.f;
-                sb[j] = in ? -sb[j] : 0.f;
+                for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+                    for (int tc = 0; tc < NCT; ++tc)
+                        if (upper_step<Tr>(tc, ks))
+                            P[tc] = Tr::mma(LdsA<Tr, LT::PT>::load(ATl, SL::perm(16 * tc + nn), ks, g), ob[ks], P[tc]);
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) xt[tc * 64] = P[tc];
+                if (lane == 0) pair_release(&xflag[2 * ct], (int)it + 1);
             }
-            const frag ob = ColOperand<Tr, OW>::load(Ol, ct, ks, lane);
-            const frag dOa = FragScale<Tr>::apply(ob, sa), dOb = FragScale<Tr>::apply(ob, sb);
-            const frag dWa = SL::from_acc_scaled(dW, ks, nsa), dWab = SL::from_acc_scaled(dW, ks, sab);
+            // chunk-start adjoints of this wave's rows, and their products with dO
+            const float abarC = cf[MDN_COEF_ABAR * C + C - 1];
+            const float bC = cf[MDN_COEF_B * C + C - 1];
+            const float mubarC = expf(cf[MDN_COEF_LM * C + C - 1]);
 #pragma unroll
-            for (int t = 0; t < NDH; ++t) {
-                const frag qT = TrOperand<Tr, LT::PK>::load(Ql, t, ks, lane);
-                const frag kT = TrOperand<Tr, LT::PK>::load(Kl, t, ks, lane);
-                XS[t] = Tr::mma(qT, dOa, XS[t]);
-                XS[t] = Tr::mma(kT, dWa, XS[t]);
-                XM[t] = Tr::mma(qT, dOb, XM[t]);
-                XM[t] = Tr::mma(kT, dWab, XM[t]);
+            for (int t = 0; t < NDL; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    XM[t][e] = mubarC * XM[t][e] - bC * XS[t][e];
+                    XS[t][e] = abarC * XS[t][e];
+                }
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                float sa[NSL], sb[NSL];
+                SL::load_row(cf + MDN_COEF_ABAR * C, ks, g, sa);
+                SL::load_row(cf + MDN_COEF_B * C, ks, g, sb);
+#pragma unroll
+                for (int j = 0; j < NSL; ++j) {
+                    // the staged dO rows past the end repeat the last row: weight 0
+                    const bool in = SL::row(ks, g, j) < vm;
+                    sa[j] = in ? sa[j] : 0.f;
+                    sb[j] = in ? -sb[j] : 0.f;
+                }
+                const frag dOa = FragScale<Tr>::apply(ob[ks], sa), dOb = FragScale<Tr>::apply(ob[ks], sb);
+#pragma unroll
+                for (int t = 0; t < NDL; ++t) {
+                    const frag qT = TrOperand<Tr, LT::PK>::load(Ql, t + h * NDL, ks, lane);
+                    XS[t] = Tr::mma(qT, dOa, XS[t]);
+                    XM[t] = Tr::mma(qT, dOb, XM[t]);
+                }
+            }
+            // dvt = P_0 + P_1 (with Aqk^T dO) and dW = T^T dvt on wave 0, which
+            // hands dW to wave 1 and dW (the chunk's dV rows) to the loaders
+            floatx4 dW[NCT];
+            if (h == 0) {
+                pair_wait(&xflag[2 * ct], (int)it + 1);
+                floatx4 dV[NCT];
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) dV[tc] = P[tc] + xt[tc * 64];
+                frag vb[KSC];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) vb[ks] = SL::from_acc(dV, ks);
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) {
+                    dW[tc] = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < KSC; ++ks)
+                        if (upper_step<Tr>(tc, ks))
+                            dW[tc] = Tr::mma(LdsA<Tr, LT::PT>::load(TTl, SL::perm(16 * tc + nn), ks, g), vb[ks], dW[tc]);
+                }
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) xt[tc * 64] = dW[tc];
+                if (lane == 0) pair_release(&xflag[2 * ct + 1], (int)it + 1);
+                HandTile<Tr, C>::write(dW, reinterpret_cast<E*>(hand + 2 * LT::SLB), lane);
+            } else {
+                pair_wait(&xflag[2 * ct + 1], (int)it + 1);
+#pragma unroll
+                for (int tc = 0; tc < NCT; ++tc) dW[tc] = xt[tc * 64];
+            }
+            // the products with dW
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                float nsa[NSL], sab[NSL];
+                SL::load_row(cf + MDN_COEF_ABAR * C, ks, g, nsa);
+                SL::load_row(cf + MDN_COEF_ABP * C, ks, g, sab);
+#pragma unroll
+                for (int j = 0; j < NSL; ++j) nsa[j] = -nsa[j];
+                const frag dWa = SL::from_acc_scaled(dW, ks, nsa), dWab = SL::from_acc_scaled(dW, ks, sab);
+#pragma unroll
+                for (int t = 0; t < NDL; ++t) {
+                    const frag kT = TrOperand<Tr, LT::PK>::load(Kl, t + h * NDL, ks, lane);
+                    XS[t] = Tr::mma(kT, dWa, XS[t]);
+                    XM[t] = Tr::mma(kT, dWab, XM[t]);
+                }
             }
         }
     }
     if constexpr (OFF) lds_barrier();                   // the loaders copy the last chunk's hand-off
 #pragma unroll
-    for (int t = 0; t < NDH; ++t)
+    for (int t = 0; t < NDL; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const size_t off = sbase + (size_t)SL::perm(16 * t + 4 * g + e) * D + col;
+            const size_t off = sbase + (size_t)SL::perm(16 * (t + h * NDL) + 4 * g + e) * D + col;
             dS0[off] = XS[t][e];
             dM0[off] = XM[t][e];
         }
@@ -1324,8 +1511,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     using CP = CarryPick<Tr, D, C>;
-    hipLaunchKernelGGL((mdn_bwd_carry_kernel<Tr, D, C, CP::NCOL, CP::NBUF>), dim3((unsigned)grid),
-                       dim3(64 * (CP::NCOL + 4)), 0, (hipStream_t)f.stream, (const E*)f.q, (const E*)f.k,
+    hipLaunchKernelGGL((mdn_bwd_carry_kernel<Tr, D, C, CP::NCOL, CP::NBUF, CP::RS, CP::NLD, CP::NST>), dim3((unsigned)grid),
+                       dim3(64 * (CP::NCOL * CP::RS + CP::NLD)), 0, (hipStream_t)f.stream, (const E*)f.q, (const E*)f.k,
                        (const E*)f.Tmat, (const E*)f.Aqk, f.coef, (const E*)a.dO, a.dST, a.dMT, (E*)a.dv,
                        (E*)a.dSst, (E*)a.dMst, a.dS0, a.dM0, f.T, f.NT, (int)f.BH);
     e = hipGetLastError();
