@@ -200,9 +200,12 @@ def chunk_bench(args, torch, mdn, inputs):
     # algorithmic bytes / FLOP per launch of each kernel: what the kernel must
     # read and write (each input once, each output once) and its causal-triangle
     # matrix work
-    intra_bytes = tok_head * (2 * 2 * d + 16 + 2 * C * es + 8 * 4)
+    # T and Aqk without their all-zero upper-right quadrant (C = 64 in bf16),
+    # which the intra kernel does not write and the inter kernel does not read
+    tq = 2 * C * es * 3 // 4 if C == 64 else 2 * C * es
+    intra_bytes = tok_head * (2 * 2 * d + 16 + tq + 8 * 4)
     nstate = 2 if x.S0 is None else 4                 # S_T, M_T written (and S0, M0 read when given)
-    inter_bytes = tok_head * (es * 3 * d + es * 2 * d + 2 * C * es + 8 * 4) + B * H * nstate * d * d * 4
+    inter_bytes = tok_head * (es * 3 * d + es * 2 * d + tq + 8 * 4) + B * H * nstate * d * d * 4
     intra_flop = tok_head * (2 * C * d + (2 * C * C) // 3)
     inter_flop = tok_head * (12 * d * d + 2 * C * d)
     kernels = {

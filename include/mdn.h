@@ -93,9 +93,11 @@ enum {
  *   [B*H*NT][C][C]  T matrices   (dtype)
  *   [B*H*NT][C][C]  (Q K^T) o Gamma, zero above the diagonal (dtype)
  *   [B*H*NT][MDN_COEF_ROWS][C]  coefficients (fp32)
- * each section starting on a 256-byte boundary.  For a widened bf16 call
- * (dk = 16 or C = 16, see mdn_chunk_fwd) the layout is that of the fp32 call,
- * followed by fp32 copies of q, k, v, O and Vtilde. */
+ * each section starting on a 256-byte boundary.  Both matrices are lower
+ * triangular; for bf16 at C = 64 and fp32 at C >= 32 their upper-right
+ * C/2 x C/2 quadrant (all zero) is not written, and nothing reads it.  For
+ * a widened bf16 call (dk = 16 or C = 16, see mdn_chunk_fwd) the layout is
+ * that of the fp32 call, followed by fp32 copies of q, k, v, O and Vtilde. */
 size_t mdn_chunk_fwd_workspace_bytes(int64_t B, int64_t H, int64_t T,
                                      int dk, int dv, int C, int dtype);
 

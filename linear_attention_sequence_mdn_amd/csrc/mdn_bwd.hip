@@ -487,6 +487,9 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
             const int r0 = lw * RPL;
             dma_tile<RPL, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rb * D), seq_row, lane, r0);
             dma_tile<RPL, LT::PK>(buf + LT::Q0, reinterpret_cast<const char*>(q + rb * D), seq_row, lane, r0);
+            // whole rows, the quadrant the intra stage leaves unwritten
+            // included (no product reads it; leaving it out of the copies
+            // measured slower here, 876 against 865 us for the whole call)
             dma_tile<RPL, LT::PT>(buf + LT::TT0, reinterpret_cast<const char*>(TT + tile * C * C), t_row, lane, r0);
             dma_tile<RPL, LT::PT>(buf + LT::AT0, reinterpret_cast<const char*>(AT + tile * C * C), t_row, lane, r0);
             if (lw == NDMA - 2)

@@ -97,6 +97,7 @@ struct InterLayout {
     static constexpr int PT = C * ES / 16;            // pieces per T/Aqk row
     static constexpr int PV = 16 * NCOL * ES / 16;    // pieces per V-slab / out row
     static constexpr int PC = MDN_COEF_ROWS * C * 4 / 16;
+    static constexpr bool QUAD = quad_unread<Tr, C>();  // T, Aqk staged without their zero quadrant
     static_assert((PK & (PK - 1)) == 0 && (PT & (PT - 1)) == 0, "power-of-two rows");
     // regions of one stage buffer (bytes)
     static constexpr int K0 = 0;
@@ -164,10 +165,12 @@ __device__ __forceinline__ void stage_chunk(int lw, lds_char* buf, const E* __re
             dma_tile_p<RPL, LT::PK>(buf + LT::K0, reinterpret_cast<const char*>(k + rowbase * D), seq_row, lane,
                                     part * RPL);
     } else {
+        constexpr int QS = LT::QUAD ? 1 : 0;          // the intra stage leaves that quadrant unwritten
         if (lw == 0)
-            dma_tile_p<C, LT::PT>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
+            dma_tile_p<C, LT::PT, 0, QS, C>(buf + LT::T0, reinterpret_cast<const char*>(Tm + tile * C * C), t_row, lane);
         else if (lw == 1)
-            dma_tile_p<C, LT::PT, 1>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row, lane);
+            dma_tile_p<C, LT::PT, 1, QS, C>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row,
+                                            lane);
         else if (lw == 2)
             dma_plain_p<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), seq_row, lane);
         else

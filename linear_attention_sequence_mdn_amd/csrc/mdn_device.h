@@ -69,6 +69,17 @@ struct TraitsF32 {
 //   fp32 (K = 4 per step ks): the single slot of group g is accumulator row
 //   16(ks/4) + 4g + ks%4, and perm is the identity.
 // ---------------------------------------------------------------------------
+// T and Aqk are lower triangular, so their upper-right C/2 x C/2 quadrant is
+// zero.  Where every matrix-core contraction step is at most C/2 columns wide
+// (bf16 at C = 64: steps of 32; fp32 at C >= 32: steps of 16), the products
+// that read T and Aqk (and T^T, Aqk^T in the backward) skip the steps that
+// fall in that quadrant, so the intra stage does not write it.
+template <typename Tr, int C>
+constexpr bool quad_unread()
+{
+    return std::is_same<Tr, TraitsBf16>::value ? C == 64 : C >= 32;
+}
+
 template <typename Tr> struct Slots;
 
 template <> struct Slots<TraitsBf16> {

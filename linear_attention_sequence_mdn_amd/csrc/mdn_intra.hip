@@ -31,7 +31,8 @@
 //      block forward substitution, T_ab = -T_aa sum_{c=b..a-1} A_ac T_cb, on
 //      the fp32 matrix cores, one wave per column block;
 //   5. T and Aqk leave through LDS tiles as full 16-byte stores (or, for the
-//      backward, T^T and Aqk^T).
+//      backward, T^T and Aqk^T), without the all-zero quadrant that no
+//      product reads (quad_unread).
 #include "mdn_device.h"
 #include "mdn_internal.h"
 #include "mdn_lds.h"
@@ -465,19 +466,23 @@ void mdn_intra_kernel(const typename Tr::elem* __restrict__ q,
 
     // ---- 5. T and Aqk -> workspace ------------------------------------------
     constexpr int NP = L::OUT / 16;
+    constexpr int EPS = 16 / L::ES;                  // elements per 16-byte piece
+    constexpr bool QS = quad_unread<Tr, C>();
     uint4* gT = reinterpret_cast<uint4*>(Tout + tile * C * C);
     uint4* gA = reinterpret_cast<uint4*>(Aqk + tile * C * C);
     if constexpr (!TRANS) {
         for (int p = tid; p < NP; p += 256) {
+            const int r = p / (C / EPS), c0 = (p % (C / EPS)) * EPS;
+            if (QS && r < C / 2 && c0 >= C / 2) continue;   // upper-right quadrant
             gT[p] = reinterpret_cast<const uint4*>(oT)[p];
             gA[p] = reinterpret_cast<const uint4*>(oAq)[p];
         }
     } else {
         // T^T and Aqk^T (the backward's A operands): piece p holds row c of
         // the transpose, columns r0 .. r0 + EPS - 1
-        constexpr int EPS = 16 / L::ES;
         for (int p = tid; p < NP; p += 256) {
             const int c = p / (C / EPS), r0 = (p % (C / EPS)) * EPS;
+            if (QS && c >= C / 2 && r0 < C / 2) continue;   // lower-left quadrant of the transpose
             union { uint4 u; E e[EPS]; } t, a;
 #pragma unroll
             for (int j = 0; j < EPS; ++j) {

@@ -70,7 +70,20 @@ template <int P, int KEY> struct LdsA<TraitsF32, P, KEY> {
 // and physical piece l%P, so its source offset is a per-lane constant plus a
 // per-instruction constant.  `rowoff(r)` gives the byte offset of global row
 // r relative to `base`.
-template <int R, int P, int KEY = 0, typename RowOff>
+//
+// QS leaves out the all-zero quadrant of a triangular tile of RT rows (its
+// LDS pieces keep whatever they held; no product reads them): 1 = the
+// upper-right quadrant (rows < RT/2, pieces >= P/2: T, Aqk), 2 = the
+// lower-left one (rows >= RT/2, pieces < P/2: T^T, Aqk^T).
+template <int QS, int RT, int P>
+__device__ __forceinline__ bool quad_piece(unsigned r, unsigned p)
+{
+    if constexpr (QS == 1) return r < (unsigned)RT / 2 && p >= (unsigned)P / 2;
+    else if constexpr (QS == 2) return r >= (unsigned)RT / 2 && p < (unsigned)P / 2;
+    else return false;
+}
+
+template <int R, int P, int KEY = 0, int QS = 0, int RT = 0, typename RowOff>
 __device__ __forceinline__ void dma_tile(uint32_t dst, const char* __restrict__ base, RowOff rowoff, int lane,
                                          int r0 = 0)
 {
@@ -84,7 +97,7 @@ __device__ __forceinline__ void dma_tile(uint32_t dst, const char* __restrict__ 
         const unsigned rl = i * RPI + lr;             // row within the copied range
         const unsigned r = (unsigned)r0 + rl;
         const unsigned p = lp ^ (unsigned)swz_key<P, KEY>((int)r);
-        if (R * P % 64 == 0 || rl < (unsigned)R)
+        if ((R * P % 64 == 0 || rl < (unsigned)R) && !quad_piece<QS, RT, P>(r, p))
             __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(uintptr_t)(d0 + i * 1024), 16, 0, 0);
     }
 }
@@ -97,7 +110,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 template <typename T>
 __device__ __forceinline__ lds_char* lds_ptr(T* p) { return (lds_char*)(__attribute__((address_space(3))) void*)p; }
 
-template <int R, int P, int KEY = 0, typename RowOff>
+template <int R, int P, int KEY = 0, int QS = 0, int RT = 0, typename RowOff>
 __device__ __forceinline__ void dma_tile_p(lds_char* dst, const char* __restrict__ base, RowOff rowoff, int lane,
                                            int r0 = 0)
 {
@@ -111,7 +124,7 @@ __device__ __forceinline__ void dma_tile_p(lds_char* dst, const char* __restrict
         const unsigned rl = i * RPI + lr;
         const unsigned r = (unsigned)r0 + rl;
         const unsigned p = lp ^ (unsigned)swz_key<P, KEY>((int)r);
-        if (R * P % 64 == 0 || rl < (unsigned)R)
+        if ((R * P % 64 == 0 || rl < (unsigned)R) && !quad_piece<QS, RT, P>(r, p))
             __builtin_amdgcn_global_load_lds(base + rowoff(r) + p * 16, (lds_void*)(d0 + i * 1024), 16, 0, 0);
     }
 }

@@ -22,18 +22,24 @@ def upstream(x, seed, with_states=True):
     return dO, dST, dMT
 
 
-def run_bwd(x, dO, dST, dMT, C=None):
-    """GPU forward (for vtilde), then the GPU backward; host fp64 dict."""
+def run_bwd(x, dO, dST, dMT, C=None, nan_workspace=False):
+    """GPU forward (for vtilde), then the GPU backward; host fp64 dict.
+    nan_workspace: the backward's workspace starts with every byte 0xFF."""
     import linear_attention_sequence_mdn_amd as mdn
     torch = torch_mod()
     C = x.C if C is None else C
+    kw = {}
+    if nan_workspace:
+        dt = mdn.MDN_BF16 if x.dtype == "bf16" else mdn.MDN_F32
+        n = mdn.chunk_bwd_workspace_bytes(x.B, x.H, x.T, x.dk, x.dv, C, dt)
+        kw["workspace"] = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
     dq, dk, dv = dev(x.q, x.dtype), dev(x.k, x.dtype), dev(x.v, x.dtype)
     gates = [dev(x.alpha), dev(x.mu), dev(x.beta), dev(x.eta)]
     S0 = None if x.S0 is None else dev(x.S0)
     M0 = None if x.M0 is None else dev(x.M0)
     _, _, _, Vt = mdn.chunk_fwd(dq, dk, dv, *gates, S0, M0, C=C)
     g = mdn.chunk_bwd(dq, dk, *gates, Vt, dev(dO, x.dtype), S0, M0,
-                      None if dST is None else dev(dST), None if dMT is None else dev(dMT), C=C)
+                      None if dST is None else dev(dST), None if dMT is None else dev(dMT), C=C, **kw)
     torch.cuda.synchronize()
     return {n: host(t) for n, t in g.items()}
 
@@ -64,6 +70,20 @@ def test_bwd_bf16_small(d, C, T):
     dO, dST, dMT = upstream(x, d + T)
     note(f"bwd bf16 d={d} C={C} T={T}")
     check(run_bwd(x, dO, dST, dMT), ref_bwd(x, dO, dST, dMT), TOL["bf16"], f"bwd bf16 d{d} C{C} T{T}")
+
+
+@pytest.mark.parametrize("dtype,d,C,T", [("bf16", 128, 64, 100), ("bf16", 64, 32, 70), ("f32", 64, 32, 64),
+                                         ("f32", 32, 64, 70)])
+def test_bwd_on_nan_workspace(dtype, d, C, T):
+    """The backward from a workspace whose every byte starts as 0xFF: every
+    gradient still matches the oracle, so nothing reads a workspace element
+    (the all-zero quadrant of T^T and Aqk^T included) that was not written."""
+    x = inputs.make_chunk_inputs(2, 2, T, d, C=C, dtype=dtype, seed=5 * d + C + T,
+                                 state_std=0.02 if dtype == "bf16" else 0.3)
+    dO, dST, dMT = upstream(x, d + C)
+    note(f"bwd nan workspace {dtype} d={d} C={C} T={T}")
+    check(run_bwd(x, dO, dST, dMT, nan_workspace=True), ref_bwd(x, dO, dST, dMT), TOL[dtype],
+          f"bwd nan-ws {dtype} d{d} C{C} T{T}")
 
 
 # bf16 at d = 16 or C = 16: the fp32 backward on widened copies
