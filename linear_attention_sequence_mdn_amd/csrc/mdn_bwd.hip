@@ -750,30 +750,39 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
                     XM[t][e] = mubarC * XM[t][e] - bC * XS[t][e];
                     XS[t][e] = abarC * XS[t][e];
                 }
+            auto dO_products = [&](int k0, int k1) __attribute__((always_inline)) {
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                float sa[NSL], sb[NSL];
-                SL::load_row(cf + MDN_COEF_ABAR * C, ks, g, sa);
-                SL::load_row(cf + MDN_COEF_B * C, ks, g, sb);
+                for (int ks = 0; ks < KSC; ++ks) {
+                    if (ks < k0 || ks >= k1) continue;
+                    float sa[NSL], sb[NSL];
+                    SL::load_row(cf + MDN_COEF_ABAR * C, ks, g, sa);
+                    SL::load_row(cf + MDN_COEF_B * C, ks, g, sb);
 #pragma unroll
-                for (int j = 0; j < NSL; ++j) {
-                    // the staged dO rows past the end repeat the last row: weight 0
-                    const bool in = SL::row(ks, g, j) < vm;
-                    sa[j] = in ? sa[j] : 0.f;
-                    sb[j] = in ? -sb[j] : 0.f;
+                    for (int j = 0; j < NSL; ++j) {
+                        // the staged dO rows past the end repeat the last row: weight 0
+                        const bool in = SL::row(ks, g, j) < vm;
+                        sa[j] = in ? sa[j] : 0.f;
+                        sb[j] = in ? -sb[j] : 0.f;
+                    }
+                    const frag dOa = FragScale<Tr>::apply(ob[ks], sa), dOb = FragScale<Tr>::apply(ob[ks], sb);
+#pragma unroll
+                    for (int t = 0; t < NDL; ++t) {
+                        const frag qT = TrOperand<Tr, LT::PK>::load(Ql, t + h * NDL, ks, lane);
+                        XS[t] = Tr::mma(qT, dOa, XS[t]);
+                        XM[t] = Tr::mma(qT, dOb, XM[t]);
+                    }
                 }
-                const frag dOa = FragScale<Tr>::apply(ob[ks], sa), dOb = FragScale<Tr>::apply(ob[ks], sb);
-#pragma unroll
-                for (int t = 0; t < NDL; ++t) {
-                    const frag qT = TrOperand<Tr, LT::PK>::load(Ql, t + h * NDL, ks, lane);
-                    XS[t] = Tr::mma(qT, dOa, XS[t]);
-                    XM[t] = Tr::mma(qT, dOb, XM[t]);
-                }
-            }
+            };
+            // wave 1 takes all its products with dO before it waits for dW;
+            // wave 0 the first half of the contraction steps before it waits
+            // for the partner's part, the rest after it has handed dW over, so
+            // that dW reaches wave 1 sooner (the accumulation order is the same)
+            constexpr int DOS = KSC / 2;
             // dvt = P_0 + P_1 (with Aqk^T dO) and dW = T^T dvt on wave 0, which
             // hands dW to wave 1 and dW (the chunk's dV rows) to the loaders
             floatx4 dW[NCT];
             if (h == 0) {
+                dO_products(0, DOS);
                 pair_wait(&xflag[2 * ct], (int)it + 1);
                 floatx4 dV[NCT];
 #pragma unroll
@@ -793,7 +802,9 @@ void mdn_bwd_carry_kernel(const typename Tr::elem* __restrict__ q, const typenam
                 for (int tc = 0; tc < NCT; ++tc) xt[tc * 64] = dW[tc];
                 if (lane == 0) pair_release(&xflag[2 * ct + 1], (int)it + 1);
                 HandTile<Tr, C>::write(dW, reinterpret_cast<E*>(hand + 2 * LT::SLB), lane);
+                dO_products(DOS, KSC);
             } else {
+                dO_products(0, KSC);
                 pair_wait(&xflag[2 * ct + 1], (int)it + 1);
 #pragma unroll
                 for (int tc = 0; tc < NCT; ++tc) dW[tc] = xt[tc * 64];
