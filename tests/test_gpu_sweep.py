@@ -114,3 +114,22 @@ def test_grid_beyond_one_wave_of_workgroups(dtype, d, C, T, B, H):
     note("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
         assert e <= TOL[dtype], (n, e)
+
+
+@pytest.mark.parametrize("dtype,d,C,T,B,H", [("bf16", 128, 64, 130, 2, 80), ("bf16", 64, 64, 70, 3, 55),
+                                             ("f32", 64, 32, 40, 2, 37)])
+def test_bwd_grid_beyond_one_wave_of_workgroups(dtype, d, C, T, B, H):
+    """The backward with more heads than the device holds carry workgroups at
+    once (one per compute unit at d = 128), so they run in several rounds;
+    B*H both a multiple of 8 (the XCD-aware head map) and not.  Every gradient
+    is compared as a whole tensor."""
+    x = inputs.make_chunk_inputs(B, H, T, d, C=C, dtype=dtype, seed=900 + d + H,
+                                 state_std=0.02 if dtype == "bf16" else 0.3)
+    dO, dST, dMT = upstream(x, 70 + H)
+    note(f"bwd {dtype} d={d} C={C} T={T} B={B} H={H}: {B * H} heads")
+    got = run_bwd(x, dO, dST, dMT)
+    ref = ref_bwd(x, dO, dST, dMT)
+    errs = {n: rel_err(got[n], ref[n]) for n in GRADS}
+    note("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL[dtype], (n, e)
