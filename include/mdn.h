@@ -152,6 +152,43 @@ int mdn_chunk_fwd_fused(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, 
                         const float* S0, const float* M0,
                         void* O, float* S_T, float* M_T, void* Vtilde, void* stream);
 
+/* Chunkwise forward with each sequence cut into nseg segments that run side
+ * by side, for batches with few heads and long sequences, whose single
+ * serial pass over the chunks leaves most compute units idle.  The result
+ * is that of mdn_chunk_fwd (up to rounding), on the same arguments plus
+ * nseg; supported sizes are the natively compiled ones (fp32: dk = dv in
+ * {16, 32, 64, 128}, C in {16, 32, 64}; bf16: dk = dv in {32, 64, 128},
+ * C in {32, 64}); others, and nseg outside [2, MDN_SPLIT_MAX_SEGMENTS],
+ * return MDN_ERR_UNSUPPORTED.
+ *
+ * Why it is exact: each chunk's update of the state pair [S; M] (summary,
+ * steps 2 and 4: S' = abar S - b M + K^T Diag(gS) vtilde, M' = mubar M -
+ * K^T Diag(gM) vtilde, with vtilde = T (V - Diag(abar) K S + Diag(alpha
+ * b_prev) K M)) is affine in [S; M], with the same 2dk x 2dk linear part
+ * for every state column.  A run of chunks therefore maps its start state
+ * to its end state by one linear map Phi plus an offset.
+ *   - Segment p holds chunks [p NT / nseg, (p + 1) NT / nseg), NT = ceil(T/C).
+ *   - Pass 1: segment 0 from S0, M0 (its O and Vtilde are final); for each
+ *     middle segment 1 .. nseg-2, the data from a zero state (the offset)
+ *     and, with V = 0, the states S = I, M = 0 and S = 0, M = I (the
+ *     columns of Phi).
+ *   - Combine: the start state of segment p is Phi_{p-1} [S; M]_{p-1} +
+ *     offset_{p-1}, in fp32, in order of p.
+ *   - Pass 2: segments 1 .. nseg-1 from their start states.
+ * The extra arithmetic is about 3x the state work of the middle segments.
+ *   workspace   at least mdn_chunk_fwd_split_workspace_bytes(); the
+ *               mdn_chunk_fwd layout, then the state slots (fp32).
+ * Errors as mdn_chunk_fwd. */
+#define MDN_SPLIT_MAX_SEGMENTS 64
+size_t mdn_chunk_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t T,
+                                           int dk, int dv, int C, int dtype, int nseg);
+int mdn_chunk_fwd_split(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype, int nseg,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha, const float* mu, const float* beta, const float* eta,
+                        const float* S0, const float* M0,
+                        void* O, float* S_T, float* M_T, void* Vtilde,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* mdn_chunk_fwd for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, semantics and errors as mdn_chunk_fwd, without the
@@ -351,7 +388,7 @@ const char* mdn_status_string(int status);
 /* ABI revision of this header (incremented on any signature change). */
 int mdn_abi_version(void);
 
-#define MDN_ABI_VERSION 7
+#define MDN_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

@@ -72,6 +72,10 @@ def lib():
         L.mdn_chunk_fwd_varlen.restype = i32
         L.mdn_chunk_fwd_noalloc.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp]
         L.mdn_chunk_fwd_noalloc.restype = i32
+        L.mdn_chunk_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32]
+        L.mdn_chunk_fwd_split_workspace_bytes.restype = sz
+        L.mdn_chunk_fwd_split.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32] + [vp] * 13 + [vp, sz, vp]
+        L.mdn_chunk_fwd_split.restype = i32
         L.mdn_chunk_fwd_fused.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 13 + [vp]
         L.mdn_chunk_fwd_fused.restype = i32
         L.mdn_chunk_intra.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 6 + [vp, sz, vp]
@@ -233,6 +237,23 @@ class ChunkCall:
                "mdn_chunk_inter")
         return self.outputs
 
+    def split(self, nseg, stream=None, workspace=None):
+        """``mdn_chunk_fwd_split`` on the same arguments, each sequence cut
+        into ``nseg`` segments; its workspace is ``workspace`` or one
+        allocated on first use for that ``nseg`` and kept."""
+        torch = _torch()
+        B, H, T, dk, dv, C, dt = self.sizes
+        need = chunk_fwd_split_workspace_bytes(B, H, T, dk, dv, C, dt, nseg)
+        if workspace is None:
+            cache = self.__dict__.setdefault("_split_ws", {})
+            if nseg not in cache:
+                cache[nseg] = torch.empty(max(need, 1), dtype=torch.uint8, device=self.outputs[0].device)
+            workspace = cache[nseg]
+        owned = list(self._owned) + [workspace]
+        _check(lib().mdn_chunk_fwd_split(B, H, T, dk, dv, C, dt, int(nseg), *self._ptrs, _ptr(workspace),
+                                         workspace.numel(), _stream(stream, owned)), "mdn_chunk_fwd_split")
+        return self.outputs
+
 
 def chunk_fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, *,
               out=None, S_T=None, M_T=None, workspace=None, stream=None):
@@ -247,6 +268,24 @@ def chunk_fwd(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, *,
     call = ChunkCall(q, k, v, alpha, mu, beta, eta, S0, M0, C, out=out, S_T=S_T, M_T=M_T,
                      workspace=workspace)
     return call.run(stream)
+
+
+def chunk_fwd_split_workspace_bytes(B, H, T, dk, dv, C, dtype, nseg) -> int:
+    n = lib().mdn_chunk_fwd_split_workspace_bytes(B, H, T, dk, dv, C, dtype, nseg)
+    if n == ctypes.c_size_t(-1).value:
+        raise MdnError(3, "mdn_chunk_fwd_split_workspace_bytes")
+    return int(n)
+
+
+def chunk_fwd_split(q, k, v, alpha, mu, beta, eta, S0=None, M0=None, C=64, nseg=3, *,
+                    out=None, S_T=None, M_T=None, workspace=None, stream=None):
+    """``mdn_chunk_fwd_split``: the chunk forward with each sequence cut into
+    ``nseg`` segments that run side by side (for few heads and long
+    sequences); arguments and results as :func:`chunk_fwd`, ``workspace`` a
+    uint8 tensor of at least ``chunk_fwd_split_workspace_bytes`` bytes."""
+    call = ChunkCall(q, k, v, alpha, mu, beta, eta, S0, M0, C, out=out, S_T=S_T, M_T=M_T,
+                     workspace=_NO_WORKSPACE)
+    return call.split(nseg, stream, workspace)
 
 
 NOALLOC_SCRATCH_BYTES = 80 << 20

@@ -150,6 +150,34 @@ size_t fwd_workspace(const ChunkSizes& s, int dk, int dv, int C, int dtype) {
     return dims_widened_chunk(dtype, dk, dv, C) ? wide_fwd_sections(s, C).total : workspace_of(s, C, dtype);
 }
 
+// Sequence split into P segments: after the forward's sections, two arrays
+// (S, then M) of D x D fp32 state slots, BH (1 + 3 (P - 2)) written by the
+// first pass and BH (P - 2) by the combine step: the bytes of one array in
+// *out; false when the sizes do not fit.
+bool split_state_bytes(const ChunkSizes& s, int dk, int dv, int P, size_t* out) {
+    int64_t slots, elems;
+    if (!mul_ok(s.BH, (int64_t)(1 + 4 * (P - 2)), &slots) || !mul_ok(slots, (int64_t)dk * dv, &elems) ||
+        elems > kMaxElems)
+        return false;
+    *out = align256((size_t)elems * sizeof(float));
+    return true;
+}
+
+// Segments mdn_chunk_fwd cuts each sequence into by itself (0: none).  The
+// split pays where one pass leaves compute units idle and its first pass
+// fills them: measured on the long-context shape (16 heads of 16384
+// tokens, bf16, d = 128, C = 64; 0.39 against 0.43 ms) with three segments,
+// whose first pass is 4 two-tile column slabs of 4 units per head, i.e.
+// 16 workgroups per head.  Taken for that family only, when those
+// workgroups fill more than half of the compute units and at most all of
+// them, and the segments hold at least 16 chunks each.
+int auto_segments(const ChunkSizes& s, int dk, int dv, int C, int dtype) {
+    if (s.nseq >= 0 || dtype != MDN_BF16 || dk != 128 || dv != 128 || C != 64 || s.NT < 48) return 0;
+    const int64_t cus = mdn::device_compute_units();
+    const int64_t pass1 = s.BH * 16;
+    return (pass1 <= cus && 2 * pass1 > cus) ? 3 : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,6 +206,9 @@ size_t mdn_chunk_fwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int dk, in
     ChunkSizes s;
     if (chunk_sizes(B, H, T, dk, dv, C, &s) != MDN_OK) return (size_t)-1;
     if (!dims_supported_chunk(dtype, dk, dv, C)) return (size_t)-1;
+    const int P = auto_segments(s, dk, dv, C, dtype);
+    size_t st;
+    if (P > 0 && split_state_bytes(s, dk, dv, P, &st)) return workspace_of(s, C, dtype) + 2 * st;
     return fwd_workspace(s, dk, dv, C, dtype);
 }
 
@@ -244,7 +275,8 @@ static int chunk_prepare(int stage, const ChunkSizes& s, int64_t T, int dk, int 
                          const float* S0, const float* M0,
                          void* O, float* S_T, float* M_T, void* Vtilde,
                          void* workspace, size_t workspace_bytes, void* stream,
-                         mdn::ChunkArgs* a, bool* empty, bool wide = false, bool no_workspace = false)
+                         mdn::ChunkArgs* a, bool* empty, bool wide = false, bool no_workspace = false,
+                         size_t extra = 0)
 {
     if (wide ? !dims_widened_chunk(dtype, dk, dv, C) : !dims_native_chunk(dtype, dk, dv, C))
         return MDN_ERR_UNSUPPORTED;
@@ -260,7 +292,7 @@ static int chunk_prepare(int stage, const ChunkSizes& s, int64_t T, int dk, int 
     if (inter && (!S_T || !M_T)) return MDN_ERR_NULL_ARG;
     if (seq && (!q || !k || !alpha || !mu || !beta || !eta)) return MDN_ERR_NULL_ARG;
     if (seq && inter && (!v || !O || !Vtilde)) return MDN_ERR_NULL_ARG;
-    const size_t need = no_workspace ? 0 : wide ? wide_fwd_sections(s, C).total : workspace_of(s, C, dtype);
+    const size_t need = (no_workspace ? 0 : wide ? wide_fwd_sections(s, C).total : workspace_of(s, C, dtype)) + extra;
     if (need > 0 && (!workspace || workspace_bytes < need)) return MDN_ERR_WORKSPACE;
 
     const void* all[] = {q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde, workspace};
@@ -367,18 +399,53 @@ static int fwd_widened(const ChunkSizes& s, int64_t T, int dk, int dv, int C, co
     return hip_status(mdn::launch_convert(Vt32, MDN_F32, Vtilde, s.v_elems, stream));
 }
 
-int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
-                  const void* q, const void* k, const void* v,
-                  const float* alpha, const float* mu, const float* beta, const float* eta,
-                  const float* S0, const float* M0,
-                  void* O, float* S_T, float* M_T, void* Vtilde,
-                  void* workspace, size_t workspace_bytes, void* stream)
+// The split forward on validated sizes (native dims, 2 <= nseg <= max).
+static int fwd_split(const ChunkSizes& s, int64_t T, int dk, int dv, int C, int dtype, int nseg,
+                     const void* q, const void* k, const void* v,
+                     const float* alpha, const float* mu, const float* beta, const float* eta,
+                     const float* S0, const float* M0,
+                     void* O, float* S_T, float* M_T, void* Vtilde,
+                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    int64_t units;
+    if (!mul_ok(s.BH, (int64_t)(1 + 3 * (nseg - 2)), &units) || units > INT32_MAX / 8) return MDN_ERR_BAD_SHAPE;
+    size_t stb;
+    if (!split_state_bytes(s, dk, dv, nseg, &stb)) return MDN_ERR_BAD_SHAPE;
+    mdn::ChunkArgs a;
+    bool empty = false;
+    int st = chunk_prepare(3, s, T, dk, dv, C, dtype, nullptr, q, k, v, alpha, mu, beta, eta, S0, M0,
+                           O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty, false, false, 2 * stb);
+    if (st != MDN_OK || empty) return st;
+    float* segS = (float*)((char*)workspace + workspace_of(s, C, dtype));
+    float* segM = (float*)((char*)segS + stb);
+    if (T > 0) {
+        st = hip_status(mdn::launch_chunk_intra(a));
+        if (st != MDN_OK) return st;
+    }
+    return hip_status(mdn::launch_chunk_inter_split(a, nseg, segS, segM));
+}
+
+// mdn_chunk_fwd; with allow_split it takes the sequence split where
+// auto_segments chooses it and the workspace holds the split's state slots.
+static int chunk_fwd_impl(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                          const void* q, const void* k, const void* v,
+                          const float* alpha, const float* mu, const float* beta, const float* eta,
+                          const float* S0, const float* M0,
+                          void* O, float* S_T, float* M_T, void* Vtilde,
+                          void* workspace, size_t workspace_bytes, void* stream, bool allow_split)
 {
     mdn::ChunkArgs a;
     bool empty = false;
     ChunkSizes s;
     int st = chunk_sizes(B, H, T, dk, dv, C, &s);
     if (st != MDN_OK) return st;
+    if (allow_split && dims_native_chunk(dtype, dk, dv, C)) {
+        const int P = auto_segments(s, dk, dv, C, dtype);
+        size_t stb;
+        if (P > 0 && split_state_bytes(s, dk, dv, P, &stb) && workspace_bytes >= workspace_of(s, C, dtype) + 2 * stb)
+            return fwd_split(s, T, dk, dv, C, dtype, P, q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde,
+                             workspace, workspace_bytes, stream);
+    }
     if (dims_widened_chunk(dtype, dk, dv, C))
         return fwd_widened(s, T, dk, dv, C, nullptr, q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde,
                            workspace, workspace_bytes, stream);
@@ -386,6 +453,46 @@ int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dt
                        O, S_T, M_T, Vtilde, workspace, workspace_bytes, stream, &a, &empty);
     if (st != MDN_OK || empty) return st;
     return fwd_launch(a, T);
+}
+
+int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                  const void* q, const void* k, const void* v,
+                  const float* alpha, const float* mu, const float* beta, const float* eta,
+                  const float* S0, const float* M0,
+                  void* O, float* S_T, float* M_T, void* Vtilde,
+                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    return chunk_fwd_impl(B, H, T, dk, dv, C, dtype, q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde,
+                          workspace, workspace_bytes, stream, true);
+}
+
+size_t mdn_chunk_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,
+                                           int nseg)
+{
+    ChunkSizes s;
+    if (chunk_sizes(B, H, T, dk, dv, C, &s) != MDN_OK) return (size_t)-1;
+    if (!dims_native_chunk(dtype, dk, dv, C) || nseg < 2 || nseg > MDN_SPLIT_MAX_SEGMENTS) return (size_t)-1;
+    size_t st;
+    if (!split_state_bytes(s, dk, dv, nseg, &st)) return (size_t)-1;
+    return workspace_of(s, C, dtype) + 2 * st;
+}
+
+// The forward with each sequence cut into nseg segments that run side by
+// side: pass 1, the combine step, pass 2 (launch_chunk_inter_split).
+int mdn_chunk_fwd_split(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype, int nseg,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha, const float* mu, const float* beta, const float* eta,
+                        const float* S0, const float* M0,
+                        void* O, float* S_T, float* M_T, void* Vtilde,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    ChunkSizes s;
+    int st = chunk_sizes(B, H, T, dk, dv, C, &s);
+    if (st != MDN_OK) return st;
+    if (!dims_native_chunk(dtype, dk, dv, C) || nseg < 2 || nseg > MDN_SPLIT_MAX_SEGMENTS)
+        return MDN_ERR_UNSUPPORTED;
+    return fwd_split(s, T, dk, dv, C, dtype, nseg, q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde,
+                     workspace, workspace_bytes, stream);
 }
 
 // The whole forward in one kernel (no workspace): bf16, C = 64, dk = dv in
@@ -462,8 +569,8 @@ int mdn_chunk_fwd_noalloc(int64_t B, int64_t H, int64_t T, int dk, int dv, int C
     }
     // the kernels write every byte of the workspace they read, so nothing
     // left by an earlier call needs clearing
-    return mdn_chunk_fwd(B, H, T, dk, dv, C, dtype, q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde,
-                         ws, ws ? (size_t)MDN_NOALLOC_SCRATCH_BYTES : 0, stream);
+    return chunk_fwd_impl(B, H, T, dk, dv, C, dtype, q, k, v, alpha, mu, beta, eta, S0, M0, O, S_T, M_T, Vtilde,
+                          ws, ws ? (size_t)MDN_NOALLOC_SCRATCH_BYTES : 0, stream, false);
 }
 
 int mdn_chunk_intra(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,

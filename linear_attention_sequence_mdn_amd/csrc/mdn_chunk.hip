@@ -141,10 +141,12 @@ struct InterPick {
 // the K and Q rows, split by rows over the NLD loaders; HALF 1: T, Aqk, the
 // V slab and the coefficient rows.  A single wave sustains only a fraction
 // of a CU's L2 bandwidth, so the copies are spread over all loaders.  Rows
-// past `valid` (ragged last chunk) repeat the last valid row.
+// past `valid` (ragged last chunk) repeat the last valid row.  `vr` points
+// at the chunk's first V row; when it is NULL the V slab is not copied (the
+// buffer's V region then holds zeros, written once at the start).
 template <typename LT, typename E, int D, int C, int NLD, int HALF>
 __device__ __forceinline__ void stage_chunk(int lw, lds_char* buf, const E* __restrict__ k, const E* __restrict__ q,
-                                            const E* __restrict__ v, const E* __restrict__ Tm,
+                                            const E* __restrict__ vr, const E* __restrict__ Tm,
                                             const E* __restrict__ Aqk, const float* __restrict__ coef,
                                             size_t rowbase, int valid, size_t tile, int col0, int lane)
 {
@@ -171,8 +173,9 @@ __device__ __forceinline__ void stage_chunk(int lw, lds_char* buf, const E* __re
         else if (lw == 1)
             dma_tile_p<C, LT::PT, 1, QS, C>(buf + LT::A0, reinterpret_cast<const char*>(Aqk + tile * C * C), t_row,
                                             lane);
-        else if (lw == 2)
-            dma_plain_p<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(v + rowbase * D + col0), seq_row, lane);
+        else if (lw == 2) {
+            if (vr) dma_plain_p<C, LT::PV>(buf + LT::V0, reinterpret_cast<const char*>(vr + col0), seq_row, lane);
+        }
         else
             dma_plain_p<1, LT::PC>(buf + LT::CF0, reinterpret_cast<const char*>(coef + tile * MDN_COEF_ROWS * C),
                                    cf_row, lane);
@@ -208,7 +211,7 @@ __device__ __forceinline__ void copy_out(const char* tile, E* __restrict__ dst, 
     }
 }
 
-template <typename Tr, int D, int C, int NCOL, int RS, int NBUF, int NLD>
+template <typename Tr, int D, int C, int NCOL, int RS, int NBUF, int NLD, bool SEG>
 __global__ __launch_bounds__(64 * (NCOL * RS + NLD))
 void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                       const typename Tr::elem* __restrict__ k,
@@ -221,7 +224,7 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
                       float* __restrict__ ST, float* __restrict__ MT,
                       typename Tr::elem* __restrict__ Vt,
                       int64_t T, int64_t NT, int BH, const int32_t* __restrict__ cu,
-                      const int32_t* __restrict__ perm, int H)
+                      const int32_t* __restrict__ perm, int H, InterSeg seg)
 {
     using E = typename Tr::elem;
     using SL = Slots<Tr>;
@@ -247,8 +250,8 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, nn = lane & 15;
-    const InterUnit unit = inter_unit(blockIdx.x, SLABS, BH, T, NT, C, cu, perm, H);
-    const int bh = unit.bh, slab = unit.slab;
+    const InterUnit unit = inter_unit<SEG>(blockIdx.x, SLABS, BH, T, NT, C, cu, perm, H, D, seg);
+    const int slab = unit.slab;
     const int64_t row0 = unit.row0, tile0 = unit.tile0, len = unit.len;
     const int col0 = slab * OW;
     const int64_t NTu = (len + C - 1) / C;
@@ -282,10 +285,12 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
             const size_t tile = (size_t)(tile0 + m);
             const size_t rb = (size_t)(row0 + m * C);
             const int vm = valid_of(m);
-            if (half == 0) stage_chunk<LT, E, D, C, NLD, 0>(lw, buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
-            else stage_chunk<LT, E, D, C, NLD, 1>(lw, buf, k, q, v, Tm, Aqk, coef, rb, vm, tile, col0, lane);
+            const E* vr = (SEG && unit.vzero) ? nullptr : v + rb * D;
+            if (half == 0) stage_chunk<LT, E, D, C, NLD, 0>(lw, buf, k, q, vr, Tm, Aqk, coef, rb, vm, tile, col0, lane);
+            else stage_chunk<LT, E, D, C, NLD, 1>(lw, buf, k, q, vr, Tm, Aqk, coef, rb, vm, tile, col0, lane);
         };
         auto copy_outs = [&](int64_t m) __attribute__((always_inline)) {
+            if (SEG && !unit.ostore) return;
             if (lw == 2)
                 copy_out<LT, E, D, C>(reinterpret_cast<const char*>(oo), O + (size_t)(row0 + m * C) * D, valid_of(m), col0, lane);
             else if (lw == 3)
@@ -344,6 +349,13 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
         };
         lds_char* const aA = lds_ptr(stA);
         lds_char* const aB = lds_ptr(stB);
+        if (SEG && lw == 2 && unit.vzero) {                    // ordered before any read by the first chunk barrier
+            constexpr int NV = C * LT::PV;              // 16-byte pieces of one V region
+            for (int i = lane; i < NV; i += 64) {
+                reinterpret_cast<uint4*>(stA + LT::V0)[i] = uint4{0u, 0u, 0u, 0u};
+                if constexpr (NBUF == 2) reinterpret_cast<uint4*>(stB + LT::V0)[i] = uint4{0u, 0u, 0u, 0u};
+            }
+        }
         if constexpr (NBUF == 2) {
             if (NTu > 0) {
                 issue(aA, 0, 0);
@@ -407,16 +419,31 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     const int td0 = h * NDH, ks0 = h * KSH;           // first state tile / contraction step owned
 
     // the wave's rows of S and M (fp32 accumulators; tile t holds state rows perm(16 (td0 + t) + 4g + e))
-    const size_t sbase = (size_t)bh * D * D;
+    // (split units: start state at unit.sin, or zero, or an identity block)
+    const size_t sbase = SEG ? 0 : (size_t)unit.bh * D * D;
     floatx4 XS[NDH], XM[NDH];
+    if constexpr (SEG) {
+        const float* S0u = (S0 && unit.sin >= 0) ? S0 + unit.sin : nullptr;
+        const float* M0u = (M0 && unit.sin >= 0) ? M0 + unit.sin : nullptr;
 #pragma unroll
-    for (int t = 0; t < NDH; ++t)
+        for (int t = 0; t < NDH; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const size_t off = sbase + (size_t)SL::perm(16 * (td0 + t) + 4 * g + e) * D + col;
-            XS[t][e] = S0 ? S0[off] : 0.f;
-            XM[t][e] = M0 ? M0[off] : 0.f;
-        }
+            for (int e = 0; e < 4; ++e) {
+                const int row = SL::perm(16 * (td0 + t) + 4 * g + e);
+                const size_t off = (size_t)row * D + col;
+                XS[t][e] = S0u ? S0u[off] : (unit.ident == 1 && row == col ? 1.f : 0.f);
+                XM[t][e] = M0u ? M0u[off] : (unit.ident == 2 && row == col ? 1.f : 0.f);
+            }
+    } else {
+#pragma unroll
+        for (int t = 0; t < NDH; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const size_t off = sbase + (size_t)SL::perm(16 * (td0 + t) + 4 * g + e) * D + col;
+                XS[t][e] = S0 ? S0[off] : 0.f;
+                XM[t][e] = M0 ? M0[off] : 0.f;
+            }
+    }
     int64_t spar = 0;                                 // parity of the chunk whose start state is stored next
     const int smo = ((ct * RS + h) * 2) * KSH * 64 + lane;
     // chunk-start state operands, for P and for the output waves; stored
@@ -585,14 +612,21 @@ void mdn_inter_kernel(const typename Tr::elem* __restrict__ q,
     lds_barrier();                                      // E1
     lds_barrier();                                      // E2
 
+    // (the identity replicas of the split store theirs transposed, [col][row],
+    // the layout the combine step reads them in)
+    if (!SEG || unit.sout >= 0) {
+        const size_t obase = SEG ? (size_t)unit.sout : sbase;
+        const bool tr = SEG && unit.ident != 0;
 #pragma unroll
-    for (int t = 0; t < NDH; ++t)
+        for (int t = 0; t < NDH; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const size_t off = sbase + (size_t)SL::perm(16 * (td0 + t) + 4 * g + e) * D + col;
-            ST[off] = XS[t][e];
-            MT[off] = XM[t][e];
-        }
+            for (int e = 0; e < 4; ++e) {
+                const size_t row = (size_t)SL::perm(16 * (td0 + t) + 4 * g + e);
+                const size_t off = obase + (tr ? (size_t)col * D + row : row * D + col);
+                ST[off] = XS[t][e];
+                MT[off] = XM[t][e];
+            }
+    }
     };
     if constexpr (RS == 1) {
         chain(std::integral_constant<int, 0>{});
@@ -614,21 +648,37 @@ static int device_cus()
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
     return n;
 }
+int device_compute_units() { return device_cus(); }
+
+// One launch of the inter stage.  `units` is the number of state units the
+// grid covers: heads of a [B, H, T] batch, (sequence, head) pairs of a packed
+// batch, or the units of one pass of the sequence split (seg.P > 0), whose
+// start and end states are read from S0/M0 and written to ST/MT at the
+// offsets the unit map gives.
+struct InterLaunch {
+    int64_t units;
+    InterSeg seg;
+    const float *S0, *M0;
+    float *ST, *MT;
+};
 
 template <typename Tr, int D, int C, int NCOL, int RS>
-static hipError_t launch_inter_cols(const ChunkArgs& a)
+static hipError_t launch_inter_cols(const ChunkArgs& a, const InterLaunch& l)
 {
     using E = typename Tr::elem;
     using P = InterPick<Tr, D, C>;
     constexpr int NLD = 4;
     constexpr int NBUF = InterLayout<Tr, D, C, NCOL, RS, 2>::TOTAL <= P::LIMIT ? 2 : 1;
     static_assert(InterLayout<Tr, D, C, NCOL, RS, NBUF>::TOTAL <= P::LIMIT, "LDS");
-    const int64_t units = a.cu ? a.BH * a.nseq : a.BH;   // (sequence, head) pairs of a packed batch
-    const int64_t grid = units * (D / (16 * NCOL));
-    hipLaunchKernelGGL((mdn_inter_kernel<Tr, D, C, NCOL, RS, NBUF, NLD>), dim3((unsigned)grid), dim3(64 * (NCOL * RS + NLD)),
-                       0, (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v,
-                       (const E*)a.Tmat, (const E*)a.Aqk, a.coef, a.S0, a.M0,
-                       (E*)a.O, a.ST, a.MT, (E*)a.Vt, a.T, a.NT, (int)units, a.cu, a.perm, (int)a.BH);
+    const int64_t grid = l.units * (D / (16 * NCOL));
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * (NCOL * RS + NLD)), 0, (hipStream_t)a.stream,
+                           (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.Tmat, (const E*)a.Aqk, a.coef,
+                           l.S0, l.M0, (E*)a.O, l.ST, l.MT, (E*)a.Vt, a.T, a.NT, (int)l.units, a.cu, a.perm,
+                           (int)a.BH, l.seg);
+    };
+    if (l.seg.P > 0) go(mdn_inter_kernel<Tr, D, C, NCOL, RS, NBUF, NLD, true>);
+    else go(mdn_inter_kernel<Tr, D, C, NCOL, RS, NBUF, NLD, false>);
     return hipGetLastError();
 }
 
@@ -639,43 +689,42 @@ static hipError_t launch_inter_cols(const ChunkArgs& a)
 // chain that bounds such a launch.  The price is reading K, Q, T and Aqk
 // once more per head and the partial-product exchange of the row split.
 template <typename Tr, int D, int C>
-static hipError_t launch_inter_nw(const ChunkArgs& a)
+static hipError_t launch_inter_nw(const ChunkArgs& a, const InterLaunch& l)
 {
     using P = InterPick<Tr, D, C>;
     if constexpr (P::NCOL == 2 && P::RS == 1) {
-        const int64_t units = a.cu ? a.BH * a.nseq : a.BH;
-        if (2 * units * (D / 32) <= device_cus()) return launch_inter_cols<Tr, D, C, 1, (D >= 64 ? 2 : 1)>(a);
+        if (2 * l.units * (D / 32) <= device_cus()) return launch_inter_cols<Tr, D, C, 1, (D >= 64 ? 2 : 1)>(a, l);
     }
-    return launch_inter_cols<Tr, D, C, P::NCOL, P::RS>(a);
+    return launch_inter_cols<Tr, D, C, P::NCOL, P::RS>(a, l);
 }
 
 template <typename Tr>
-static hipError_t inter_dispatch(const ChunkArgs& a)
+static hipError_t inter_dispatch(const ChunkArgs& a, const InterLaunch& l)
 {
     if constexpr (std::is_same<Tr, TraitsBf16>::value) {
         switch (a.dk * 1000 + a.C) {
-        case 32032: return launch_inter_nw<Tr, 32, 32>(a);
-        case 32064: return launch_inter_nw<Tr, 32, 64>(a);
-        case 64032: return launch_inter_nw<Tr, 64, 32>(a);
-        case 64064: return launch_inter_nw<Tr, 64, 64>(a);
-        case 128032: return launch_inter_nw<Tr, 128, 32>(a);
-        case 128064: return launch_inter_nw<Tr, 128, 64>(a);
+        case 32032: return launch_inter_nw<Tr, 32, 32>(a, l);
+        case 32064: return launch_inter_nw<Tr, 32, 64>(a, l);
+        case 64032: return launch_inter_nw<Tr, 64, 32>(a, l);
+        case 64064: return launch_inter_nw<Tr, 64, 64>(a, l);
+        case 128032: return launch_inter_nw<Tr, 128, 32>(a, l);
+        case 128064: return launch_inter_nw<Tr, 128, 64>(a, l);
         default: return hipErrorInvalidValue;
         }
     } else {
         switch (a.dk * 1000 + a.C) {
-        case 16016: return launch_inter_nw<Tr, 16, 16>(a);
-        case 16032: return launch_inter_nw<Tr, 16, 32>(a);
-        case 16064: return launch_inter_nw<Tr, 16, 64>(a);
-        case 32016: return launch_inter_nw<Tr, 32, 16>(a);
-        case 32032: return launch_inter_nw<Tr, 32, 32>(a);
-        case 32064: return launch_inter_nw<Tr, 32, 64>(a);
-        case 64016: return launch_inter_nw<Tr, 64, 16>(a);
-        case 64032: return launch_inter_nw<Tr, 64, 32>(a);
-        case 64064: return launch_inter_nw<Tr, 64, 64>(a);
-        case 128016: return launch_inter_nw<Tr, 128, 16>(a);
-        case 128032: return launch_inter_nw<Tr, 128, 32>(a);
-        case 128064: return launch_inter_nw<Tr, 128, 64>(a);
+        case 16016: return launch_inter_nw<Tr, 16, 16>(a, l);
+        case 16032: return launch_inter_nw<Tr, 16, 32>(a, l);
+        case 16064: return launch_inter_nw<Tr, 16, 64>(a, l);
+        case 32016: return launch_inter_nw<Tr, 32, 16>(a, l);
+        case 32032: return launch_inter_nw<Tr, 32, 32>(a, l);
+        case 32064: return launch_inter_nw<Tr, 32, 64>(a, l);
+        case 64016: return launch_inter_nw<Tr, 64, 16>(a, l);
+        case 64032: return launch_inter_nw<Tr, 64, 32>(a, l);
+        case 64064: return launch_inter_nw<Tr, 64, 64>(a, l);
+        case 128016: return launch_inter_nw<Tr, 128, 16>(a, l);
+        case 128032: return launch_inter_nw<Tr, 128, 32>(a, l);
+        case 128064: return launch_inter_nw<Tr, 128, 64>(a, l);
         default: return hipErrorInvalidValue;
         }
     }
@@ -684,7 +733,120 @@ static hipError_t inter_dispatch(const ChunkArgs& a)
 hipError_t launch_chunk_inter(const ChunkArgs& a)
 {
     if (a.BH == 0 || (a.cu && a.nseq == 0)) return hipSuccess;
-    return a.dtype == MDN_BF16 ? inter_dispatch<TraitsBf16>(a) : inter_dispatch<TraitsF32>(a);
+    const InterLaunch l{a.cu ? a.BH * a.nseq : a.BH, InterSeg{0, 0}, a.S0, a.M0, a.ST, a.MT};
+    return a.dtype == MDN_BF16 ? inter_dispatch<TraitsBf16>(a, l) : inter_dispatch<TraitsF32>(a, l);
+}
+
+// ---------------------------------------------------------------------------
+// Sequence split: the combine step between the two passes.  Per sequence s
+// and middle segment p - 1 (p = 2 .. P-1), in order of p:
+//   [S; M]_p = Phi [S; M]_{p-1} + offset,   Phi = [[A_S, B_S], [A_M, B_M]]
+// where (A_S, A_M), (B_S, B_M) and the offset are the end states of pass-1
+// replicas 1, 2 and 0 of segment p - 1 (the replicas' stored transposed,
+// A^T[k][r]), and [S; M]_1 is the end state of segment 0.  One workgroup per
+// (sequence, 16 state columns) keeps the columns' [S; M]_{p-1} (2D x 16,
+// fp32) in LDS; thread r forms row r of the result, so for each k the
+// threads read consecutive elements of A^T[k] and B^T[k], and every thread
+// reads the same X row (an LDS broadcast).  Slots are D x D fp32 blocks of
+// `segS` / `segM`: pass-1 slot s U1 + j, the results at H U1 + s (P - 2) +
+// p - 2.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(2 * D * 4) void mdn_seg_combine_kernel(float* __restrict__ segS, float* __restrict__ segM,
+                                                                    int H, int P)
+{
+    constexpr int CB = 16, NB = D / CB;
+    constexpr int KQ = 4, KL = D / KQ;                 // contraction quarters, steps per quarter
+    __shared__ __attribute__((aligned(16))) float X[2 * D][CB];
+    __shared__ __attribute__((aligned(16))) float red[KQ - 1][2 * D][CB];   // partial sums of quarters 1..3
+    const int s = blockIdx.x / NB, c0 = (blockIdx.x % NB) * CB;
+    const int U1 = 1 + 3 * (P - 2);
+    const int64_t DD = (int64_t)D * D;
+    const int tid = threadIdx.x;
+    const int r = tid % (2 * D), kq = tid / (2 * D);   // row of [S; M], contraction quarter
+    float* const base = r < D ? segS : segM;
+    const int rr = r % D;
+    for (int i = tid; i < 2 * D * CB; i += 2 * D * KQ) {
+        const int xr = i / CB, c = i % CB;
+        X[xr][c] = (xr < D ? segS : segM)[(int64_t)s * U1 * DD + (int64_t)(xr % D) * D + c0 + c];
+    }
+    for (int p = 2; p < P; ++p) {
+        const int64_t j0 = (int64_t)s * U1 + 1 + 3 * (p - 2);
+        // this quarter's A^T[k][rr], B^T[k][rr], all in flight at once
+        const float* aT = base + (j0 + 1) * DD + rr + (int64_t)kq * KL * D;
+        const float* bT = base + (j0 + 2) * DD + rr + (int64_t)kq * KL * D;
+        float av[KL], bv[KL];
+#pragma unroll
+        for (int k = 0; k < KL; ++k) {
+            av[k] = aT[(int64_t)k * D];
+            bv[k] = bT[(int64_t)k * D];
+        }
+        float acc[CB];
+        if (kq == 0) {
+            const float* off = base + j0 * DD + (int64_t)rr * D + c0;
+#pragma unroll
+            for (int c = 0; c < CB; c += 4) {
+                const float4 o = *reinterpret_cast<const float4*>(off + c);
+                acc[c] = o.x; acc[c + 1] = o.y; acc[c + 2] = o.z; acc[c + 3] = o.w;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < CB; ++c) acc[c] = 0.f;
+        }
+        __syncthreads();                               // X_{p-1} complete
+#pragma unroll
+        for (int k = 0; k < KL; ++k) {
+            const int kk = kq * KL + k;
+#pragma unroll
+            for (int c = 0; c < CB; c += 4) {
+                const float4 xs = *reinterpret_cast<const float4*>(&X[kk][c]);
+                const float4 xm = *reinterpret_cast<const float4*>(&X[D + kk][c]);
+                acc[c] = fmaf(av[k], xs.x, fmaf(bv[k], xm.x, acc[c]));
+                acc[c + 1] = fmaf(av[k], xs.y, fmaf(bv[k], xm.y, acc[c + 1]));
+                acc[c + 2] = fmaf(av[k], xs.z, fmaf(bv[k], xm.z, acc[c + 2]));
+                acc[c + 3] = fmaf(av[k], xs.w, fmaf(bv[k], xm.w, acc[c + 3]));
+            }
+        }
+        if (kq > 0) {
+#pragma unroll
+            for (int c = 0; c < CB; c += 4)
+                *reinterpret_cast<float4*>(&red[kq - 1][r][c]) = float4{acc[c], acc[c + 1], acc[c + 2], acc[c + 3]};
+        }
+        __syncthreads();                               // partial sums written, every read of X_{p-1} done
+        if (kq == 0) {
+            const int64_t out = (int64_t)H * U1 + (int64_t)s * (P - 2) + p - 2;
+            float* dst = base + out * DD + (int64_t)rr * D + c0;
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                const float v = acc[c] + red[0][r][c] + red[1][r][c] + red[2][r][c];
+                X[r][c] = v;
+                dst[c] = v;
+            }
+        }
+    }
+}
+
+hipError_t launch_chunk_inter_split(const ChunkArgs& a, int P, float* segS, float* segM)
+{
+    if (a.BH == 0) return hipSuccess;
+    auto run = [&](const InterLaunch& l) {
+        return a.dtype == MDN_BF16 ? inter_dispatch<TraitsBf16>(a, l) : inter_dispatch<TraitsF32>(a, l);
+    };
+    const int U1 = 1 + 3 * (P - 2);
+    hipError_t e = run(InterLaunch{a.BH * U1, InterSeg{P, 1}, a.S0, a.M0, segS, segM});
+    if (e != hipSuccess) return e;
+    if (P > 2) {
+        const int NB = a.dk / 16;
+        switch (a.dk) {
+        case 16: hipLaunchKernelGGL(mdn_seg_combine_kernel<16>, dim3((unsigned)(a.BH * NB)), dim3(2 * a.dk * 4), 0, (hipStream_t)a.stream, segS, segM, (int)a.BH, P); break;
+        case 32: hipLaunchKernelGGL(mdn_seg_combine_kernel<32>, dim3((unsigned)(a.BH * NB)), dim3(2 * a.dk * 4), 0, (hipStream_t)a.stream, segS, segM, (int)a.BH, P); break;
+        case 64: hipLaunchKernelGGL(mdn_seg_combine_kernel<64>, dim3((unsigned)(a.BH * NB)), dim3(2 * a.dk * 4), 0, (hipStream_t)a.stream, segS, segM, (int)a.BH, P); break;
+        case 128: hipLaunchKernelGGL(mdn_seg_combine_kernel<128>, dim3((unsigned)(a.BH * NB)), dim3(2 * a.dk * 4), 0, (hipStream_t)a.stream, segS, segM, (int)a.BH, P); break;
+        default: return hipErrorInvalidValue;
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return run(InterLaunch{a.BH * (P - 1), InterSeg{P, 2}, segS, segM, a.ST, a.MT});
 }
 
 }  // namespace mdn

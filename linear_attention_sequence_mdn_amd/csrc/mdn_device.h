@@ -272,20 +272,79 @@ __device__ __forceinline__ void xcd_head_map(int id, int slabs, int BH, int& bh,
 // XCD meets its units longest first.  The bounds read from cu are clamped
 // into [0, T] and ordered, which keeps every row and tile slot in range
 // whatever the table holds.
+//
+// Sequence split (seg.P > 0, [BH, T] layout): each sequence is cut at chunk
+// boundaries into P segments, segment p holding chunks [P0(p), P0(p + 1))
+// with P0(p) = p NT / P.  Each chunk's map of the state [S; M] is affine, so
+// a segment's is too; the columns of the state evolve independently under
+// one 2D x 2D map.  Pass 1 (seg.pass == 1) runs, per sequence, segment 0
+// from the true start state (its outputs are final) and, for each middle
+// segment 1 .. P-2, three replicas from chunk P0(p): the data from a zero
+// state (the map's offset), and V = 0 from S = I, M = 0 and from S = 0,
+// M = I (the columns of the map); replicas store no O or vtilde.  Units are
+// (sequence, j) with j = 0 for segment 0 and j = 1 + 3 (p - 1) + replica;
+// the end states go to slot unit.  Pass 2 reruns segments 1 .. P-1, unit
+// (sequence, p - 1), from the start states the combine step placed at
+// unit.sin; only the last segment stores its end state (at the sequence's
+// own slot).
+struct InterSeg {
+    int P, pass;
+};
 struct InterUnit {
     int bh, slab;
     int64_t row0, tile0, len;
+    int64_t sin, sout;      // state element offsets of the start / end states (-1: zero start / no store)
+    int ident;              // 1: start from S = I, M = 0; 2: from S = 0, M = I
+    bool vzero, ostore;     // V read as zero; O and vtilde stored
 };
+__device__ __forceinline__ int64_t seg_first_chunk(int p, int P, int64_t NT) { return (int64_t)p * NT / P; }
+// SEG: the kernel is the sequence split's (seg.P > 0); the other kernels
+// are compiled without the split's unit fields.
+template <bool SEG>
 __device__ __forceinline__ InterUnit inter_unit(int id, int slabs, int BH, int64_t T, int64_t NT, int C,
                                                 const int32_t* __restrict__ cu, const int32_t* __restrict__ perm,
-                                                int H)
+                                                int H, int D, InterSeg seg)
 {
     InterUnit u;
+    u.ident = 0;
+    u.vzero = false;
+    u.ostore = true;
+    if constexpr (SEG) {
+        // BH counts the units of the pass here; H the sequences
+        const int U = seg.pass == 1 ? 1 + 3 * (seg.P - 2) : seg.P - 1;
+        int un;
+        xcd_head_map(id, slabs, BH, un, u.slab);
+        const int s = un / U, j = un % U;
+        const int p = seg.pass == 1 ? (j == 0 ? 0 : 1 + (j - 1) / 3) : 1 + j;
+        const int64_t c0 = seg_first_chunk(p, seg.P, NT), c1 = seg_first_chunk(p + 1, seg.P, NT);
+        u.bh = s;
+        u.row0 = (int64_t)s * T + c0 * C;
+        u.tile0 = (int64_t)s * NT + c0;
+        u.len = (c1 * C < T ? c1 * C : T) - c0 * C;
+        const int64_t DD = (int64_t)D * D;
+        if (seg.pass == 1) {
+            const int rep = j == 0 ? 0 : (j - 1) % 3;
+            u.sin = j == 0 ? s * DD : -1;
+            u.ident = rep;
+            u.vzero = rep > 0;
+            u.ostore = j == 0;
+            u.sout = (int64_t)un * DD;
+        } else {
+            // start states: segment 1 from the end state of segment 0 (pass-1
+            // slot (s, 0)); segment p >= 2 from the combine step's slot
+            // H U1 + s (P - 2) + p - 2 (U1 = 1 + 3 (P - 2))
+            const int U1 = 1 + 3 * (seg.P - 2);
+            u.sin = (p == 1 ? (int64_t)s * U1 : (int64_t)H * U1 + (int64_t)s * (seg.P - 2) + p - 2) * DD;
+            u.sout = p == seg.P - 1 ? s * DD : -1;
+        }
+        return u;
+    }
     if (!cu) {
         xcd_head_map(id, slabs, BH, u.bh, u.slab);
         u.row0 = (int64_t)u.bh * T;
         u.tile0 = (int64_t)u.bh * NT;
         u.len = T;
+        u.sin = u.sout = (int64_t)u.bh * D * D;
         return u;
     }
     int r;
@@ -307,6 +366,7 @@ __device__ __forceinline__ InterUnit inter_unit(int id, int slabs, int BH, int64
     u.row0 = h * T + c0;
     u.tile0 = h * NT + c0 / C + i;
     u.len = c1 - c0;
+    u.sin = u.sout = (int64_t)u.bh * D * D;
     return u;
 }
 

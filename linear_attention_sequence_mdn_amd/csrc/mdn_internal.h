@@ -90,6 +90,12 @@ hipError_t launch_chunk_intra(const ChunkArgs& a);
 hipError_t launch_chunk_coef(const ChunkArgs& a);
 // sequential inter-chunk stage (vtilde, O, state carry)
 hipError_t launch_chunk_inter(const ChunkArgs& a);
+// the inter-chunk stage with each sequence cut into P segments ([B, H, T]
+// layout): pass 1, the combine step and pass 2, with the state slots in
+// segS / segM (BH (1 + 4 (P - 2)) blocks of dk x dv fp32 each)
+hipError_t launch_chunk_inter_split(const ChunkArgs& a, int P, float* segS, float* segM);
+// compute units of the current device (256 when the query fails)
+int device_compute_units();
 // the whole forward in one kernel, without a workspace, for the shapes it
 // covers (bf16, C = 64, dk = dv in {64, 128}, [B, H, T] layout)
 bool fwd_fused_supported(const ChunkArgs& a);

@@ -35,6 +35,7 @@ def test_header_declares_expected_entry_points():
               "mdn_chunk_inter", "mdn_chunk_coef", "mdn_gates", "mdn_chunk_fwd_varlen",
               "mdn_chunk_fwd_varlen_workspace_bytes", "mdn_chunk_bwd", "mdn_chunk_bwd_workspace_bytes",
               "mdn_chunk_fwd_fused", "mdn_chunk_fwd_noalloc", "mdn_stream_rw",
+              "mdn_chunk_fwd_split", "mdn_chunk_fwd_split_workspace_bytes",
               "mdn_status_string", "mdn_abi_version"):
         assert n in names
 
@@ -50,7 +51,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.mdn_abi_version() == 7
+    assert L.mdn_abi_version() == 8
 
 
 def test_status_strings(L):
@@ -372,6 +373,53 @@ def test_fused_forward_validation(L):
         assert f(ptrs=q) == NULL_ARG, i
     q = list(p)
     q[9] = q[0]                                   # O over q
+    assert f(ptrs=q) == ALIAS
+    q = list(p)
+    q[12] = ctypes.c_void_p(BASE + 8)             # misaligned vtilde
+    assert f(ptrs=q) == ALIGN
+
+
+def test_split_forward_validation(L):
+    """mdn_chunk_fwd_split: the forward's workspace plus 2 * BH (1 + 4 (nseg - 2))
+    fp32 state slots; native sizes and 2 <= nseg <= 64 only; the state slots
+    count in the workspace and alias checks."""
+    bad = ctypes.c_size_t(-1).value
+    B, H, T, d, C = 1, 16, 16384, 128, 64
+    base = 2 * B * H * (T // C) * C * C * 2 + B * H * (T // C) * 8 * C * 4     # the single pass's workspace
+    for nseg in (2, 3, 5):
+        slots = B * H * (1 + 4 * (nseg - 2)) * d * d * 4
+        assert L.mdn_chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, 1, nseg) == base + 2 * slots
+    assert L.mdn_chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, 1, 1) == bad
+    assert L.mdn_chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, 1, 65) == bad
+    assert L.mdn_chunk_fwd_split_workspace_bytes(1, 1, 64, 16, 16, 16, 1, 3) == bad     # widened bf16 shape
+    # mdn_chunk_fwd sizes its workspace for the three-segment split where it
+    # takes it (few heads of bf16 d = 128, C = 64, long sequences; the head
+    # range depends on the device's compute units), else for one pass
+    assert L.mdn_chunk_fwd_workspace_bytes(B, H, T, d, d, C, 1) in (
+        base, L.mdn_chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, 1, 3))
+    one_pass = 2 * 64 * 64 * 64 * 64 * 2 + 64 * 64 * 8 * 64 * 4
+    assert L.mdn_chunk_fwd_workspace_bytes(8, 8, 4096, 128, 128, 64, 1) == one_pass
+    assert L.mdn_chunk_fwd_workspace_bytes(1, 16, 1024, 128, 128, 64, 1) == 2 * 16 * 16 * 64 * 64 * 2 + 16 * 16 * 8 * 64 * 4
+    p = addrs(14)
+
+    def f(B=1, H=2, T=640, d=64, C=64, dt=1, nseg=3, ptrs=p, ws=None):
+        n = L.mdn_chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, dt, nseg) if ws is None else ws
+        return L.mdn_chunk_fwd_split(B, H, T, d, d, C, dt, nseg, *ptrs[:13], ptrs[13], n, None)
+    assert f(nseg=1, ws=1 << 30) == UNSUPPORTED
+    assert f(nseg=65, ws=1 << 30) == UNSUPPORTED
+    assert f(d=16) == UNSUPPORTED and f(C=16, ws=1 << 30) == UNSUPPORTED
+    assert f(d=48, ws=1 << 30) == UNSUPPORTED
+    assert f(B=-1, ws=1 << 30) == BAD_SHAPE
+    assert f(B=0, ptrs=[None] * 14, ws=0) == OK
+    # the forward's own workspace is not enough
+    assert f(ws=L.mdn_chunk_fwd_workspace_bytes(1, 2, 640, 64, 64, 64, 1)) == WORKSPACE
+    for i in (0, 1, 2, 3, 4, 5, 6, 9, 10, 11, 12, 13):
+        q = list(p)
+        q[i] = None
+        assert f(ptrs=q) == (WORKSPACE if i == 13 else NULL_ARG), i
+    # an output inside the state slots at the end of the workspace
+    q = list(p)
+    q[10] = ctypes.c_void_p(p[13].value + L.mdn_chunk_fwd_split_workspace_bytes(1, 2, 640, 64, 64, 64, 1, 3) - 256)
     assert f(ptrs=q) == ALIAS
     q = list(p)
     q[12] = ctypes.c_void_p(BASE + 8)             # misaligned vtilde
