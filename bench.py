@@ -281,9 +281,23 @@ def chunk_bench(args, torch, mdn, inputs):
         ms_sus = timed(call.run)
         sustained = {"ms_per_call": ms_sus, "tokens_per_s": tokens / (ms_sus / 1e3),
                      "after_ms_of_calls": args.sustained_ms}
+    # which forward mdn_chunk_fwd ran: with few long heads it cuts each
+    # sequence into segments (mdn_chunk_fwd_split), and its workspace query
+    # then returns the split's size; `kernels` above are the single pass's
+    # stage entry points either way
+    dt = mdn.MDN_BF16 if x.dtype == "bf16" else mdn.MDN_F32
+    n_ws = mdn.chunk_fwd_workspace_bytes(B, H, T, d, d, C, dt)
+    path = {"kind": "single pass", "segments": 1}
+    if x.dk == x.dv:
+        try:
+            if n_ws == mdn.chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, dt, 3):
+                path = {"kind": "sequence split", "segments": 3,
+                        "single_pass_stages_ms": ms_intra + ms_inter}
+        except mdn.MdnError:
+            pass
     return dict(ms_step=ms_step, ms_call_median=ms_call_median, tokens_per_s=tps, mfma_frac=mfma_frac,
                 kernels=kernels, roofline=roof, finite=finite, x=x, cfg=cfg, call=call, call_bytes=call_bytes,
-                hbm_cap=hbm_cap, fused=fused, settle=settle, sustained=sustained)
+                hbm_cap=hbm_cap, fused=fused, settle=settle, sustained=sustained, path=path)
 
 
 def decode_bench(args, torch, mdn, inputs):
@@ -545,6 +559,7 @@ def main():
                     "call_alg_bytes": ch["call_bytes"], "hbm_capped_tokens_per_s": ch["hbm_cap"],
                     "frac_of_hbm_cap": ch["tokens_per_s"] / ch["hbm_cap"],
                     "kernels": ch["kernels"], "roofline": ch["roofline"], "outputs_finite": ch["finite"]})
+        out["forward_path"] = ch["path"]
         out["settle"] = ch["settle"]
         if ch["sustained"] is not None:
             out["sustained_load"] = ch["sustained"]
