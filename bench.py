@@ -289,12 +289,14 @@ def chunk_bench(args, torch, mdn, inputs):
     n_ws = mdn.chunk_fwd_workspace_bytes(B, H, T, d, d, C, dt)
     path = {"kind": "single pass", "segments": 1}
     if x.dk == x.dv:
-        try:
-            if n_ws == mdn.chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, dt, 3):
-                path = {"kind": "sequence split", "segments": 3,
-                        "single_pass_stages_ms": ms_intra + ms_inter}
-        except mdn.MdnError:
-            pass
+        for nseg in range(3, 65):
+            try:
+                if n_ws == mdn.chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, dt, nseg):
+                    path = {"kind": "sequence split", "segments": nseg,
+                            "single_pass_stages_ms": ms_intra + ms_inter}
+                    break
+            except mdn.MdnError:
+                break
     return dict(ms_step=ms_step, ms_call_median=ms_call_median, tokens_per_s=tps, mfma_frac=mfma_frac,
                 kernels=kernels, roofline=roof, finite=finite, x=x, cfg=cfg, call=call, call_bytes=call_bytes,
                 hbm_cap=hbm_cap, fused=fused, settle=settle, sustained=sustained, path=path)

@@ -5,6 +5,7 @@
 // alignment, overlap between outputs and inputs, and workspace size.  A
 // failed check returns its status and enqueues nothing.  Validated calls are
 // handed to the launchers in mdn_step.hip / mdn_chunk.hip.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -164,18 +165,24 @@ bool split_state_bytes(const ChunkSizes& s, int dk, int dv, int P, size_t* out) 
 }
 
 // Segments mdn_chunk_fwd cuts each sequence into by itself (0: none).  The
-// split pays where one pass leaves compute units idle and its first pass
-// fills them: measured on the long-context shape (16 heads of 16384
-// tokens, bf16, d = 128, C = 64; 0.39 against 0.43 ms) with three segments,
-// whose first pass is 4 two-tile column slabs of 4 units per head, i.e.
-// 16 workgroups per head.  Taken for that family only, when those
-// workgroups fill more than half of the compute units and at most all of
-// them, and the segments hold at least 16 chunks each.
+// split pays where one pass leaves compute units idle.  Its first pass runs
+// 1 + 3 (P - 2) units per head in slabs of two column tiles (4 workgroups
+// per unit at d = 128); measured (bf16, d = 128, C = 64, heads x tokens
+// 16 x 16384 to 2 x 65536), the best P is the largest whose first pass fits
+// the device in one round of workgroups, as long as the segments hold at
+// least 64 chunks; two segments never paid.  E.g. on 256 compute units:
+// 16 heads of 16384 tokens take 3 segments (0.40 against 0.44 ms), 8 of
+// 32768 take 4 (0.56 against 0.80 ms), 2 of 65536 take 12; 16 heads of
+// 8192 tokens and more than 16 heads keep the single pass.  Taken for that
+// family only.
 int auto_segments(const ChunkSizes& s, int dk, int dv, int C, int dtype) {
-    if (s.nseq >= 0 || dtype != MDN_BF16 || dk != 128 || dv != 128 || C != 64 || s.NT < 48) return 0;
+    if (s.nseq >= 0 || dtype != MDN_BF16 || dk != 128 || dv != 128 || C != 64 || s.BH <= 0) return 0;
     const int64_t cus = mdn::device_compute_units();
-    const int64_t pass1 = s.BH * 16;
-    return (pass1 <= cus && 2 * pass1 > cus) ? 3 : 0;
+    const int64_t units = cus / (4 * s.BH);            // first-pass units per head that fit one round
+    int64_t P = units >= 1 ? (units - 1) / 3 + 2 : 0;
+    P = std::min<int64_t>(P, s.NT / 64);
+    P = std::min<int64_t>(P, MDN_SPLIT_MAX_SEGMENTS);
+    return P >= 3 ? (int)P : 0;
 }
 
 }  // namespace

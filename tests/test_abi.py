@@ -392,7 +392,7 @@ def test_split_forward_validation(L):
     assert L.mdn_chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, 1, 1) == bad
     assert L.mdn_chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, 1, 65) == bad
     assert L.mdn_chunk_fwd_split_workspace_bytes(1, 1, 64, 16, 16, 16, 1, 3) == bad     # widened bf16 shape
-    # mdn_chunk_fwd sizes its workspace for the three-segment split where it
+    # mdn_chunk_fwd sizes its workspace for the sequence split where it
     # takes it (few heads of bf16 d = 128, C = 64, long sequences; the head
     # range depends on the device's compute units), else for one pass
     assert L.mdn_chunk_fwd_workspace_bytes(B, H, T, d, d, C, 1) in (

@@ -55,6 +55,8 @@ CASES = [
     ("f32", 1, 2, 64 * 6, 128, 64, 3, 0.3),
     ("f32", 1, 1, 32 * 9, 64, 32, 3, None),
     ("f32", 1, 3, 64 * 4 + 63, 64, 64, 2, 0.3),
+    ("bf16", 1, 1, 64 * 30 + 7, 128, 64, 12, 0.02),     # ten combine steps in order
+    ("f32", 1, 2, 32 * 40 + 3, 32, 32, 23, 0.3),
 ]
 
 
@@ -103,7 +105,8 @@ def start_state_matters(x, nseg, tol):
 
 
 @pytest.mark.parametrize("dtype,d,C,T,nseg", [("bf16", 128, 64, 64 * 12 + 5, 3), ("bf16", 64, 32, 32 * 17, 5),
-                                              ("f32", 128, 64, 64 * 9, 3), ("f32", 32, 32, 32 * 14 + 7, 4)])
+                                              ("f32", 128, 64, 64 * 9, 3), ("f32", 32, 32, 32 * 14 + 7, 4),
+                                              ("bf16", 128, 64, 64 * 26, 12)])
 def test_split_long_memory_gates(dtype, d, C, T, nseg):
     x = long_memory(inputs.make_chunk_inputs(1, 2, T, d, C=C, dtype=dtype, seed=808 + d + nseg,
                                              state_std=0.3), 909 + T)
@@ -159,26 +162,40 @@ def test_split_long_context_full_size():
         note(f"    {n}: worst head {int(per.argmax())} err {per.max():.2e}, median head {np.median(per):.2e}")
 
 
-def test_forward_takes_the_split_on_few_long_heads():
-    """mdn_chunk_fwd on the long-context shape, with the workspace its query
-    returns, is the three-segment split: bit for bit the same outputs as
-    mdn_chunk_fwd_split(nseg=3); with only the single pass's workspace it runs
-    the single pass (both within the bar of the oracle elsewhere)."""
+def auto_segments(BH, T, cus):
+    """The segment count mdn_chunk_fwd takes for bf16, d = 128, C = 64 (0:
+    the single pass): the largest P whose first pass, 1 + 3 (P - 2) units of
+    4 workgroups per head, fits the compute units in one round, with at
+    least 64 chunks per segment, and at least 3."""
+    units = cus // (4 * BH)
+    P = (units - 1) // 3 + 2 if units >= 1 else 0
+    P = min(P, (-(-T // 64)) // 64, 64)
+    return P if P >= 3 else 0
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 16, 16384), (1, 4, 32768), (1, 16, 8192)])
+def test_forward_takes_the_split_on_few_long_heads(B, H, T):
+    """mdn_chunk_fwd with the workspace its query returns takes the sequence
+    split where the rule above chooses it: bit for bit the outputs of
+    mdn_chunk_fwd_split with that segment count (and the single pass where it
+    chooses none: the query then returns the single pass's size)."""
     import linear_attention_sequence_mdn_amd as mdn
     torch = torch_mod()
-    x = inputs.config_inputs(4)
+    x = inputs.config_inputs(4) if (B, H, T) == (1, 16, 16384) else \
+        inputs.make_chunk_inputs(B, H, T, 128, C=64, dtype="bf16", seed=T + H)
     args = [dev(x.q, "bf16"), dev(x.k, "bf16"), dev(x.v, "bf16"), dev(x.alpha), dev(x.mu), dev(x.beta),
             dev(x.eta), None, None]
-    B, H, T, d, C = x.B, x.H, x.T, x.dk, x.C
-    n_auto = mdn.chunk_fwd_workspace_bytes(B, H, T, d, d, C, mdn.MDN_BF16)
-    n_split = mdn.chunk_fwd_split_workspace_bytes(B, H, T, d, d, C, mdn.MDN_BF16, 3)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    note(f"long-context shape: workspace query {n_auto} bytes, split(3) {n_split} bytes, {cus} compute units")
-    if not (B * H * 16 <= cus < 2 * B * H * 16):
-        pytest.skip(f"the split is not chosen on a device with {cus} compute units")
-    assert n_auto == n_split
-    auto = [t.clone() for t in mdn.chunk_fwd(*args, C=C)]
-    split = [t.clone() for t in mdn.chunk_fwd_split(*args, C=C, nseg=3)]
+    P = auto_segments(B * H, T, cus)
+    n_auto = mdn.chunk_fwd_workspace_bytes(B, H, T, 128, 128, 64, mdn.MDN_BF16)
+    note(f"B{B} H{H} T{T}: {cus} compute units, rule: {P or 'single pass'}; workspace query {n_auto} bytes")
+    if P == 0:
+        single = 2 * B * H * (T // 64) * 64 * 64 * 2 + B * H * (T // 64) * 8 * 64 * 4
+        assert n_auto == single
+        return
+    assert n_auto == mdn.chunk_fwd_split_workspace_bytes(B, H, T, 128, 128, 64, mdn.MDN_BF16, P)
+    auto = [t.clone() for t in mdn.chunk_fwd(*args, C=64)]
+    split = [t.clone() for t in mdn.chunk_fwd_split(*args, C=64, nseg=P)]
     torch.cuda.synchronize()
     for n, a, b in zip(NAMES, auto, split):
         assert torch.equal(a, b), n
