@@ -97,7 +97,12 @@ enum {
  * triangular; for bf16 at C = 64 and fp32 at C >= 32 their upper-right
  * C/2 x C/2 quadrant (all zero) is not written, and nothing reads it.  For
  * a widened bf16 call (dk = 16 or C = 16, see mdn_chunk_fwd) the layout is
- * that of the fp32 call, followed by fp32 copies of q, k, v, O and Vtilde. */
+ * that of the fp32 call, followed by fp32 copies of q, k, v, O and Vtilde.
+ * Where mdn_chunk_fwd would cut the sequences into segments (bf16, dk = dv
+ * = 128, C = 64, at most 16 heads with long sequences; see
+ * mdn_chunk_fwd_split) the size is mdn_chunk_fwd_split_workspace_bytes()
+ * for that segment count, which depends on the current device's compute
+ * units: query it with the device current that the call will run on. */
 size_t mdn_chunk_fwd_workspace_bytes(int64_t B, int64_t H, int64_t T,
                                      int dk, int dv, int C, int dtype);
 
@@ -124,7 +129,11 @@ size_t mdn_chunk_fwd_workspace_bytes(int64_t B, int64_t H, int64_t T,
  *   Vtilde      [B][H][T][dv]  (dtype) out: the materialised vtilde_t.
  *   workspace   device scratch of at least mdn_chunk_fwd_workspace_bytes();
  *               must not overlap any other argument.  Its contents on return
- *               follow the layout above.
+ *               follow the layout above.  Where that size includes the
+ *               sequence split's state slots and the workspace holds them,
+ *               the call runs mdn_chunk_fwd_split with the segment count the
+ *               query chose (same results up to rounding); a workspace of
+ *               only the single pass's size runs the single pass.
  *   stream      hipStream_t.
  */
 int mdn_chunk_fwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int C, int dtype,

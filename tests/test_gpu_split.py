@@ -142,6 +142,22 @@ def test_split_on_nan_workspace(dtype, d, C):
     check_all(run_split(x, 4, ws_fill=0xFF), oracle_of(x), TOL[dtype], f"split nan-ws {dtype}")
 
 
+def test_split_in_place_states():
+    """S_T, M_T given as S0, M0 (the in-place update): the first pass reads the
+    start state before the second pass writes the end state."""
+    import linear_attention_sequence_mdn_amd as mdn
+    torch = torch_mod()
+    x = long_memory(inputs.make_chunk_inputs(1, 2, 64 * 10 + 3, 128, C=64, dtype="bf16", seed=515,
+                                             state_std=0.3), 516)
+    note("split in-place states bf16 T643 nseg=4")
+    args = [dev(x.q, "bf16"), dev(x.k, "bf16"), dev(x.v, "bf16"), dev(x.alpha), dev(x.mu), dev(x.beta), dev(x.eta)]
+    S, M = dev(x.S0), dev(x.M0)
+    O, ST, MT, Vt = mdn.chunk_fwd_split(*args, S, M, C=64, nseg=4, S_T=S, M_T=M)
+    torch.cuda.synchronize()
+    assert ST.data_ptr() == S.data_ptr() and MT.data_ptr() == M.data_ptr()
+    check_all((host(O), host(S), host(M), host(Vt)), oracle_of(x), TOL["bf16"], "split in place")
+
+
 def test_split_deterministic():
     x = inputs.make_chunk_inputs(1, 2, 64 * 10, 128, C=64, dtype="bf16", seed=707, state_std=0.02)
     a, b = run_split(x, 3), run_split(x, 3)
