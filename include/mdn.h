@@ -99,7 +99,7 @@ enum {
  * a widened bf16 call (dk = 16 or C = 16, see mdn_chunk_fwd) the layout is
  * that of the fp32 call, followed by fp32 copies of q, k, v, O and Vtilde.
  * Where mdn_chunk_fwd would cut the sequences into segments (bf16, dk = dv
- * = 128, C = 64, at most 16 heads with long sequences; see
+ * in {64, 128}, C = 64, few heads with long sequences; see
  * mdn_chunk_fwd_split) the size is mdn_chunk_fwd_split_workspace_bytes()
  * for that segment count, which depends on the current device's compute
  * units: query it with the device current that the call will run on. */

@@ -166,22 +166,28 @@ bool split_state_bytes(const ChunkSizes& s, int dk, int dv, int P, size_t* out) 
 
 // Segments mdn_chunk_fwd cuts each sequence into by itself (0: none).  The
 // split pays where one pass leaves compute units idle.  Its first pass runs
-// 1 + 3 (P - 2) units per head in slabs of two column tiles (4 workgroups
-// per unit at d = 128); measured (bf16, d = 128, C = 64, heads x tokens
-// 16 x 16384 to 2 x 65536), the best P is the largest whose first pass fits
-// the device in one round of workgroups, as long as the segments hold at
-// least 64 chunks; two segments never paid.  E.g. on 256 compute units:
-// 16 heads of 16384 tokens take 3 segments (0.40 against 0.44 ms), 8 of
-// 32768 take 4 (0.56 against 0.80 ms), 2 of 65536 take 12; 16 heads of
-// 8192 tokens and more than 16 heads keep the single pass.  Taken for that
-// family only.
+// 1 + 3 (P - 2) units per head in slabs of two column tiles, d / 32
+// workgroups per unit.  Measured (bf16, C = 64, d = 128 and d = 64, 1 to 32
+// heads of 4096 to 65536 tokens), the best P is about the largest whose first
+// pass fits the device in one round of workgroups, with segments of at
+// least 32 chunks, or 64 where the three-segment first pass would fill more
+// than half of the device (short segments then lose to the slower rate of a
+// full device), and at most 12 (beyond, the combine steps in sequence cost
+// more); two segments never paid.  E.g. on 256 compute units, d = 128: 16
+// heads of 16384 tokens take 3 segments (0.40 against 0.44 ms), 4 heads of
+// 32768 take 7 (0.36 against 0.65 ms), 2 of 65536 take 12 (0.47 against
+// 1.27 ms); 16 heads of 8192 tokens keep the single pass.  d = 64: 16 heads
+// of 8192 take 4 (0.13 against 0.15 ms), 8 of 32768 take 7 (about 0.30
+// against 0.54 ms).  Taken for those two families only.
 int auto_segments(const ChunkSizes& s, int dk, int dv, int C, int dtype) {
-    if (s.nseq >= 0 || dtype != MDN_BF16 || dk != 128 || dv != 128 || C != 64 || s.BH <= 0) return 0;
+    if (s.nseq >= 0 || dtype != MDN_BF16 || dk != dv || (dk != 128 && dk != 64) || C != 64 || s.BH <= 0) return 0;
     const int64_t cus = mdn::device_compute_units();
-    const int64_t units = cus / (4 * s.BH);            // first-pass units per head that fit one round
+    const int64_t w = dk / 32;                         // first-pass workgroups per unit
+    const int64_t units = cus / (w * s.BH);            // first-pass units per head that fit one round
     int64_t P = units >= 1 ? (units - 1) / 3 + 2 : 0;
-    P = std::min<int64_t>(P, s.NT / 64);
-    P = std::min<int64_t>(P, MDN_SPLIT_MAX_SEGMENTS);
+    const int64_t floor_chunks = 2 * (4 * w * s.BH) > cus ? 64 : 32;
+    P = std::min<int64_t>(P, s.NT / floor_chunks);
+    P = std::min<int64_t>(P, 12);
     return P >= 3 ? (int)P : 0;
 }
 

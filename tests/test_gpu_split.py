@@ -178,38 +178,42 @@ def test_split_long_context_full_size():
         note(f"    {n}: worst head {int(per.argmax())} err {per.max():.2e}, median head {np.median(per):.2e}")
 
 
-def auto_segments(BH, T, cus):
-    """The segment count mdn_chunk_fwd takes for bf16, d = 128, C = 64 (0:
-    the single pass): the largest P whose first pass, 1 + 3 (P - 2) units of
-    4 workgroups per head, fits the compute units in one round, with at
-    least 64 chunks per segment, and at least 3."""
-    units = cus // (4 * BH)
+def auto_segments(BH, T, cus, d=128):
+    """The segment count mdn_chunk_fwd takes for bf16, C = 64, d in {64, 128}
+    (0: the single pass): the largest P whose first pass, 1 + 3 (P - 2) units
+    of d / 32 workgroups per head, fits the compute units in one round, with
+    at least 32 chunks per segment (64 where the three-segment first pass
+    fills more than half of the device), at most 12, and at least 3."""
+    w = d // 32
+    units = cus // (w * BH)
     P = (units - 1) // 3 + 2 if units >= 1 else 0
-    P = min(P, (-(-T // 64)) // 64, 64)
+    floor_chunks = 64 if 2 * 4 * w * BH > cus else 32
+    P = min(P, (-(-T // 64)) // floor_chunks, 12)
     return P if P >= 3 else 0
 
 
-@pytest.mark.parametrize("B,H,T", [(1, 16, 16384), (1, 4, 32768), (1, 16, 8192)])
-def test_forward_takes_the_split_on_few_long_heads(B, H, T):
+@pytest.mark.parametrize("B,H,T,d", [(1, 16, 16384, 128), (1, 4, 32768, 128), (1, 16, 8192, 128),
+                                     (1, 16, 8192, 64), (1, 32, 8192, 64)])
+def test_forward_takes_the_split_on_few_long_heads(B, H, T, d):
     """mdn_chunk_fwd with the workspace its query returns takes the sequence
     split where the rule above chooses it: bit for bit the outputs of
     mdn_chunk_fwd_split with that segment count (and the single pass where it
     chooses none: the query then returns the single pass's size)."""
     import linear_attention_sequence_mdn_amd as mdn
     torch = torch_mod()
-    x = inputs.config_inputs(4) if (B, H, T) == (1, 16, 16384) else \
-        inputs.make_chunk_inputs(B, H, T, 128, C=64, dtype="bf16", seed=T + H)
+    x = inputs.config_inputs(4) if (B, H, T, d) == (1, 16, 16384, 128) else \
+        inputs.make_chunk_inputs(B, H, T, d, C=64, dtype="bf16", seed=T + H + d)
     args = [dev(x.q, "bf16"), dev(x.k, "bf16"), dev(x.v, "bf16"), dev(x.alpha), dev(x.mu), dev(x.beta),
             dev(x.eta), None, None]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    P = auto_segments(B * H, T, cus)
-    n_auto = mdn.chunk_fwd_workspace_bytes(B, H, T, 128, 128, 64, mdn.MDN_BF16)
-    note(f"B{B} H{H} T{T}: {cus} compute units, rule: {P or 'single pass'}; workspace query {n_auto} bytes")
+    P = auto_segments(B * H, T, cus, d)
+    n_auto = mdn.chunk_fwd_workspace_bytes(B, H, T, d, d, 64, mdn.MDN_BF16)
+    note(f"B{B} H{H} T{T} d{d}: {cus} compute units, rule: {P or 'single pass'}; workspace query {n_auto} bytes")
     if P == 0:
         single = 2 * B * H * (T // 64) * 64 * 64 * 2 + B * H * (T // 64) * 8 * 64 * 4
         assert n_auto == single
         return
-    assert n_auto == mdn.chunk_fwd_split_workspace_bytes(B, H, T, 128, 128, 64, mdn.MDN_BF16, P)
+    assert n_auto == mdn.chunk_fwd_split_workspace_bytes(B, H, T, d, d, 64, mdn.MDN_BF16, P)
     auto = [t.clone() for t in mdn.chunk_fwd(*args, C=64)]
     split = [t.clone() for t in mdn.chunk_fwd_split(*args, C=64, nseg=P)]
     torch.cuda.synchronize()
